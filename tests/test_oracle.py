@@ -1,0 +1,374 @@
+"""Pins for the float64 oracle, independent of the oracle's own formulas.
+
+Each pin checks the oracle against something it does not compute itself:
+hand-derived closed forms, a library routine (torch's scaled dot-product
+attention in float64), brute force over every way to split a tiny history,
+exact special cases and invariants of softmax attention. The last test plants
+plausible mistakes in copies of the oracle and shows each is caught.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as oa
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape).astype(np.float32)
+
+
+# ---------------------------------------------------------------- pin checks
+# Each check takes the attention function under test so the same check can be
+# run against deliberately broken copies.
+
+def check_closed_forms(attn):
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        q = np.array(c["q"], dtype=np.float32)
+        k = np.array(c["k"], dtype=np.float32)
+        v = np.array(c["v"], dtype=np.float32)
+        out, lse = attn(q, k, v, np.array(c["seq_lens"]), dtype="f32",
+                        scale=c["scale"])
+        exp_out = np.array(c["out"], dtype=np.float64)
+        exp_lse = np.array([[float(x) for x in row] for row in c["lse"]])
+        assert np.allclose(out, exp_out, rtol=0, atol=c["tol"]), c["name"]
+        fin = np.isfinite(exp_lse)
+        assert np.array_equal(np.isneginf(lse), np.isneginf(exp_lse)), c["name"]
+        assert np.allclose(lse[fin], exp_lse[fin], rtol=0, atol=c["tol"]), c["name"]
+
+
+def check_library_sdpa(attn, seed=0):
+    """torch scaled_dot_product_attention in float64, KV heads repeated."""
+    rng = np.random.default_rng(seed)
+    for (B, Hq, Hkv, D, L) in [(2, 8, 2, 16, 37), (1, 4, 4, 8, 5),
+                               (3, 6, 3, 32, 70)]:
+        q = _rand(rng, B, Hq, D)
+        k = _rand(rng, B, Hkv, L, D)
+        v = _rand(rng, B, Hkv, L, D)
+        lens = rng.integers(1, L + 1, size=B)
+        for scale in (None, 0.3):
+            out, lse = attn(q, k, v, lens, dtype="f32", scale=scale)
+            G = Hq // Hkv
+            for b in range(B):
+                n = int(lens[b])
+                qt = torch.from_numpy(q[b].astype(np.float64))[None, :, None, :]
+                kt = torch.from_numpy(k[b, :, :n].astype(np.float64))
+                vt = torch.from_numpy(v[b, :, :n].astype(np.float64))
+                kt = kt.repeat_interleave(G, dim=0)[None]
+                vt = vt.repeat_interleave(G, dim=0)[None]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qt, kt, vt, scale=scale)[0, :, 0, :].numpy()
+                assert np.allclose(out[b], ref, rtol=0, atol=1e-12)
+                sc = scale if scale else 1.0 / math.sqrt(D)
+                s = torch.einsum("hd,hnd->hn", qt[0, :, 0], kt[0]) * sc
+                ref_lse = torch.logsumexp(s, dim=-1).numpy()
+                assert np.allclose(lse[b], ref_lse, rtol=0, atol=1e-12)
+
+
+def check_gqa_equals_repeated_mha(attn, seed=1):
+    rng = np.random.default_rng(seed)
+    B, Hkv, G, D, L = 2, 3, 4, 16, 25
+    q = _rand(rng, B, Hkv * G, D)
+    k = _rand(rng, B, Hkv, L, D)
+    v = _rand(rng, B, Hkv, L, D)
+    lens = np.array([25, 11])
+    out, lse = attn(q, k, v, lens, dtype="f32")
+    out2, lse2 = attn(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1),
+                      lens, dtype="f32")
+    assert np.allclose(out, out2, atol=1e-14) and np.allclose(lse, lse2, atol=1e-14)
+
+
+def check_paged_equals_contiguous(attn, seed=4):
+    w = workloads.make("ragged_paged", seed=seed, batch=3, num_q_heads=4,
+                       num_kv_heads=2, head_dim=16, max_seq_len=70,
+                       min_seq_len=1, poison_tail=True)
+    c = workloads.to_contiguous(w)
+    a, b = w.numpy_view(), c.numpy_view()
+    o1, l1 = attn(a["q"], a["k"], a["v"], a["seq_lens"], dtype="bf16",
+                  block_table=a["block_table"], block_size=a["block_size"])
+    o2, l2 = attn(b["q"], b["k"], b["v"], b["seq_lens"], dtype="bf16")
+    assert np.all(np.isfinite(o1))
+    assert np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)
+
+
+def check_single_token(attn, seed=5):
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand(rng, 1, 2, 8), _rand(rng, 1, 2, 4, 8), _rand(rng, 1, 2, 4, 8)
+    out, lse = attn(q, k, v, np.array([1]), dtype="f32", scale=0.7)
+    assert np.array_equal(out[0], v[0, :, 0].astype(np.float64))
+    s0 = 0.7 * np.einsum("hd,hd->h", q[0].astype(np.float64),
+                         k[0, :, 0].astype(np.float64))
+    assert np.allclose(lse[0], s0, rtol=0, atol=1e-15)
+
+
+def check_equal_keys_mean(attn, seed=6):
+    rng = np.random.default_rng(seed)
+    L, D = 33, 16
+    q = _rand(rng, 1, 3, D)
+    k = np.repeat(_rand(rng, 1, 1, 1, D), L, axis=2)
+    v = _rand(rng, 1, 1, L, D)
+    out, lse = attn(q, k, v, np.array([L]), dtype="f32")
+    mean = v[0, 0].astype(np.float64).mean(axis=0)
+    assert np.allclose(out[0], mean[None], rtol=0, atol=1e-12)
+    s = np.einsum("hd,d->h", q[0].astype(np.float64),
+                  k[0, 0, 0].astype(np.float64)) / math.sqrt(D)
+    assert np.allclose(lse[0], s + math.log(L), atol=1e-12)
+
+
+def check_dominant_logit(attn, seed=7):
+    rng = np.random.default_rng(seed)
+    L, D = 40, 8
+    for gap, j in ((50.0, 0), (50.0, L - 1), (800.0, 17)):
+        q = np.zeros((1, 1, D), np.float32)
+        q[0, 0, 0] = 1.0
+        k = np.zeros((1, 1, L, D), np.float32)
+        k[0, 0, :, 0] = rng.uniform(-1, 1, L).astype(np.float32)
+        k[0, 0, j, 0] = gap + 1.0
+        v = _rand(rng, 1, 1, L, D)
+        out, lse = attn(q, k, v, np.array([L]), dtype="f32", scale=1.0)
+        bound = L * math.exp(-(gap - 0.0)) * np.abs(v).max() + 1e-15
+        assert np.all(np.isfinite(out))
+        assert np.allclose(out[0, 0], v[0, 0, j], rtol=0, atol=bound)
+        assert abs(lse[0, 0] - (gap + 1.0)) < 1e-9
+
+
+# ------------------------------------------------------------ the pins proper
+
+def test_bf16_decode_matches_torch_on_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_bits_to_f64(bits)
+    ref = (torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+           .to(torch.float64).numpy())
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    # and the sign bit really is the sign
+    assert oracle.bf16_bits_to_f64(np.array([0xBF80], np.uint16))[0] == -1.0
+
+
+def test_closed_forms():
+    check_closed_forms(oracle.decode_attention)
+
+
+def test_library_sdpa():
+    check_library_sdpa(oracle.decode_attention)
+
+
+def test_gqa_equals_repeated_mha():
+    check_gqa_equals_repeated_mha(oracle.decode_attention)
+
+
+def test_paged_equals_contiguous():
+    check_paged_equals_contiguous(oracle.decode_attention)
+
+
+def test_single_token_is_exact():
+    check_single_token(oracle.decode_attention)
+
+
+def test_equal_keys_give_mean_of_values():
+    check_equal_keys_mean(oracle.decode_attention)
+
+
+def test_dominant_logit_gives_its_value_row():
+    check_dominant_logit(oracle.decode_attention)
+
+
+def test_permuting_history_jointly_is_invariant():
+    rng = np.random.default_rng(8)
+    q, k, v = _rand(rng, 1, 4, 8), _rand(rng, 1, 2, 19, 8), _rand(rng, 1, 2, 19, 8)
+    perm = rng.permutation(19)
+    o1, l1 = oracle.decode_attention(q, k, v, [19], dtype="f32")
+    o2, l2 = oracle.decode_attention(q, k[:, :, perm], v[:, :, perm], [19],
+                                     dtype="f32")
+    assert np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)
+
+
+def test_convex_and_affine_in_values():
+    rng = np.random.default_rng(9)
+    q, k, v = _rand(rng, 2, 2, 8), _rand(rng, 2, 1, 30, 8), _rand(rng, 2, 1, 30, 8)
+    lens = np.array([30, 7])
+    out, _ = oracle.decode_attention(q, k, v, lens, dtype="f32")
+    for b in range(2):
+        vv = v[b, 0, :lens[b]]
+        assert np.all(out[b] <= vv.max(axis=0) + 1e-12)
+        assert np.all(out[b] >= vv.min(axis=0) - 1e-12)
+    a, c = 2.5, -1.25
+    out2, _ = oracle.decode_attention(q, k, (a * v.astype(np.float64) + c),
+                                      lens, dtype="f32")
+    # a*v + c is rounded to float32 inside the oracle's f32 decode
+    out3, _ = oracle.decode_attention(
+        q, k, (a * v.astype(np.float64) + c).astype(np.float32), lens,
+        dtype="f32")
+    assert np.allclose(out2, out3, atol=0)
+    assert np.allclose(out3, a * out + c, atol=1e-5)
+
+
+def test_shift_of_all_scores_moves_only_lse():
+    rng = np.random.default_rng(10)
+    s = rng.standard_normal((3, 12))
+    vals = rng.standard_normal((12, 5))
+    o1, l1 = oracle.softmax_attention(s, vals)
+    o2, l2 = oracle.softmax_attention(s + 123.0, vals)
+    assert np.allclose(o1, o2, atol=1e-13)
+    assert np.allclose(l2 - l1, 123.0, atol=1e-12)
+
+
+def test_split_then_combine_brute_force():
+    """Every split of a tiny history into <= 4 contiguous chunks (empty ones
+    included), in every chunk order: combining the chunk partials equals
+    attention over the whole history."""
+    rng = np.random.default_rng(11)
+    for n in range(1, 11):
+        s = rng.standard_normal((2, n)) * 3.0
+        vals = rng.standard_normal((n, 4))
+        full_o, full_l = oracle.softmax_attention(s, vals)
+        for parts in range(1, 5):
+            for cuts in itertools.combinations_with_replacement(range(n + 1),
+                                                                parts - 1):
+                edges = (0,) + cuts + (n,)
+                chunks = [(edges[i], edges[i + 1]) for i in range(parts)]
+                os_, ls_ = [], []
+                for (a, b) in chunks:
+                    o, l = oracle.softmax_attention(s[:, a:b], vals[a:b])
+                    os_.append(o)
+                    ls_.append(l)
+                orders = list(itertools.permutations(range(parts)))
+                for order in orders[:6]:
+                    op = np.stack([os_[i] for i in order], axis=1)
+                    lp = np.stack([ls_[i] for i in order], axis=1)
+                    o, l = oracle.combine_partials(op, lp)
+                    assert np.allclose(o, full_o, rtol=0, atol=1e-12)
+                    assert np.allclose(l, full_l, rtol=0, atol=1e-12)
+
+
+def test_combine_of_all_empty_is_zero_and_neg_inf():
+    o, l = oracle.combine_partials(np.full((2, 3, 4), 5.0),
+                                   np.full((2, 3), -np.inf))
+    assert np.array_equal(o, np.zeros((2, 4))) and np.all(np.isneginf(l))
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 16, 40])
+def test_split_partials_recombine_to_unsplit(S):
+    w = workloads.make("ragged_paged", seed=12, batch=3, num_q_heads=8,
+                       num_kv_heads=2, head_dim=16, max_seq_len=150,
+                       min_seq_len=0)
+    a = w.numpy_view()
+    kw = dict(dtype="bf16", block_table=a["block_table"],
+              block_size=a["block_size"])
+    op, lp = oracle.split_partials(a["q"], a["k"], a["v"], a["seq_lens"], S,
+                                   max_seq_len=150, **kw)
+    P = oracle.split_length(150, S)
+    for b in range(3):
+        n = int(a["seq_lens"][b])
+        nonempty = -(-n // P)
+        assert np.all(np.isfinite(lp[b, :, :nonempty]))
+        assert np.all(np.isneginf(lp[b, :, nonempty:]))
+    o, l = oracle.combine_partials(op, lp)
+    ro, rl = oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"], **kw)
+    assert np.allclose(o, ro, atol=1e-12)
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(l))
+    assert np.allclose(l[fin], rl[fin], atol=1e-12)
+
+
+def test_split_length():
+    assert oracle.split_length(65536, 128) == 512
+    assert oracle.split_length(512, 4) == 128
+    assert oracle.split_length(100, 3) == 48
+    assert oracle.split_length(262144, 32) == 8192
+    for L in (1, 15, 16, 17, 1000, 65536):
+        for S in (1, 2, 3, 7, 64):
+            P = oracle.split_length(L, S)
+            assert P % 16 == 0 and P * S >= L and P - 16 < -(-L // S)
+
+
+# ------------------------------------------------ planted mistakes are caught
+
+def _mutant(kind):
+    """A copy of decode_attention with one plausible mistake planted."""
+    def attn(q, k, v, seq_lens, *, dtype, scale=None, block_table=None,
+             block_size=0, token_range=None):
+        qf = oa.decode_values(q, dtype)
+        B, Hq, D = qf.shape
+        Hkv = k.shape[1]
+        G = Hq // Hkv
+        sc = scale if scale else 1.0 / math.sqrt(D)
+        if kind == "no_scale":
+            sc = 1.0
+        out = np.zeros((B, Hq, D))
+        lse = np.full((B, Hq), -np.inf)
+        for b in range(B):
+            n = int(seq_lens[b])
+            if kind == "off_by_one_len":
+                n = min(n + 1, k.shape[2] if block_table is None else n + 1)
+            if n <= 0:
+                continue
+            for h in range(Hq):
+                kvh = (h % Hkv) if kind == "gqa_modulo" else h // G
+                if block_table is not None and block_size:
+                    pos = np.arange(n)
+                    slot = (pos // block_size if kind == "paged_slot_swap"
+                            else pos % block_size)
+                    blk = np.asarray(block_table)[b, pos // block_size]
+                    if kind == "paged_slot_swap":
+                        slot = np.minimum(slot, block_size - 1)
+                    kr = oa.decode_values(k[blk, kvh, slot], dtype)
+                    vr = oa.decode_values(v[blk, kvh, slot], dtype)
+                else:
+                    kr = oa.decode_values(k[b, kvh, :n], dtype)
+                    vr = oa.decode_values(v[b, kvh, :n], dtype)
+                s = sc * (kr @ qf[b, h])
+                if kind == "no_max_subtract":
+                    w = np.exp(s)
+                else:
+                    m = s.max()
+                    w = np.exp(s - m)
+                z = w.sum()
+                if kind == "unnormalised":
+                    z = 1.0
+                o = (w @ vr) / z
+                if kind == "key_value_swap":
+                    o = (w @ kr) / z
+                out[b, h] = o
+                base = 0.0 if kind == "no_max_subtract" else m
+                lse[b, h] = (base + (math.log2(w.sum()) if kind == "log2_lse"
+                                     else math.log(w.sum())))
+        return out, lse
+    return attn
+
+
+CHECKS = [check_closed_forms, check_library_sdpa, check_gqa_equals_repeated_mha,
+          check_paged_equals_contiguous, check_single_token,
+          check_equal_keys_mean, check_dominant_logit]
+MUTANTS = ["no_scale", "gqa_modulo", "no_max_subtract", "unnormalised",
+           "key_value_swap", "log2_lse", "paged_slot_swap", "off_by_one_len"]
+
+
+def test_reference_copy_passes_every_check():
+    attn = _mutant("none")
+    for chk in CHECKS:
+        chk(attn)
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_planted_mistake_is_caught(kind):
+    attn = _mutant(kind)
+    failed = []
+    for chk in CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                chk(attn)
+        except (AssertionError, IndexError, ValueError, FloatingPointError):
+            failed.append(chk.__name__)
+    assert failed, f"mutant {kind} passed every pin"
