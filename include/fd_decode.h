@@ -1,0 +1,197 @@
+/*
+ * fd_decode.h -- C ABI of the split-KV decode-attention library (gfx950).
+ *
+ * The operation (slavadubrov.com, "What is Flash-Decoding, and when does it
+ * speed up LLMs?", sections "What is Flash-Decoding" and "Why decode needs a
+ * different schedule"): during decode each active sequence contributes one
+ * new query position, which attends over the sequence's whole cached key /
+ * value history. Flash-Decoding cuts that history into parts handled by
+ * separate workgroups; each part yields a partial output and its
+ * log-sum-exp, and a reduction combines the parts, with a correct
+ * normalization, into the output that attention over the complete history
+ * gives. The aiexpertsdirectory.org summary of the method calls the second
+ * step the "split-KV cache reduction" and warns that it costs a little for
+ * very short histories, which the planner below accounts for.
+ *
+ * Per sequence b and query head h (kv head h / (Hq/Hkv)):
+ *   s_i   = scale * <q[b,h,:], k_i>                  for i < seq_lens[b]
+ *   out   = sum_i e^{s_i} v_i / sum_i e^{s_i}         (fp32)
+ *   lse   = ln sum_i e^{s_i}                          (natural log, fp32)
+ *   seq_lens[b] == 0 gives out = 0, lse = -inf.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is caller-owned. Device pointers are HIP device
+ *     memory of the current device; host pointers are marked "host". The
+ *     library allocates nothing and keeps no mutable global state; calls are
+ *     reentrant and thread-safe.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream). Nothing is synchronised.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     failed check the call returns a negative fd_status, launches nothing
+ *     and writes nothing. A launch failure reported by HIP returns
+ *     FD_ERR_HIP.
+ *   - Caller's contract, not checked: 0 <= seq_lens[b] <= max_seq_len;
+ *     every block id a sequence reaches is in [0, num_blocks); outputs do
+ *     not alias inputs. (Out-of-range lengths are clamped into
+ *     [0, max_seq_len] and block ids into [0, num_blocks) on the device so a
+ *     broken call cannot read outside the buffers, but its result is
+ *     meaningless.)
+ *   - For fixed inputs and num_splits the result is bitwise deterministic.
+ */
+#ifndef FD_DECODE_H
+#define FD_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_status {
+  FD_OK = 0,
+  FD_ERR_INVALID_ARG = -1,  /* null pointer, bad shape, bad alignment */
+  FD_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, dtype) */
+  FD_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  FD_ERR_HIP = -4           /* HIP reported an error at launch */
+} fd_status;
+
+typedef enum fd_dtype {
+  FD_DTYPE_F32 = 0,         /* q, k, v are IEEE float32 */
+  FD_DTYPE_BF16 = 1         /* q, k, v are bfloat16; math in fp32 */
+} fd_dtype;
+
+/*
+ * Shape of one decode-attention call.
+ *
+ *   q            [batch, num_q_heads, head_dim]              (dtype)
+ *   contiguous   k, v [batch, num_kv_heads, max_seq_len, head_dim]
+ *   paged        k, v pools [num_blocks, num_kv_heads, block_size, head_dim];
+ *                block_table int32 [batch, max_blocks_per_seq]; position i of
+ *                sequence b is slot i % block_size of block
+ *                block_table[b, i / block_size] (PagedAttention's block
+ *                table, listed by title among the sources of the "Faster Than
+ *                Flash" page). Entries past a sequence's last block are
+ *                never read.
+ *   out          fp32 [batch, num_q_heads, head_dim]; lse fp32 [batch, Hq]
+ *
+ * num_q_heads must be a multiple of num_kv_heads; query head h reads kv head
+ * h / (num_q_heads / num_kv_heads) (grouped-query attention).
+ */
+typedef struct fd_shape {
+  int32_t batch;               /* >= 1 */
+  int32_t num_q_heads;         /* >= 1 */
+  int32_t num_kv_heads;        /* >= 1, divides num_q_heads */
+  int32_t head_dim;            /* 64 or 128 */
+  int32_t max_seq_len;         /* L >= 0: bound on seq_lens[]; sets split size */
+  int32_t block_size;          /* 0 = contiguous; else a multiple of 16, <= 4096 */
+  int32_t max_blocks_per_seq;  /* paged: block_table row stride, >= ceil(L/bs) */
+  int32_t num_blocks;          /* paged: blocks in each of the k and v pools */
+  int32_t dtype;               /* fd_dtype */
+  float scale;                 /* logit scale; <= 0 selects 1/sqrt(head_dim) */
+} fd_shape;
+
+/* Split sizing used by every call below: with S = num_splits and
+ * L = max_seq_len, split s covers positions [s*P, (s+1)*P) of each sequence,
+ * P = ceil(ceil(L / S) / g) * g where g = max(16, block_size). A sequence
+ * shorter than s*P leaves split s empty; its partial is o = 0, lse = -inf. */
+
+/*
+ * Choose the number of splits for a call (host only, no device access).
+ *
+ * The pages give the regimes, not a rule: splitting helps when a small batch
+ * offers too few independent blocks for a long history, while for a short
+ * history or a batch that already fills the GPU the extra partials and the
+ * reduction may cost more than they save (slavadubrov.com, "Why decode needs
+ * a different schedule"; aiexpertsdirectory.org, operational constraints).
+ * The rule here: with units = batch * num_kv_heads, return 1 if units already
+ * cover num_cus or L is short; otherwise size splits so that the attended
+ * tokens spread over about num_cus workgroups, no split shorter than a
+ * minimum length.
+ *
+ *   shape        host pointer, validated as for fd_decode_attn
+ *   num_cus      compute units of the device (hipDeviceProp_t
+ *                multiProcessorCount), >= 1
+ *   sum_seq_len  sum of seq_lens[] if the caller knows it, else -1
+ *   num_splits   host out: the chosen S >= 1
+ */
+int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
+                   int* num_splits);
+
+/*
+ * Bytes of device workspace fd_decode_attn needs for num_splits splits:
+ * 0 when num_splits == 1, else room for the fp32 partials
+ * o_part [batch, Hq, S, head_dim] and lse_part [batch, Hq, S] (natural log),
+ * 256-byte aligned. shape and bytes are host pointers.
+ */
+int fd_workspace_size(const fd_shape* shape, int num_splits, size_t* bytes);
+
+/*
+ * Full decode attention: the split kernel, then (if num_splits > 1) the
+ * log-sum-exp combine kernel, on `stream`.
+ *
+ *   q, k_cache, v_cache  device, dtype per shape, 16-byte aligned
+ *   block_table          device int32, non-NULL iff shape->block_size > 0
+ *   seq_lens             device int32 [batch]
+ *   num_splits           S >= 1 (e.g. from fd_plan_splits); S == 1 writes
+ *                        `out` directly and needs no workspace
+ *   workspace            device, >= fd_workspace_size bytes, 16-byte aligned
+ *                        (ignored, may be NULL, when S == 1). Scratch only:
+ *                        its contents on entry do not matter.
+ *   out                  device fp32 [batch, Hq, head_dim], 16-byte aligned
+ *   lse_out              device fp32 [batch, Hq] natural log, or NULL
+ */
+int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* block_table,
+                   const int32_t* seq_lens, int num_splits, void* workspace,
+                   size_t workspace_bytes, float* out, float* lse_out,
+                   void* stream);
+
+/*
+ * The split step alone: per split s, the partial output of attention over
+ * that split's positions, normalised by its own softmax sum, and its
+ * log-sum-exp ("each unit computes a partial output and a log-sum-exp
+ * normalization value", slavadubrov.com, "Why decode needs a different
+ * schedule"). Empty splits get o = 0, lse = -inf. These partials can be
+ * combined with fd_combine_partials, also after gathering partials computed
+ * over different shards of a history.
+ *
+ *   o_part    device fp32 [batch, Hq, num_splits, head_dim], 16-byte aligned
+ *   lse_part  device fp32 [batch, Hq, num_splits], natural log
+ * Other arguments as for fd_decode_attn.
+ */
+int fd_decode_partials(const fd_shape* shape, const void* q,
+                       const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int num_splits, float* o_part, float* lse_part,
+                       void* stream);
+
+/*
+ * The reduction step alone: for each (b, h), with M = max_s lse_part[b,h,s],
+ *   out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M},
+ *   lse = M + ln sum_s e^{lse_s - M};
+ * splits with lse = -inf contribute nothing; if all are -inf, out = 0 and
+ * lse = -inf. ("A reduction combines them into the output that attention
+ * over the complete history requires", slavadubrov.com, same section.)
+ *
+ *   batch, num_q_heads, head_dim (64 or 128), num_splits >= 1
+ *   o_part, lse_part  device fp32, layouts as for fd_decode_partials
+ *   out               device fp32 [batch, Hq, head_dim], 16-byte aligned
+ *   lse_out           device fp32 [batch, Hq], or NULL
+ */
+int fd_combine_partials(int batch, int num_q_heads, int head_dim,
+                        int num_splits, const float* o_part,
+                        const float* lse_part, float* out, float* lse_out,
+                        void* stream);
+
+/* Static description of an fd_status value (never NULL). */
+const char* fd_status_str(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FD_DECODE_H */

@@ -1,0 +1,65 @@
+// Internal declarations shared by the host checks and the HIP launchers.
+#ifndef FD_INTERNAL_H
+#define FD_INTERNAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fd_decode.h"
+
+namespace fd {
+
+// Planner constants. A split is never shorter than kMinSplitTokens; the
+// attended tokens are spread over about kWavesPerCu * num_cus split units.
+constexpr int kMinSplitTokens = 256;
+constexpr int kOccupancy = 1;
+constexpr int kMaxSplits = 65535;
+constexpr int kMaxBlockSize = 4096;
+constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves
+
+// A validated, resolved call shape.
+struct Shape {
+  int B, Hq, Hkv, G, D, L;
+  int bs, max_blocks, num_blocks;
+  int dtype;
+  float scale;        // resolved (> 0)
+};
+
+int check_shape(const fd_shape* s, Shape* out);
+int tokens_per_split(const Shape& s, int num_splits);   // P
+int head_groups(const Shape& s);                        // ceil(G / 16)
+size_t partial_o_bytes(const Shape& s, int num_splits);
+size_t workspace_bytes(const Shape& s, int num_splits);
+
+// Kernel arguments (passed by value).
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* o_dst;       // out [B,Hq,D] (final) or o_part [B,Hq,S,D]
+  float* lse_dst;     // lse_out [B,Hq] (final, may be null) or lse_part
+  int B, Hq, Hkv, G, L;
+  int bs, max_blocks, num_blocks;
+  int S, P, nhg;      // splits, tokens per split, head groups per kv head
+  int final_out;      // 1: write normalised output + lse to out/lse_out
+  float scale_log2;   // scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse_part;
+  float* out;
+  float* lse_out;     // may be null
+  const int32_t* seq_lens;   // may be null: then all S splits are read
+  int B, Hq, S, P, L;
+};
+
+// Launchers (fd_kernels.hip). Return hipError_t as int.
+int launch_split(const Shape& s, const SplitArgs& a, void* stream);
+int launch_combine(int D, const CombineArgs& a, void* stream);
+
+}  // namespace fd
+
+#endif  // FD_INTERNAL_H

@@ -1,0 +1,560 @@
+// Split-KV decode attention kernels for gfx950 (CDNA4, wave64).
+//
+// The method (slavadubrov.com, "What is Flash-Decoding", section "Why decode
+// needs a different schedule"): the cached history of each sequence is cut
+// into splits, separate workgroups process the splits in parallel, each
+// emits a partial output with its log-sum-exp, and a reduction combines the
+// partials into exact softmax attention over the whole history. Inside a
+// split the scores are streamed with a running maximum and normaliser (the
+// online softmax named in the last abstract of the INT-FlashAttention related
+// list), so one pass over K and V suffices.
+//
+// Kernels:
+//   split_mfma<D, NW>    bf16 K/V, head_dim 64/128. One workgroup per
+//                        (split, kv head, 16-head group, sequence); NW waves
+//                        share the split, each wave streaming 32-token
+//                        subtiles straight from HBM into registers, and the
+//                        GQA group's QK^T and PV tile products run on the
+//                        16x16x32 bf16 matrix cores.
+//   split_generic<T, D>  fp32 (and any shape the MFMA path does not take):
+//                        LDS-tiled, plain fp32 FMA, exact fp32 products.
+//   combine_kernel<D>    log-sum-exp reduction of the split partials.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fd_internal.h"
+
+namespace fd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.44269504088896341f;
+
+__device__ __forceinline__ float fexp2(float x) {
+  return __builtin_amdgcn_exp2f(x);   // v_exp_f32; exp2(-inf) = 0
+}
+__device__ __forceinline__ float flog2(float x) {
+  return __builtin_amdgcn_logf(x);    // v_log_f32
+}
+
+__device__ __forceinline__ int clamp_len(const SplitArgs& a, int b) {
+  int n = a.seq_lens[b];
+  n = n < 0 ? 0 : n;
+  return n > a.L ? a.L : n;
+}
+
+// Where head h's result for split s goes.
+template <int D>
+__device__ __forceinline__ float* o_dst(const SplitArgs& a, int b, int h, int s) {
+  return a.final_out ? a.o_dst + ((size_t)b * a.Hq + h) * D
+                     : a.o_dst + (((size_t)b * a.Hq + h) * a.S + s) * D;
+}
+__device__ __forceinline__ float* lse_dst(const SplitArgs& a, int b, int h, int s) {
+  if (a.final_out)
+    return a.lse_dst ? a.lse_dst + (size_t)b * a.Hq + h : nullptr;
+  return a.lse_dst + ((size_t)b * a.Hq + h) * a.S + s;
+}
+
+// An empty split (or an empty history when final_out): o = 0, lse = -inf.
+template <int D>
+__device__ void write_empty(const SplitArgs& a, int b, int h0, int nh, int s) {
+  for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
+    const int g = i / D;
+    o_dst<D>(a, b, h0 + g, s)[i - g * D] = 0.f;
+  }
+  for (int g = threadIdx.x; g < nh; g += blockDim.x) {
+    float* l = lse_dst(a, b, h0 + g, s);
+    if (l) *l = -INFINITY;
+  }
+}
+
+// Element offset of cache row t (t < the sequence's length) of (b, kvh).
+template <int D>
+__device__ __forceinline__ size_t row_offset(const SplitArgs& a, int b, int kvh,
+                                             int t) {
+  if (a.bs == 0) return ((size_t)(b * a.Hkv + kvh) * a.L + t) * D;
+  const int page = t / a.bs;
+  int blk = a.block_table[(size_t)b * a.max_blocks + page];
+  blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+  return (((size_t)blk * a.Hkv + kvh) * a.bs + (t - page * a.bs)) * D;
+}
+
+// ----------------------------------------------------------------------------
+// Generic LDS-tiled split kernel (fp32 FMA).
+
+constexpr int kGenThreads = 256;
+constexpr int kGenTile = 32;
+
+__device__ __forceinline__ float load_f32(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_f32(const uint16_t* p, size_t i) {
+  return __uint_as_float((unsigned)p[i] << 16);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
+  constexpr int GH = kHeadsPerGroup;
+  __shared__ float q_s[GH][D];
+  __shared__ float acc_s[GH][D];
+  __shared__ float k_s[kGenTile][D + 1];
+  __shared__ float v_s[kGenTile][D + 1];
+  __shared__ float p_s[GH][kGenTile + 1];
+  __shared__ float m_s[GH], l_s[GH], al_s[GH];
+
+  const int tid = threadIdx.x;
+  const int s = blockIdx.x, b = blockIdx.z;
+  const int kvh = blockIdx.y / a.nhg;
+  const int hg = blockIdx.y - kvh * a.nhg;
+  const int h0 = kvh * a.G + hg * GH;
+  const int nh = min(GH, a.G - hg * GH);
+  const int len = clamp_len(a, b);
+  const int lo = s * a.P;
+  const int hi = min(lo + a.P, len);
+  if (lo >= hi) {
+    write_empty<D>(a, b, h0, nh, s);
+    return;
+  }
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  const T* Q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + h0) * D;
+
+  for (int i = tid; i < nh * D; i += kGenThreads) {
+    q_s[i / D][i % D] = load_f32(Q, i);
+    acc_s[i / D][i % D] = 0.f;
+  }
+  if (tid < GH) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.f;
+  }
+  __syncthreads();
+
+  for (int t0 = lo; t0 < hi; t0 += kGenTile) {
+    const int nt = min(kGenTile, hi - t0);
+    for (int i = tid; i < nt * D; i += kGenThreads) {
+      const int r = i / D, d = i - r * D;
+      const size_t off = row_offset<D>(a, b, kvh, t0 + r);
+      k_s[r][d] = load_f32(K, off + d);
+      v_s[r][d] = load_f32(V, off + d);
+    }
+    __syncthreads();
+    for (int i = tid; i < nh * kGenTile; i += kGenThreads) {
+      const int g = i / kGenTile, jj = i - g * kGenTile;
+      float sc = -INFINITY;
+      if (jj < nt) {
+        float acc = 0.f;
+#pragma unroll 8
+        for (int d = 0; d < D; ++d) acc = fmaf(q_s[g][d], k_s[jj][d], acc);
+        sc = acc * a.scale_log2;
+      }
+      p_s[g][jj] = sc;
+    }
+    __syncthreads();
+    if (tid < nh) {
+      float mx = -INFINITY;
+      for (int jj = 0; jj < nt; ++jj) mx = fmaxf(mx, p_s[tid][jj]);
+      const float mn = fmaxf(m_s[tid], mx);
+      const float al = fexp2(m_s[tid] - mn);
+      float sum = 0.f;
+      for (int jj = 0; jj < kGenTile; ++jj) {
+        const float e = jj < nt ? fexp2(p_s[tid][jj] - mn) : 0.f;
+        p_s[tid][jj] = e;
+        sum += e;
+      }
+      l_s[tid] = l_s[tid] * al + sum;
+      m_s[tid] = mn;
+      al_s[tid] = al;
+    }
+    __syncthreads();
+    for (int i = tid; i < nh * D; i += kGenThreads) {
+      const int g = i / D, d = i - g * D;
+      float acc = acc_s[g][d] * al_s[g];
+      for (int jj = 0; jj < nt; ++jj) acc = fmaf(p_s[g][jj], v_s[jj][d], acc);
+      acc_s[g][d] = acc;
+    }
+    __syncthreads();
+  }
+
+  for (int i = tid; i < nh * D; i += kGenThreads) {
+    const int g = i / D, d = i - g * D;
+    o_dst<D>(a, b, h0 + g, s)[d] = acc_s[g][d] / l_s[g];
+  }
+  if (tid < nh) {
+    float* l = lse_dst(a, b, h0 + tid, s);
+    if (l) *l = (m_s[tid] + flog2(l_s[tid])) * kLn2;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// MFMA split kernel (bf16).
+//
+// Lane layout of v_mfma_f32_16x16x32_bf16 used throughout (lane l, n = l%16,
+// j = l/16): the A operand's row and the B operand's column are n, and the
+// lane holds 8 consecutive k-slots 8j..8j+7 of it; the 16x16 fp32 result has
+// column n and rows 4j..4j+3 in the lane.
+//
+// Scores are computed transposed, S^T = K * Q^T, so that a lane ends up with
+// ONE query head (column n) and 8 tokens; that is exactly the lane's share
+// of P^T as the B operand of O^T = V^T * P^T, and the O^T result again has
+// head n in column n. Every per-head quantity (running max, alpha, sum)
+// therefore lives in the lane that needs it; only the max needs a 4-lane
+// exchange per subtile.
+//
+// A wave consumes a 32-token subtile: tokens 16*tg + 4j + i (tg = 0,1,
+// i = 0..3) are the rows of the two S^T tiles in lane group j, and the same
+// 8 tokens, T_j = {4j..4j+3, 16+4j..16+4j+3}, are lane group j's k-slots in
+// the PV product, so P never leaves its lane.
+//
+// K rows (A operand of QK): lane (n, j) loads 16 bytes of token 16*tg + n at
+// dims 32c + 8j (c = 0..D/32-1); Q^T (B operand) uses the same dims.
+// V rows (A operand of PV): lane (n, j) loads 16 bytes (8 dims starting at
+// 8n for D = 128) of each token in T_j -- every load instruction reads four
+// whole 256-byte rows -- and an 8x8 transpose in registers (v_perm_b32)
+// turns the 8 tokens x 8 dims block into 8 k-vectors, one per PV call.
+//
+// P is rounded to bf16 for the matrix cores as a hi/lo pair (p_hi = bf16(p),
+// p_lo = bf16(p - p_hi)); both products accumulate in fp32, so the weights
+// carry ~16 mantissa bits instead of 8.
+
+template <int D>
+struct MfmaCfg {
+  static constexpr int KC = D / 32;   // QK calls per 16-token tile
+  static constexpr int NV = D / 16;   // PV calls per subtile
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) {
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 v_kvec(const u32x4 (&vr)[8], int cc, int n) {
+  // k-vector for PV call cc: element e = element `idx` of vr[e].
+  //   D = 128: lane's row n <-> dim 8n + cc, element cc of its 8-dim chunk.
+  //   D = 64 : row n <-> dim 8(n&7) + 4(n>>3) + cc, element cc + 4(n>>3).
+  const unsigned sel = (cc & 1) ? 0x07060302u : 0x05040100u;
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    unsigned lo, hi;
+    if (D == 128) {
+      lo = vr[2 * k][cc >> 1];
+      hi = vr[2 * k + 1][cc >> 1];
+    } else {
+      const bool up = n >= 8;
+      lo = up ? vr[2 * k][2 + (cc >> 1)] : vr[2 * k][cc >> 1];
+      hi = up ? vr[2 * k + 1][2 + (cc >> 1)] : vr[2 * k + 1][cc >> 1];
+    }
+    r[k] = __builtin_amdgcn_perm(hi, lo, sel);
+  }
+  return as_bf16x8(r);
+}
+
+// Output dim of accumulator element (cc, i) in lane group j.
+template <int D>
+__device__ __forceinline__ int out_dim(int cc, int i, int j) {
+  const int m = 4 * j + i;
+  return D == 128 ? 8 * m + cc : 8 * (m & 7) + 4 * (m >> 3) + cc;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void split_mfma(SplitArgs a) {
+  constexpr int KC = MfmaCfg<D>::KC;
+  constexpr int NV = MfmaCfg<D>::NV;
+  __shared__ float xch[NW / 2 > 0 ? NW / 2 : 1][NV * 4 + 2][64];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int s = blockIdx.x, b = blockIdx.z;
+  const int kvh = blockIdx.y / a.nhg;
+  const int hg = blockIdx.y - kvh * a.nhg;
+  const int h0 = kvh * a.G + hg * 16;
+  const int nh = min(16, a.G - hg * 16);
+  const int len = clamp_len(a, b);
+  const int lo = s * a.P;
+  const int hi = min(lo + a.P, len);
+  if (lo >= hi) {
+    write_empty<D>(a, b, h0, nh, s);
+    return;
+  }
+
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+
+  bf16x8 qf[KC];
+  {
+    const uint16_t* qp =
+        static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h0 + (n < nh ? n : 0)) * D + 8 * j;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qp + 32 * c);
+      if (n >= nh) x = u32x4{0u, 0u, 0u, 0u};
+      qf[c] = as_bf16x8(x);
+    }
+  }
+
+  // Loads one 32-token subtile starting at t0 into registers.
+  auto load_subtile = [&](int t0, u32x4 (&kr)[2][KC], u32x4 (&vr)[8]) {
+    const size_t g0 = row_offset<D>(a, b, kvh, t0);
+    const size_t g1 = (t0 + 16 < hi) ? row_offset<D>(a, b, kvh, t0 + 16) : g0;
+    auto row = [&](int t) -> size_t {   // t in [t0, t0+32), clamped below hi
+      const int tc = min(t, hi - 1);
+      return tc < t0 + 16 ? g0 + (size_t)(tc - t0) * D
+                          : g1 + (size_t)(tc - t0 - 16) * D;
+    };
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      const size_t r = row(t0 + 16 * tg + n) + 8 * j;
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        kr[tg][c] = *reinterpret_cast<const u32x4*>(K + r + 32 * c);
+    }
+    const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
+      vr[e] = *reinterpret_cast<const u32x4*>(V + row(t) + vcol);
+    }
+  };
+
+  f32x4 o[NV];
+#pragma unroll
+  for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto compute_subtile = [&](int t0, const u32x4 (&kr)[2][KC],
+                             const u32x4 (&vr)[8]) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      sacc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(kr[tg][c]), qf[c], sacc[tg], 0, 0, 0);
+    }
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * tg + 4 * j + i;
+        const float x = tok < hi ? sacc[tg][i] * a.scale_log2 : -INFINITY;
+        sv[4 * tg + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = fexp2(m_run - mn);
+    m_run = mn;
+    bf16x8 ph, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fexp2(sv[e] - mn);
+      psum += p;
+      const __bf16 hb = (__bf16)p;
+      ph[e] = hb;
+      pl[e] = (__bf16)(p - (float)hb);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int cc = 0; cc < NV; ++cc) {
+      o[cc] *= alpha;
+      const bf16x8 vk = v_kvec<D>(vr, cc, n);
+      o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, ph, o[cc], 0, 0, 0);
+      o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, pl, o[cc], 0, 0, 0);
+    }
+  };
+
+  // Wave w takes subtiles w, w+NW, ...; double-buffered in registers.
+  {
+    u32x4 ka[2][KC], va[8], kb[2][KC], vb[8];
+    int t0 = lo + 32 * w;
+    if (t0 < hi) load_subtile(t0, ka, va);
+    while (t0 < hi) {
+      int t1 = t0 + 32 * NW;
+      if (t1 < hi) load_subtile(t1, kb, vb);
+      compute_subtile(t0, ka, va);
+      t0 = t1;
+      if (t0 >= hi) break;
+      t1 = t0 + 32 * NW;
+      if (t1 < hi) load_subtile(t1, ka, va);
+      compute_subtile(t0, kb, vb);
+      t0 = t1;
+    }
+  }
+
+  // Per-head sum over the 4 lane groups.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  // Merge the waves' (m, l, O) pairwise through LDS; every wave has the same
+  // lane -> (head, dims) layout, so the merge is element-wise.
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half >>= 1) {
+    if (w >= half && w < 2 * half) {
+      float(*slot)[64] = xch[w - half];
+#pragma unroll
+      for (int cc = 0; cc < NV; ++cc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slot[cc * 4 + i][lane] = o[cc][i];
+      slot[NV * 4][lane] = m_run;
+      slot[NV * 4 + 1][lane] = l_run;
+    }
+    __syncthreads();
+    if (w < half) {
+      float(*slot)[64] = xch[w];
+      const float mb = slot[NV * 4][lane];
+      const float lb = slot[NV * 4 + 1][lane];
+      const float mn = fmaxf(m_run, mb);
+      if (mn != -INFINITY) {
+        const float fa = fexp2(m_run - mn), fb = fexp2(mb - mn);
+#pragma unroll
+        for (int cc = 0; cc < NV; ++cc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[cc][i] = o[cc][i] * fa + slot[cc * 4 + i][lane] * fb;
+        l_run = l_run * fa + lb * fb;
+        m_run = mn;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (w == 0 && n < nh) {
+    const float inv = 1.f / l_run;
+    float* dst = o_dst<D>(a, b, h0 + n, s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (D == 128) {
+        const int d0 = out_dim<D>(0, i, j);
+        *reinterpret_cast<f32x4*>(dst + d0) =
+            f32x4{o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv};
+        *reinterpret_cast<f32x4*>(dst + d0 + 4) =
+            f32x4{o[4][i] * inv, o[5][i] * inv, o[6][i] * inv, o[7][i] * inv};
+      } else {
+        const int d0 = out_dim<D>(0, i, j);
+        *reinterpret_cast<f32x4*>(dst + d0) =
+            f32x4{o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv};
+      }
+    }
+    if (j == 0) {
+      float* l = lse_dst(a, b, h0 + n, s);
+      if (l) *l = (m_run + flog2(l_run)) * kLn2;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Log-sum-exp combine of split partials.
+
+constexpr int kCombThreads = 256;
+
+__device__ __forceinline__ float block_max(float x, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kCombThreads / 64; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
+  constexpr int C4 = D / 4;
+  constexpr int R = kCombThreads / C4;
+  __shared__ float red[kCombThreads / 64];
+  __shared__ f32x4 racc[R][C4];
+  __shared__ float rsum[R];
+
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq;
+  const int tid = threadIdx.x;
+  int n = a.S;
+  if (a.seq_lens) {
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > a.L ? a.L : len);
+    n = min(a.S, (len + a.P - 1) / a.P);
+  }
+  const float* lse = a.lse_part + (size_t)bh * a.S;
+  float mx = -INFINITY;
+  for (int s = tid; s < n; s += kCombThreads) mx = fmaxf(mx, lse[s]);
+  const float M = block_max(mx, red);
+  float* out = a.out + (size_t)bh * D;
+  if (M == -INFINITY) {
+    for (int d = tid; d < D; d += kCombThreads) out[d] = 0.f;
+    if (tid == 0 && a.lse_out) a.lse_out[bh] = -INFINITY;
+    return;
+  }
+  const int c = tid % C4, r = tid / C4;
+  const float* op = a.o_part + (size_t)bh * a.S * D + 4 * c;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+#pragma unroll 4
+  for (int s = r; s < n; s += R) {
+    const float wt = fexp2((lse[s] - M) * kLog2e);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)s * D);
+    acc += wt * v;
+    wsum += wt;
+  }
+  racc[r][c] = acc;
+  if (c == 0) rsum[r] = wsum;
+  __syncthreads();
+  if (r == 0) {
+    f32x4 t = racc[0][c];
+    float z = rsum[0];
+#pragma unroll
+    for (int k = 1; k < R; ++k) {
+      t += racc[k][c];
+      z += rsum[k];
+    }
+    const float inv = 1.f / z;
+    *reinterpret_cast<f32x4*>(out + 4 * c) = t * inv;
+    if (c == 0 && a.lse_out) a.lse_out[bh] = M + flog2(z) * kLn2;
+  }
+}
+
+constexpr int kMfmaWaves = 8;
+
+}  // namespace
+
+int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(a.S, s.Hkv * a.nhg, s.B);
+  if (s.dtype == FD_DTYPE_BF16) {
+    const dim3 block(kMfmaWaves * 64);
+    if (s.D == 128)
+      hipLaunchKernelGGL((split_mfma<128, kMfmaWaves>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((split_mfma<64, kMfmaWaves>), grid, block, 0, st, a);
+  } else {
+    const dim3 block(kGenThreads);
+    if (s.D == 128)
+      hipLaunchKernelGGL((split_generic<float, 128>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((split_generic<float, 64>), grid, block, 0, st, a);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_combine(int D, const CombineArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(a.B * a.Hq));
+  if (D == 128)
+    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(kCombThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(kCombThreads), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace fd

@@ -1,0 +1,181 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before launching."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from split_kv_long_amd import binding as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fd_decode.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fb.LIB_PATH),
+                                reason="library not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = fb.load()
+    names = header_functions()
+    assert set(names) == set(fb.SYMBOLS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_shape_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct fd_shape \{(.*?)\} fd_shape;", text, re.S)
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body.group(1))
+    assert [f for _, f in fields] == [f for f, _ in fb.FdShape._fields_]
+    assert ctypes.sizeof(fb.FdShape) == 40
+
+
+def test_status_strings_and_version():
+    assert fb.fd_status_str(0) == "ok"
+    for st in (-1, -2, -3, -4):
+        assert fb.fd_status_str(st) and fb.fd_status_str(st) != "ok"
+    assert fb.fd_status_str(7) == "unknown status"
+    assert fb.fd_version() >= 10000
+
+
+def shp(**kw):
+    d = dict(batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
+             max_seq_len=65536, dtype="bf16")
+    d.update(kw)
+    return fb.make_shape(**d)
+
+
+def plan(cus=256, sum_len=-1, **kw):
+    return fb.fd_plan_splits(shp(**kw), cus, sum_len)
+
+
+def test_planner_regimes():
+    # batch-one long history: spread over the CUs, 512-token splits
+    assert plan() == 128
+    assert plan(num_q_heads=64, num_kv_heads=8, max_seq_len=262144) == 32
+    # a batch that already fills the GPU: no split
+    assert plan(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=1024) == 1
+    # a short history: no split
+    assert plan(max_seq_len=400) == 1
+    # tiny MHA history of 512 tokens: at most 2 minimum-length splits
+    assert plan(num_q_heads=8, num_kv_heads=8, head_dim=64, max_seq_len=512,
+                dtype="f32") <= 2
+
+
+def test_planner_properties():
+    for L in (512, 1000, 4096, 65536, 262144, 1 << 20):
+        for B in (1, 2, 4, 16):
+            S = plan(batch=B, max_seq_len=L)
+            assert S >= 1
+            P = -(-(-(-L // S)) // 16) * 16
+            assert S * P >= L
+            if S > 1:
+                assert P >= 256 and B * 2 * S >= 1
+            assert S == plan(batch=B, max_seq_len=L)   # deterministic
+    # splits never grow as the batch grows at fixed L
+    prev = 10 ** 9
+    for B in (1, 2, 4, 8, 16, 32, 64, 128):
+        S = plan(batch=B, max_seq_len=32768)
+        assert S <= prev
+        prev = S
+    # a known, smaller total work gives shorter splits, so at least as many
+    full = plan(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=32768)
+    part = plan(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=32768,
+                sum_len=266240)
+    assert part >= full
+
+
+def test_workspace_size():
+    s = shp()
+    assert fb.fd_workspace_size(s, 1) == 0
+    n = fb.fd_workspace_size(s, 128)
+    assert n >= 16 * 128 * 129 * 4 and n % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=10, num_kv_heads=4), fb.FD_ERR_INVALID_ARG),
+    (dict(batch=0), fb.FD_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), fb.FD_ERR_INVALID_ARG),
+    (dict(head_dim=96), fb.FD_ERR_UNSUPPORTED),
+    (dict(head_dim=100), fb.FD_ERR_INVALID_ARG),
+    (dict(dtype=7), fb.FD_ERR_UNSUPPORTED),
+    (dict(max_seq_len=-1), fb.FD_ERR_INVALID_ARG),
+    (dict(block_size=8, max_blocks_per_seq=8192, num_blocks=10),
+     fb.FD_ERR_INVALID_ARG),
+    (dict(block_size=16, max_blocks_per_seq=10, num_blocks=10),
+     fb.FD_ERR_INVALID_ARG),
+    (dict(block_size=16, max_blocks_per_seq=4096, num_blocks=0),
+     fb.FD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fb.FD_ERR_INVALID_ARG),
+])
+def test_bad_shapes_are_rejected(kw, status):
+    s = shp(**kw)
+    lib = fb.load()
+    out = ctypes.c_int(-99)
+    assert lib.fd_plan_splits(ctypes.byref(s), 256, -1, ctypes.byref(out)) == status
+    assert out.value == -99
+    size = ctypes.c_size_t(12345)
+    assert lib.fd_workspace_size(ctypes.byref(s), 4, ctypes.byref(size)) == status
+    assert size.value == 12345
+    # a decode call with the bad shape is rejected before any pointer is used
+    assert lib.fd_decode_attn(ctypes.byref(s), 16, 16, 16, None, 16, 1, None,
+                              0, 16, None, None) == status
+
+
+FAKE = 1 << 20   # aligned, never dereferenced: every call below is rejected
+
+
+def call(**kw):
+    lib = fb.load()
+    args = dict(shape=shp(), q=FAKE, k=FAKE, v=FAKE, bt=None, lens=FAKE,
+                S=4, ws=FAKE, ws_bytes=1 << 30, out=FAKE, lse=None)
+    args.update(kw)
+    return lib.fd_decode_attn(ctypes.byref(args["shape"]), args["q"],
+                              args["k"], args["v"], args["bt"], args["lens"],
+                              args["S"], args["ws"], args["ws_bytes"],
+                              args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fb.FD_ERR_INVALID_ARG),
+    (dict(k=None), fb.FD_ERR_INVALID_ARG),
+    (dict(lens=None), fb.FD_ERR_INVALID_ARG),
+    (dict(out=None), fb.FD_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), fb.FD_ERR_INVALID_ARG),
+    (dict(v=FAKE + 2), fb.FD_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), fb.FD_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fb.FD_ERR_INVALID_ARG),
+    (dict(S=0), fb.FD_ERR_INVALID_ARG),
+    (dict(S=70000), fb.FD_ERR_INVALID_ARG),
+    (dict(ws=None), fb.FD_ERR_WORKSPACE),
+    (dict(ws_bytes=100), fb.FD_ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), fb.FD_ERR_INVALID_ARG),
+    (dict(bt=FAKE), fb.FD_ERR_INVALID_ARG),      # table given, contiguous shape
+    (dict(shape=shp(block_size=16, max_blocks_per_seq=4096, num_blocks=64)),
+     fb.FD_ERR_INVALID_ARG),                      # paged shape, no table
+])
+def test_bad_calls_are_rejected_on_the_host(kw, status):
+    assert call(**kw) == status
+
+
+def test_partials_and_combine_reject_bad_args():
+    lib = fb.load()
+    s = shp()
+    assert lib.fd_decode_partials(ctypes.byref(s), FAKE, FAKE, FAKE, None,
+                                  FAKE, 4, None, FAKE, None) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_decode_partials(ctypes.byref(s), FAKE, FAKE, FAKE, None,
+                                  FAKE, 0, FAKE, FAKE, None) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_combine_partials(1, 16, 96, 4, FAKE, FAKE, FAKE, None,
+                                   None) == fb.FD_ERR_UNSUPPORTED
+    assert lib.fd_combine_partials(0, 16, 128, 4, FAKE, FAKE, FAKE, None,
+                                   None) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_combine_partials(1, 16, 128, 4, FAKE + 4, FAKE, FAKE, None,
+                                   None) == fb.FD_ERR_INVALID_ARG

@@ -1,0 +1,262 @@
+"""Parity of the HIP library against the float64 oracle (needs a gfx950 GPU).
+
+Every case draws seeded inputs from ``workloads``, runs them through the C ABI
+(``split_kv_long_amd.binding``) and through ``oracle``, and compares every
+output element. Bars: max |out - oracle| <= 1e-5 for fp32 inputs and 2e-3 for
+bf16 inputs (fp32 accumulation); |lse - oracle| <= 1e-4; empty histories give
+exactly 0 / -inf.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from split_kv_long_amd import binding as fb
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+LSE_TOL = 1e-4
+LOG = os.environ.get("FD_PARITY_LOG")
+
+
+def num_cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def shape_of(w):
+    return fb.make_shape(**w.shape_dict())
+
+
+def device_inputs(w):
+    d = torch.device("cuda")
+    return dict(q=w.q.to(d), k=w.k.to(d), v=w.v.to(d),
+                seq_lens=w.seq_lens.to(d),
+                bt=None if w.block_table is None else w.block_table.to(d))
+
+
+def gpu_attention(w, S, t=None):
+    t = t or device_inputs(w)
+    shape = shape_of(w)
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"),
+                     device="cuda")
+    lse = torch.full((w.batch, w.num_q_heads), float("nan"), device="cuda")
+    nbytes = fb.fd_workspace_size(shape, S)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    print(f"[gpu] {w.name} S={S}", flush=True)
+    fb.fd_decode_attn(shape, t["q"], t["k"], t["v"], t["bt"], t["seq_lens"],
+                      S, ws, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def oracle_attention(w):
+    a = w.numpy_view()
+    return oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                   dtype=a["dtype"], scale=a["scale"],
+                                   block_table=a["block_table"],
+                                   block_size=a["block_size"])
+
+
+def assert_parity(name, dtype, out, lse, ref_out, ref_lse):
+    tol = TOL[dtype]
+    assert np.all(np.isfinite(out)), f"{name}: non-finite output"
+    err = float(np.abs(out - ref_out).max())
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isneginf(lse), ~fin), f"{name}: -inf lse mismatch"
+    lerr = float(np.abs(lse[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+    if LOG:
+        with open(LOG, "a") as f:
+            f.write(json.dumps(dict(case=name, dtype=dtype, max_abs=err,
+                                    lse_max_abs=lerr, tol=tol)) + "\n")
+    assert err <= tol, f"{name}: max |out - oracle| = {err:.3g} > {tol}"
+    assert lerr <= LSE_TOL, f"{name}: max |lse - oracle| = {lerr:.3g}"
+    empty = ~fin
+    assert np.all(out[empty] == 0.0)
+
+
+def check(w, S):
+    out, lse = gpu_attention(w, S)
+    ref_out, ref_lse = oracle_attention(w)
+    assert_parity(f"{w.name}/S={S}", w.dtype, out, lse, ref_out, ref_lse)
+    return out, lse
+
+
+# ------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_workload_at_planned_splits(name):
+    w = workloads.make(name)
+    S = fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len())
+    check(w, S)
+
+
+@pytest.mark.parametrize("name,splits", [
+    ("tiny_mha", [1, 4]),
+    ("long_gqa_64k", [1, 2, 8, 512]),
+    ("ragged_paged", [1, 16]),
+    ("short_batch", [2, 8]),
+])
+def test_workload_at_forced_splits(name, splits):
+    w = workloads.make(name)
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    for S in splits:
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"{name}/S={S}", w.dtype, out, lse, ref_out, ref_lse)
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("paged", [False, True])
+def test_ragged_tails_with_poisoned_cache(dtype, paged):
+    lens = [1, 15, 16, 17, 31, 33, 100, 511, 0, 257]
+    w = workloads.make("ragged", seed=21, batch=len(lens), num_q_heads=16,
+                       num_kv_heads=2, head_dim=128, max_seq_len=512,
+                       dtype=dtype, paged=paged, seq_lens=lens,
+                       poison_tail=True)
+    for S in (1, 3, 8, 32):
+        check(w, S)
+
+
+def test_more_splits_than_tiles():
+    lens = [3, 64, 40, 17]
+    w = workloads.make("few_tiles", seed=22, batch=4, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, max_seq_len=64,
+                       seq_lens=lens, poison_tail=True)
+    for S in (4, 16, 64):          # P = 16: most splits of short rows empty
+        check(w, S)
+
+
+def test_empty_histories():
+    w = workloads.make("empty", seed=23, batch=3, num_q_heads=4,
+                       num_kv_heads=1, head_dim=64, max_seq_len=32,
+                       seq_lens=[0, 0, 0])
+    for S in (1, 2):
+        out, lse = gpu_attention(w, S)
+        assert np.all(out == 0.0) and np.all(np.isneginf(lse))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_needles_at_boundaries(paged):
+    L, S = 4096, 8
+    P = oracle.split_length(L, S)
+    n = L - 5
+    positions = sorted({0, n - 1, P - 1, P, 3 * P - 1, 3 * P, 7 * P - 1,
+                        (n - 1) // 16 * 16})
+    for p in positions:
+        w = workloads.make("needle", seed=24, batch=1, num_q_heads=16,
+                           num_kv_heads=2, head_dim=128, max_seq_len=L,
+                           seq_lens=[n], paged=paged, needles=[p],
+                           needle_logit=40.0, poison_tail=True)
+        out, lse = check(w, S)
+        ref_v = w.v.float()
+        for kvh in range(2):
+            h = kvh * 8
+            if paged:
+                row = ref_v[int(w.block_table[0, p // 16]), kvh, p % 16]
+            else:
+                row = ref_v[0, kvh, p]
+            assert np.abs(out[0, h] - row.double().numpy()).max() < 2e-3, p
+
+
+def test_paged_matches_contiguous_bitwise():
+    w = workloads.make("ragged_paged", seed=25, batch=6, max_seq_len=3000,
+                       min_seq_len=1)
+    c = workloads.to_contiguous(w)
+    for S in (1, 5):
+        o1, l1 = gpu_attention(w, S)
+        o2, l2 = gpu_attention(c, S)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (12, 3, 128), (16, 1, 128),
+                                      (64, 2, 128), (40, 2, 64), (32, 8, 64),
+                                      (4, 4, 64)])
+def test_head_layouts_bf16(hq, hkv, d):
+    w = workloads.make("heads", seed=26, batch=2, num_q_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, max_seq_len=700,
+                       seq_lens=[700, 333])
+    for S in (1, 3):
+        check(w, S)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (6, 3, 64)])
+def test_head_layouts_f32(hq, hkv, d):
+    w = workloads.make("heads32", seed=27, batch=2, num_q_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, max_seq_len=300,
+                       seq_lens=[300, 129], dtype="f32")
+    for S in (1, 4):
+        check(w, S)
+
+
+def test_custom_scale_and_large_logits():
+    w = workloads.make("ultra_long_256k", max_seq_len=8192, scale=0.3,
+                       hot_key_fraction=0.002)
+    check(w, 1)
+    check(w, 16)
+
+
+def test_partials_and_combine_entry_points():
+    w = workloads.make("ragged_paged", seed=28, batch=3, num_q_heads=16,
+                       num_kv_heads=4, head_dim=128, max_seq_len=900,
+                       min_seq_len=1, poison_tail=True)
+    S = 7
+    t = device_inputs(w)
+    shape = shape_of(w)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    op = torch.empty(B, Hq, S, D, device="cuda")
+    lp = torch.empty(B, Hq, S, device="cuda")
+    fb.fd_decode_partials(shape, t["q"], t["k"], t["v"], t["bt"],
+                          t["seq_lens"], S, op, lp)
+    torch.cuda.synchronize()
+    a = w.numpy_view()
+    ref_op, ref_lp = oracle.split_partials(
+        a["q"], a["k"], a["v"], a["seq_lens"], S, dtype="bf16",
+        max_seq_len=900, block_table=a["block_table"],
+        block_size=a["block_size"])
+    got_op, got_lp = op.cpu().double().numpy(), lp.cpu().double().numpy()
+    assert_parity("partials", "bf16", got_op.reshape(B, Hq * S, D),
+                  got_lp.reshape(B, Hq * S), ref_op.reshape(B, Hq * S, D),
+                  ref_lp.reshape(B, Hq * S))
+    # combine of the oracle's partials (rounded to fp32) on the GPU
+    op2 = torch.from_numpy(ref_op.astype(np.float32)).cuda()
+    lp2 = torch.from_numpy(ref_lp.astype(np.float32)).cuda()
+    out = torch.empty(B, Hq, D, device="cuda")
+    lse = torch.empty(B, Hq, device="cuda")
+    fb.fd_combine_partials(B, Hq, D, S, op2, lp2, out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.combine_partials(ref_op.astype(np.float32),
+                                               ref_lp.astype(np.float32))
+    assert_parity("combine", "f32", out.cpu().double().numpy(),
+                  lse.cpu().double().numpy(), ref_out, ref_lse)
+
+
+def test_deterministic_bitwise():
+    w = workloads.make("long_gqa_64k", max_seq_len=16384)
+    t = device_inputs(w)
+    o1, l1 = gpu_attention(w, 32, t)
+    o2, l2 = gpu_attention(w, 32, t)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_convenience_wrapper_plans_and_allocates():
+    import split_kv_long_amd as fd
+    w = workloads.make("long_gqa_64k", max_seq_len=5000)
+    t = device_inputs(w)
+    out, lse = fd.decode_attention(t["q"], t["k"], t["v"], t["seq_lens"],
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_attention(w)
+    assert_parity("wrapper", "bf16", out.cpu().double().numpy(),
+                  lse.cpu().double().numpy(), ref_out, ref_lse)
