@@ -1,0 +1,302 @@
+"""Benchmark of split-KV decode attention on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one fd_decode_attn call (split kernel + log-sum-exp combine) over
+one synthetic decode batch whose K/V already sit in HBM. The default workload
+is batch 1, 16 query / 2 kv heads, head_dim 128, 65536 cached tokens, bf16.
+K/V are replicated into R copies (>= 512 MiB in total) and successive steps
+rotate through them, so the 256 MB Infinity Cache cannot serve a step from
+the previous one. The K timed steps are captured once into a HIP graph and
+replayed between two events, so host-side launch cost is not timed.
+
+Prints one JSON line (rank 0). Besides the metric it carries
+  roofline      the split kernel's algorithmic bytes per launch over its
+                average launch time, measured here with events around a
+                graph of split-only launches, against 8 TB/s HBM peak;
+  cpu_baseline  the float64 CPU oracle timed on the same call.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+COUNTERS_FILE = os.path.join(ROOT, "profiles",
+                             "split_mfma_long_gqa_64k_counters.md")
+KERNEL_SOURCE = os.path.join(ROOT, "split_kv_long_amd", "csrc",
+                             "fd_kernels.hip")
+
+
+def parse_args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="long_gqa_64k")
+    p.add_argument("--splits", type=int, default=0,
+                   help="force the split count (0: planner)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time for the oracle baseline")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain device copy of known size (for "
+                        "scaling HBM byte counters)")
+    p.add_argument("--all", action="store_true",
+                   help="also time every workload (extra JSON lines, "
+                        "stderr)")
+    return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per split-kernel launch from the committed counter summary,
+    or None if absent or taken on a different kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_source_digest():
+        return None
+    return float(t.group(1))
+
+
+class Bench:
+    def __init__(self, name, splits, steps):
+        import torch
+        import workloads
+        from split_kv_long_amd import binding as fb
+        self.torch, self.fb = torch, fb
+        self.w = w = workloads.make(name)
+        self.shape = fb.make_shape(**w.shape_dict())
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        self.cus = cus
+        self.S = splits or fb.fd_plan_splits(self.shape, cus, w.sum_seq_len())
+        self.P = -(-(-(-max(w.max_seq_len, 1) // self.S)) // 16) * 16
+        dev = torch.device("cuda")
+        kv = w.kv_bytes()
+        self.R = max(1, math.ceil(2 * MALL_BYTES / max(kv, 1)))
+        self.R = min(self.R, max(1, steps))
+        self.q = w.q.to(dev)
+        self.lens = w.seq_lens.to(dev)
+        self.bt = None if w.block_table is None else w.block_table.to(dev)
+        self.ks = [w.k.to(dev) for _ in range(self.R)]
+        self.vs = [w.v.to(dev) for _ in range(self.R)]
+        B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+        self.out = torch.empty(B, Hq, D, device=dev)
+        self.lse = torch.empty(B, Hq, device=dev)
+        nb = fb.fd_workspace_size(self.shape, self.S)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        self.op = torch.empty(B, Hq, max(self.S, 1), D, device=dev)
+        self.lp = torch.empty(B, Hq, max(self.S, 1), device=dev)
+        esz = 4 if w.dtype == "f32" else 2
+        self.bytes_alg = (kv + B * Hq * D * esz + B * Hq * D * 4 + B * Hq * 4
+                          + (0 if self.bt is None else
+                             4 * w.batch * -(-w.max_seq_len // w.block_size)))
+        self.bytes_split = kv + B * Hq * D * esz   # K/V + q, per split launch
+
+    def step(self, i):
+        r = i % self.R
+        self.fb.fd_decode_attn(self.shape, self.q, self.ks[r], self.vs[r],
+                               self.bt, self.lens, self.S, self.ws, self.out,
+                               self.lse)
+
+    def split_only(self, i):
+        r = i % self.R
+        self.fb.fd_decode_partials(self.shape, self.q, self.ks[r], self.vs[r],
+                                   self.bt, self.lens, self.S, self.op,
+                                   self.lp)
+
+    def combine_only(self, i):
+        w = self.w
+        self.fb.fd_combine_partials(w.batch, w.num_q_heads, w.head_dim,
+                                    self.S, self.op, self.lp, self.out,
+                                    self.lse)
+
+    def time_graph(self, fn, steps, warmup):
+        """Eager warmup, capture `steps` calls in a graph, replay once
+        untimed, then time one replay. Returns (ms total, wall ms)."""
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(steps):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        return e0.elapsed_time(e1), wall
+
+
+def copy_probe(torch):
+    """A plain device-to-device copy of a known size (counter scaling and
+    achievable-bandwidth context)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return dict(bytes_read=n, bytes_written=n, ms=ms,
+                GBps_read_plus_write=2 * n / (ms * 1e6))
+
+
+def cpu_baseline(w, target_s):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    a = w.numpy_view()
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                dtype=a["dtype"], scale=a["scale"],
+                                block_table=a["block_table"],
+                                block_size=a["block_size"])
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= target_s or len(times) >= 50:
+            break
+    med = statistics.median(times)
+    return dict(value=med * 1e6, unit="us/call", cores=threads, kind="oracle",
+                sample=(f"{len(times)} full calls of the {w.name} workload "
+                        f"(float64 NumPy oracle, median)"),
+                host_cpu_count=os.cpu_count())
+
+
+def run_one(args, name, steps, warmup, with_cpu):
+    import torch
+    b = Bench(name, args.splits if name == args.workload else 0, steps)
+    ms, wall = b.time_graph(b.step, steps, warmup)
+    us_call = ms * 1e3 / steps
+    ms_split, _ = b.time_graph(b.split_only, steps, warmup)
+    us_split = ms_split * 1e3 / steps
+    us_comb = None
+    if b.S > 1:
+        ms_c, _ = b.time_graph(b.combine_only, steps, 2)
+        us_comb = ms_c * 1e3 / steps
+    gbps = b.bytes_alg / (us_call * 1e3)
+    split_gbps = b.bytes_split / (us_split * 1e3)
+    w = b.w
+    traffic = read_traffic() if name == "long_gqa_64k" else None
+    rec = {
+        "metric": ("decode-attn us/call + achieved HBM GB/s (% of peak), "
+                   "B=1 L=64K GQA 16/2 d128"),
+        "value": round(us_call, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), see workloads/)",
+        "config": {
+            "workload": name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "max_seq_len": w.max_seq_len, "sum_seq_len": w.sum_seq_len(),
+            "paged": w.paged, "num_splits": b.S, "tokens_per_split": b.P,
+            "kv_copies_rotated": b.R, "timing": "hip graph replay of all "
+            "timed steps between two events",
+        },
+        "achieved_GBps": round(gbps, 1),
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes_per_call": b.bytes_alg,
+        "wall_ms_timed_region": round(wall, 3),
+        "split_kernel_us": round(us_split, 3),
+        "combine_kernel_us": None if us_comb is None else round(us_comb, 3),
+        "roofline": {
+            "kernel": "split_mfma" if w.dtype == "bf16" else "split_generic",
+            "bound": "hbm",
+            "achieved": round(split_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": b.bytes_split,
+            "launch_us": round(us_split, 3),
+        },
+    }
+    if args.copy_probe and name == args.workload:
+        rec["copy_probe"] = copy_probe(torch)
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    del b
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(sequence- or head-sharded multi-GPU decode is not built)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from split_kv_long_amd import binding
+    binding.load()     # fails loudly if the HIP library is missing
+    rec = run_one(args, args.workload, args.steps, args.warmup,
+                  not args.no_cpu_baseline)
+    if args.all:
+        import workloads
+        for name in workloads.ORDER:
+            if name == args.workload:
+                continue
+            r = run_one(args, name, args.steps, args.warmup, False)
+            print(json.dumps(r), file=sys.stderr, flush=True)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

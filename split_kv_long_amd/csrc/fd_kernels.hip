@@ -260,66 +260,115 @@ __device__ __forceinline__ int out_dim(int cc, int i, int j) {
   return D == 128 ? 8 * m + cc : 8 * (m & 7) + 4 * (m >> 3) + cc;
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void split_mfma(SplitArgs a) {
+// One workgroup = NW waves on one split of one (sequence, kv head, group of
+// at most GM query heads). Wave w owns the 32-token subtiles w, w+NW, ... of
+// the split, each loaded and then consumed; the other resident waves cover
+// the latency. A wave's first subtile is requested before the sequence
+// length is known: its rows are clamped to the split's range for a
+// full-length history, which is always inside the cache, and V rows past the
+// true length are zeroed once the length arrives (they may hold anything,
+// NaN included, and are multiplied by p = 0). At the end every wave parks
+// its (O, m, l) in LDS and the whole workgroup merges them in one pass.
+template <int D, int NW, int GM, bool PAGED>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(4))) void split_mfma(SplitArgs a) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int NV = MfmaCfg<D>::NV;
-  __shared__ float xch[NW / 2 > 0 ? NW / 2 : 1][NV * 4 + 2][64];
+  constexpr int DP = D + 4;                 // padded LDS row
+  __shared__ float mo[NW][GM][DP];
+  __shared__ float mm[NW][GM], ml[NW][GM];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, j = lane >> 4;
   const int s = blockIdx.x, b = blockIdx.z;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  // Fetch every kernel argument in one batch before the first branch, so the
+  // first K/V requests wait for one argument round trip, not two.
+  asm volatile("" ::"s"(K), "s"(V), "s"(a.q), "s"(a.seq_lens), "s"(a.o_dst),
+               "s"(a.lse_dst), "s"(a.block_table));
   const int kvh = blockIdx.y / a.nhg;
   const int hg = blockIdx.y - kvh * a.nhg;
-  const int h0 = kvh * a.G + hg * 16;
-  const int nh = min(16, a.G - hg * 16);
-  const int len = clamp_len(a, b);
+  const int h0 = kvh * a.G + hg * GM;
+  const int nh = min(GM, a.G - hg * GM);
   const int lo = s * a.P;
-  const int hi = min(lo + a.P, len);
-  if (lo >= hi) {
+  const int hi_max = min(lo + a.P, a.L);    // split end for a full history
+  if (lo >= hi_max) {                       // no sequence reaches this split
     write_empty<D>(a, b, h0, nh, s);
     return;
   }
 
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  // Element offset of the row of token t (t a multiple of 16 below the
+  // clamp bound; wave-uniform).
+  auto group_base = [&](int t) -> size_t {
+    if (!PAGED) return ((size_t)(b * a.Hkv + kvh) * a.L + t) * D;
+    const int page = t / a.bs;
+    int blk = a.block_table[(size_t)b * a.max_blocks + page];
+    blk = __builtin_amdgcn_readfirstlane(blk);
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    return (((size_t)blk * a.Hkv + kvh) * a.bs + (t - page * a.bs)) * D;
+  };
 
-  bf16x8 qf[KC];
-  {
-    const uint16_t* qp =
-        static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + h0 + (n < nh ? n : 0)) * D + 8 * j;
+  // Requests the subtile starting at t0 with every row clamped below `end`.
+  auto load_subtile = [&](int t0, int end, u32x4 (&kr)[2][KC],
+                          u32x4 (&vr)[8]) {
+    const int last0 = min(15, end - 1 - t0);
+    const int last1 = end - 1 - (t0 + 16);
+    const uint16_t* K0 = K + group_base(t0);
+    const uint16_t* V0 = V + group_base(t0);
+    const uint16_t* K1;
+    const uint16_t* V1;
+    int cap1;
+    if (last1 >= 0) {
+      const size_t g1 = group_base(t0 + 16);
+      K1 = K + g1;
+      V1 = V + g1;
+      cap1 = min(15, last1);
+    } else {
+      K1 = K0 + (size_t)last0 * D;
+      V1 = V0 + (size_t)last0 * D;
+      cap1 = 0;
+    }
+    const unsigned r0 = (unsigned)(min(n, last0) * D + 8 * j);
+    const unsigned r1 = (unsigned)(min(n, cap1) * D + 8 * j);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(qp + 32 * c);
-      if (n >= nh) x = u32x4{0u, 0u, 0u, 0u};
-      qf[c] = as_bf16x8(x);
-    }
-  }
-
-  // Loads one 32-token subtile starting at t0 into registers.
-  auto load_subtile = [&](int t0, u32x4 (&kr)[2][KC], u32x4 (&vr)[8]) {
-    const size_t g0 = row_offset<D>(a, b, kvh, t0);
-    const size_t g1 = (t0 + 16 < hi) ? row_offset<D>(a, b, kvh, t0 + 16) : g0;
-    auto row = [&](int t) -> size_t {   // t in [t0, t0+32), clamped below hi
-      const int tc = min(t, hi - 1);
-      return tc < t0 + 16 ? g0 + (size_t)(tc - t0) * D
-                          : g1 + (size_t)(tc - t0 - 16) * D;
-    };
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg) {
-      const size_t r = row(t0 + 16 * tg + n) + 8 * j;
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-        kr[tg][c] = *reinterpret_cast<const u32x4*>(K + r + 32 * c);
+      kr[0][c] = *reinterpret_cast<const u32x4*>(K0 + r0 + 32 * c);
+      kr[1][c] = *reinterpret_cast<const u32x4*>(K1 + r1 + 32 * c);
     }
     const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
-      vr[e] = *reinterpret_cast<const u32x4*>(V + row(t) + vcol);
+    for (int e = 0; e < 4; ++e) {
+      const unsigned v0 = (unsigned)(min(4 * j + e, last0) * D + vcol);
+      const unsigned v1 = (unsigned)(min(4 * j + e, cap1) * D + vcol);
+      vr[e] = *reinterpret_cast<const u32x4*>(V0 + v0);
+      vr[4 + e] = *reinterpret_cast<const u32x4*>(V1 + v1);
     }
   };
+
+  // The wave's first subtile goes out before anything else.
+  const int t_first = lo + 32 * w;
+  u32x4 k1[2][KC], v1[8];
+  if (t_first < hi_max) load_subtile(t_first, hi_max, k1, v1);
+
+  // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
+  // scores are computed and never used.
+  bf16x8 qf[KC];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         ((size_t)b * a.Hq + h0 + (n < nh ? n : 0)) * D + 8 * j;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 32 * c));
+  }
+
+  const int len = clamp_len(a, b);
+  const int hi = min(lo + a.P, len);
+  if (lo >= hi) {                           // uniform over the workgroup
+    write_empty<D>(a, b, h0, nh, s);
+    return;
+  }
 
   f32x4 o[NV];
 #pragma unroll
@@ -373,81 +422,60 @@ __global__ __launch_bounds__(NW * 64) void split_mfma(SplitArgs a) {
     }
   };
 
-  // Wave w takes subtiles w, w+NW, ...; double-buffered in registers.
-  {
-    u32x4 ka[2][KC], va[8], kb[2][KC], vb[8];
-    int t0 = lo + 32 * w;
-    if (t0 < hi) load_subtile(t0, ka, va);
-    while (t0 < hi) {
-      int t1 = t0 + 32 * NW;
-      if (t1 < hi) load_subtile(t1, kb, vb);
-      compute_subtile(t0, ka, va);
-      t0 = t1;
-      if (t0 >= hi) break;
-      t1 = t0 + 32 * NW;
-      if (t1 < hi) load_subtile(t1, ka, va);
-      compute_subtile(t0, kb, vb);
-      t0 = t1;
+  if (t_first < hi) {
+    if (hi < hi_max && t_first + 32 > hi) {
+      // Rows at or past hi were read speculatively: zero their V.
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = t_first + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
+        if (t >= hi) v1[e] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    compute_subtile(t_first, k1, v1);
+    for (int t0 = t_first + 32 * NW; t0 < hi; t0 += 32 * NW) {
+      u32x4 kr[2][KC], vr[8];
+      load_subtile(t0, hi, kr, vr);
+      compute_subtile(t0, kr, vr);
     }
   }
 
-  // Per-head sum over the 4 lane groups.
+  // Per-head sum over the 4 lane groups; then park (O, m, l) in LDS.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-
-  // Merge the waves' (m, l, O) pairwise through LDS; every wave has the same
-  // lane -> (head, dims) layout, so the merge is element-wise.
-#pragma unroll
-  for (int half = NW / 2; half >= 1; half >>= 1) {
-    if (w >= half && w < 2 * half) {
-      float(*slot)[64] = xch[w - half];
-#pragma unroll
-      for (int cc = 0; cc < NV; ++cc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) slot[cc * 4 + i][lane] = o[cc][i];
-      slot[NV * 4][lane] = m_run;
-      slot[NV * 4 + 1][lane] = l_run;
-    }
-    __syncthreads();
-    if (w < half) {
-      float(*slot)[64] = xch[w];
-      const float mb = slot[NV * 4][lane];
-      const float lb = slot[NV * 4 + 1][lane];
-      const float mn = fmaxf(m_run, mb);
-      if (mn != -INFINITY) {
-        const float fa = fexp2(m_run - mn), fb = fexp2(mb - mn);
-#pragma unroll
-        for (int cc = 0; cc < NV; ++cc)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            o[cc][i] = o[cc][i] * fa + slot[cc * 4 + i][lane] * fb;
-        l_run = l_run * fa + lb * fb;
-        m_run = mn;
-      }
-    }
-    __syncthreads();
-  }
-
-  if (w == 0 && n < nh) {
-    const float inv = 1.f / l_run;
-    float* dst = o_dst<D>(a, b, h0 + n, s);
+  if (n < nh) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (D == 128) {
-        const int d0 = out_dim<D>(0, i, j);
-        *reinterpret_cast<f32x4*>(dst + d0) =
-            f32x4{o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv};
-        *reinterpret_cast<f32x4*>(dst + d0 + 4) =
-            f32x4{o[4][i] * inv, o[5][i] * inv, o[6][i] * inv, o[7][i] * inv};
-      } else {
-        const int d0 = out_dim<D>(0, i, j);
-        *reinterpret_cast<f32x4*>(dst + d0) =
-            f32x4{o[0][i] * inv, o[1][i] * inv, o[2][i] * inv, o[3][i] * inv};
-      }
+      float* row = &mo[w][n][out_dim<D>(0, i, j)];
+      *reinterpret_cast<f32x4*>(row) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+      if (D == 128)
+        *reinterpret_cast<f32x4*>(row + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
     }
     if (j == 0) {
-      float* l = lse_dst(a, b, h0 + n, s);
-      if (l) *l = (m_run + flog2(l_run)) * kLn2;
+      mm[w][n] = m_run;
+      ml[w][n] = l_run;
+    }
+  }
+  __syncthreads();
+
+  // Merge: thread -> (head g, 4 dims); waves that saw no token carry m = -inf.
+  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
+    const int g = idx / (D / 4);
+    const int d = 4 * (idx - g * (D / 4));
+    float M = mm[0][g];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, mm[ww][g]);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float wt = fexp2(mm[ww][g] - M);
+      acc += wt * *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
+      lsum += wt * ml[ww][g];
+    }
+    *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) = acc * (1.f / lsum);
+    if (d == 0) {
+      float* l = lse_dst(a, b, h0 + g, s);
+      if (l) *l = (M + flog2(lsum)) * kLn2;
     }
   }
 }
@@ -524,20 +552,56 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
-constexpr int kMfmaWaves = 8;
+// Waves per workgroup for the MFMA kernel. Measured on MI355X: about two
+// subtiles per wave is best for short splits; more waves per workgroup make
+// the end-of-split merge and the workgroup's slowest wave costlier.
+int mfma_waves(int P) {
+  const int nsub = (P + 31) / 32;
+  return nsub >= 16 ? 8 : 4;
+}
+
+template <int D, bool PAGED, int GM>
+void launch_mfma_gm(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
+  switch (nw) {
+    case 16:
+      hipLaunchKernelGGL((split_mfma<D, 16, GM, PAGED>), grid, dim3(1024), 0, st, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL((split_mfma<D, 8, GM, PAGED>), grid, dim3(512), 0, st, a);
+      break;
+    default:
+      hipLaunchKernelGGL((split_mfma<D, 4, GM, PAGED>), grid, dim3(256), 0, st, a);
+      break;
+  }
+}
+
+template <int D, bool PAGED>
+void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
+  const int gm = s.G <= 8 ? 8 : 16;
+  a.nhg = (s.G + gm - 1) / gm;
+  const dim3 grid(a.S, s.Hkv * a.nhg, s.B);
+  const int nw = mfma_waves(a.P);
+  if (gm == 8)
+    launch_mfma_gm<D, PAGED, 8>(grid, nw, a, st);
+  else
+    launch_mfma_gm<D, PAGED, 16>(grid, nw, a, st);
+}
 
 }  // namespace
 
 int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(a.S, s.Hkv * a.nhg, s.B);
   if (s.dtype == FD_DTYPE_BF16) {
-    const dim3 block(kMfmaWaves * 64);
-    if (s.D == 128)
-      hipLaunchKernelGGL((split_mfma<128, kMfmaWaves>), grid, block, 0, st, a);
-    else
-      hipLaunchKernelGGL((split_mfma<64, kMfmaWaves>), grid, block, 0, st, a);
+    const bool paged = s.bs > 0;
+    if (s.D == 128) {
+      if (paged) launch_mfma<128, true>(s, a, st);
+      else launch_mfma<128, false>(s, a, st);
+    } else {
+      if (paged) launch_mfma<64, true>(s, a, st);
+      else launch_mfma<64, false>(s, a, st);
+    }
   } else {
+    const dim3 grid(a.S, s.Hkv * a.nhg, s.B);
     const dim3 block(kGenThreads);
     if (s.D == 128)
       hipLaunchKernelGGL((split_generic<float, 128>), grid, block, 0, st, a);
