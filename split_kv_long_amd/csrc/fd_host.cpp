@@ -81,6 +81,7 @@ static int check_splits(const Shape& s, int num_splits) {
   if (num_splits < 1 || num_splits > kMaxSplits) return FD_ERR_INVALID_ARG;
   // B*Hq*S*D must stay addressable with 64-bit offsets and 32-bit rows.
   if ((int64_t)s.B * s.Hq * num_splits > INT32_MAX) return FD_ERR_UNSUPPORTED;
+  if ((int64_t)s.B * s.Hq * 16 > INT32_MAX) return FD_ERR_UNSUPPORTED;   // combine grid
   return FD_OK;
 }
 
@@ -161,6 +162,9 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
   const int64_t work = tokens * s.Hkv * head_groups(s);
   const int64_t target = (int64_t)kOccupancy * num_cus;
   int64_t per = (work + target - 1) / target;
+  // Long splits: two workgroups per CU balance better and the extra
+  // partials cost nothing measurable.
+  if (per > kLongSplitTokens) per = (per + 1) / 2;
   if (per < kMinSplitTokens) per = kMinSplitTokens;
   const int64_t g = s.bs > 16 ? s.bs : 16;
   per = (per + g - 1) / g * g;
@@ -261,7 +265,7 @@ int fd_combine_partials(int batch, int num_q_heads, int head_dim,
       num_splits > kMaxSplits)
     return FD_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return FD_ERR_UNSUPPORTED;
-  if ((int64_t)batch * num_q_heads > INT32_MAX) return FD_ERR_UNSUPPORTED;
+  if ((int64_t)batch * num_q_heads * 16 > INT32_MAX) return FD_ERR_UNSUPPORTED;
   if (!o_part || !lse_part || !out) return FD_ERR_INVALID_ARG;
   if (!aligned16(o_part) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0 ||

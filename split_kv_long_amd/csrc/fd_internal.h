@@ -10,9 +10,11 @@
 namespace fd {
 
 // Planner constants. A split is never shorter than kMinSplitTokens; the
-// attended tokens are spread over about kWavesPerCu * num_cus split units.
+// attended tokens are spread over about kOccupancy * num_cus workgroups,
+// twice that when the resulting splits exceed kLongSplitTokens.
 constexpr int kMinSplitTokens = 256;
 constexpr int kOccupancy = 1;
+constexpr int kLongSplitTokens = 2048;
 constexpr int kMaxSplits = 65535;
 constexpr int kMaxBlockSize = 4096;
 constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves

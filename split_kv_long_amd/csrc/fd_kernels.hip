@@ -62,16 +62,22 @@ __device__ __forceinline__ float* lse_dst(const SplitArgs& a, int b, int h, int 
 }
 
 // An empty split (or an empty history when final_out): o = 0, lse = -inf.
-template <int D>
-__device__ void write_empty(const SplitArgs& a, int b, int h0, int nh, int s) {
+// Kept out of line so the hot path's code stays contiguous.
+__device__ __attribute__((noinline)) void write_empty_rows(
+    float* o, size_t o_stride, float* lse, size_t lse_stride, int nh, int D) {
   for (int i = threadIdx.x; i < nh * D; i += blockDim.x) {
     const int g = i / D;
-    o_dst<D>(a, b, h0 + g, s)[i - g * D] = 0.f;
+    o[g * o_stride + (i - g * D)] = 0.f;
   }
-  for (int g = threadIdx.x; g < nh; g += blockDim.x) {
-    float* l = lse_dst(a, b, h0 + g, s);
-    if (l) *l = -INFINITY;
-  }
+  if (lse)
+    for (int g = threadIdx.x; g < nh; g += blockDim.x) lse[g * lse_stride] = -INFINITY;
+}
+
+template <int D>
+__device__ __forceinline__ void write_empty(const SplitArgs& a, int b, int h0,
+                                            int nh, int s) {
+  write_empty_rows(o_dst<D>(a, b, h0, s), a.final_out ? D : (size_t)a.S * D,
+                   lse_dst(a, b, h0, s), a.final_out ? 1 : (size_t)a.S, nh, D);
 }
 
 // Element offset of cache row t (t < the sequence's length) of (b, kvh).
@@ -269,13 +275,16 @@ __device__ __forceinline__ int out_dim(int cc, int i, int j) {
 // true length are zeroed once the length arrives (they may hold anything,
 // NaN included, and are multiplied by p = 0). At the end every wave parks
 // its (O, m, l) in LDS and the whole workgroup merges them in one pass.
-template <int D, int NW, int GM, bool PAGED>
+constexpr int kMaxPages = 1024;   // page ids a workgroup stages in LDS
+
+template <int D, int NW, int U, int GM, bool PAGED>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(4))) void split_mfma(SplitArgs a) {
+__attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int NV = MfmaCfg<D>::NV;
   constexpr int DP = D + 4;                 // padded LDS row
   __shared__ float mo[NW][GM][DP];
+  __shared__ int pg_s[PAGED ? kMaxPages : 1];
   __shared__ float mm[NW][GM], ml[NW][GM];
 
   const int lane = threadIdx.x & 63;
@@ -294,19 +303,39 @@ __attribute__((amdgpu_waves_per_eu(4))) void split_mfma(SplitArgs a) {
   const int nh = min(GM, a.G - hg * GM);
   const int lo = s * a.P;
   const int hi_max = min(lo + a.P, a.L);    // split end for a full history
-  if (lo >= hi_max) {                       // no sequence reaches this split
+  if (__builtin_expect(lo >= hi_max, 0)) {  // no sequence reaches this split
     write_empty<D>(a, b, h0, nh, s);
     return;
   }
 
   // Element offset of the row of token t (t a multiple of 16 below the
   // clamp bound; wave-uniform).
+  // Paged cache: the block ids of the pages this split can reach are staged
+  // in LDS once (one round trip), so no cache request waits on a table read.
+  // A split spanning more than kMaxPages pages reads the table directly.
+  const int pg0 = PAGED ? lo / a.bs : 0;
+  const int npg = PAGED ? (hi_max - 1) / a.bs - pg0 + 1 : 0;
+  const bool staged = PAGED && npg <= kMaxPages;
+  if (PAGED && staged) {
+    const int32_t* row = a.block_table + (size_t)b * a.max_blocks + pg0;
+    for (int i = threadIdx.x; i < npg; i += NW * 64) {
+      const int blk = row[i];
+      pg_s[i] = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    }
+    __syncthreads();
+  }
+
   auto group_base = [&](int t) -> size_t {
     if (!PAGED) return ((size_t)(b * a.Hkv + kvh) * a.L + t) * D;
     const int page = t / a.bs;
-    int blk = a.block_table[(size_t)b * a.max_blocks + page];
-    blk = __builtin_amdgcn_readfirstlane(blk);
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    int blk;
+    if (staged) {
+      blk = __builtin_amdgcn_readfirstlane(pg_s[page - pg0]);
+    } else {
+      blk = __builtin_amdgcn_readfirstlane(
+          a.block_table[(size_t)b * a.max_blocks + page]);
+      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    }
     return (((size_t)blk * a.Hkv + kvh) * a.bs + (t - page * a.bs)) * D;
   };
 
@@ -347,10 +376,16 @@ __attribute__((amdgpu_waves_per_eu(4))) void split_mfma(SplitArgs a) {
     }
   };
 
-  // The wave's first subtile goes out before anything else.
+  // The wave's first U subtiles go out before anything else.
   const int t_first = lo + 32 * w;
-  u32x4 k1[2][KC], v1[8];
-  if (t_first < hi_max) load_subtile(t_first, hi_max, k1, v1);
+  u32x4 kp[U][2][KC], vp[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    load_subtile(min(t_first + 32 * NW * u, (hi_max - 1) & ~15), hi_max,
+                 kp[u], vp[u]);
+  // Keep the compiler from moving the length load (and its wait) above
+  // these requests.
+  asm volatile("" ::: "memory");
 
   // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
   // scores are computed and never used.
@@ -365,7 +400,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void split_mfma(SplitArgs a) {
 
   const int len = clamp_len(a, b);
   const int hi = min(lo + a.P, len);
-  if (lo >= hi) {                           // uniform over the workgroup
+  if (__builtin_expect(lo >= hi, 0)) {      // uniform over the workgroup
     write_empty<D>(a, b, h0, nh, s);
     return;
   }
@@ -422,21 +457,30 @@ __attribute__((amdgpu_waves_per_eu(4))) void split_mfma(SplitArgs a) {
     }
   };
 
-  if (t_first < hi) {
-    if (hi < hi_max && t_first + 32 > hi) {
-      // Rows at or past hi were read speculatively: zero their V.
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t_first + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
-        if (t >= hi) v1[e] = u32x4{0u, 0u, 0u, 0u};
+  for (int u = 0; u < U; ++u) {
+    const int t0 = t_first + 32 * NW * u;
+    if (t0 < hi) {
+      if (hi < hi_max && t0 + 32 > hi) {
+        // Rows at or past hi were read speculatively: zero their V.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
+          if (t >= hi) vp[u][e] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
+      compute_subtile(t0, kp[u], vp[u]);
     }
-    compute_subtile(t_first, k1, v1);
-    for (int t0 = t_first + 32 * NW; t0 < hi; t0 += 32 * NW) {
-      u32x4 kr[2][KC], vr[8];
-      load_subtile(t0, hi, kr, vr);
-      compute_subtile(t0, kr, vr);
-    }
+  }
+  for (int t0 = t_first + 32 * NW * U; t0 < hi; t0 += 32 * NW * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      load_subtile(min(t0 + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u]);
+    // All of the block's requests go out before its first use.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t0 + 32 * NW * u < hi) compute_subtile(t0 + 32 * NW * u, kp[u], vp[u]);
   }
 
   // Per-head sum over the 4 lane groups; then park (O, m, l) in LDS.
@@ -483,31 +527,20 @@ __attribute__((amdgpu_waves_per_eu(4))) void split_mfma(SplitArgs a) {
 // ----------------------------------------------------------------------------
 // Log-sum-exp combine of split partials.
 
-constexpr int kCombThreads = 256;
-
-__device__ __forceinline__ float block_max(float x, float* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = x;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int i = 1; i < kCombThreads / 64; ++i) r = fmaxf(r, red[i]);
-  return r;
-}
-
+// One wave per (sequence, head, 16-dim slice of the output). Lane l takes
+// split group g = l/4 and dims 4*(l%4) of the slice; group g reads splits
+// g, g+16, g+32, ... . A chunk's loads (8 splits per lane) are all issued
+// before any is used, so a chunk costs one memory round trip; chunks merge
+// online, and the 16 groups are reduced with cross-lane shuffles.
 template <int D>
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
-  constexpr int C4 = D / 4;
-  constexpr int R = kCombThreads / C4;
-  __shared__ float red[kCombThreads / 64];
-  __shared__ f32x4 racc[R][C4];
-  __shared__ float rsum[R];
-
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
+  constexpr int SL = D / 16;                // slices per head
+  constexpr int CH = 8;                     // splits per lane per chunk
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x / SL;
+  const int sl = blockIdx.x - bh * SL;
   const int b = bh / a.Hq;
-  const int tid = threadIdx.x;
+  const int g = lane >> 2, qd = lane & 3;
   int n = a.S;
   if (a.seq_lens) {
     int len = a.seq_lens[b];
@@ -515,64 +548,76 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
     n = min(a.S, (len + a.P - 1) / a.P);
   }
   const float* lse = a.lse_part + (size_t)bh * a.S;
-  float mx = -INFINITY;
-  for (int s = tid; s < n; s += kCombThreads) mx = fmaxf(mx, lse[s]);
-  const float M = block_max(mx, red);
-  float* out = a.out + (size_t)bh * D;
-  if (M == -INFINITY) {
-    for (int d = tid; d < D; d += kCombThreads) out[d] = 0.f;
-    if (tid == 0 && a.lse_out) a.lse_out[bh] = -INFINITY;
-    return;
-  }
-  const int c = tid % C4, r = tid / C4;
-  const float* op = a.o_part + (size_t)bh * a.S * D + 4 * c;
+  const float* op = a.o_part + (size_t)bh * a.S * D + 16 * sl + 4 * qd;
+
+  float M = -INFINITY, z = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-#pragma unroll 4
-  for (int s = r; s < n; s += R) {
-    const float wt = fexp2((lse[s] - M) * kLog2e);
-    const f32x4 v = *reinterpret_cast<const f32x4*>(op + (size_t)s * D);
-    acc += wt * v;
-    wsum += wt;
-  }
-  racc[r][c] = acc;
-  if (c == 0) rsum[r] = wsum;
-  __syncthreads();
-  if (r == 0) {
-    f32x4 t = racc[0][c];
-    float z = rsum[0];
+  for (int base = 0; base < n; base += 16 * CH) {
+    float lv[CH];
+    f32x4 ov[CH];
 #pragma unroll
-    for (int k = 1; k < R; ++k) {
-      t += racc[k][c];
-      z += rsum[k];
+    for (int k = 0; k < CH; ++k) {
+      const int sp = base + g + 16 * k;
+      const bool ok = sp < n;
+      lv[k] = ok ? lse[sp] : -INFINITY;
+      ov[k] = ok ? *reinterpret_cast<const f32x4*>(op + (size_t)sp * D)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float inv = 1.f / z;
-    *reinterpret_cast<f32x4*>(out + 4 * c) = t * inv;
-    if (c == 0 && a.lse_out) a.lse_out[bh] = M + flog2(z) * kLn2;
+    float mx = lv[0];
+#pragma unroll
+    for (int k = 1; k < CH; ++k) mx = fmaxf(mx, lv[k]);
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float Mn = fmaxf(M, mx);           // wave-uniform
+    if (Mn == -INFINITY) continue;
+    const float f = fexp2((M - Mn) * kLog2e);
+    acc *= f;
+    z *= f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float wt = fexp2((lv[k] - Mn) * kLog2e);
+      acc += wt * ov[k];
+      z += wt;
+    }
+    M = Mn;
   }
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) {
+    acc[0] += __shfl_xor(acc[0], off);
+    acc[1] += __shfl_xor(acc[1], off);
+    acc[2] += __shfl_xor(acc[2], off);
+    acc[3] += __shfl_xor(acc[3], off);
+    z += __shfl_xor(z, off);
+  }
+  float* out = a.out + (size_t)bh * D + 16 * sl + 4 * qd;
+  if (g == 0)
+    *reinterpret_cast<f32x4*>(out) =
+        M == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / z);
+  if (lane == 0 && sl == 0 && a.lse_out)
+    a.lse_out[bh] = M == -INFINITY ? -INFINITY : M + flog2(z) * kLn2;
 }
 
-// Waves per workgroup for the MFMA kernel. Measured on MI355X: about two
-// subtiles per wave is best for short splits; more waves per workgroup make
-// the end-of-split merge and the workgroup's slowest wave costlier.
-int mfma_waves(int P) {
+// Launch shape of the MFMA kernel for a split of P tokens: waves per
+// workgroup and subtiles each wave requests at once. Measured on MI355X
+// (64K, 256K and batch-64 histories): short splits want about two subtiles
+// per wave (4 or 8 waves); long splits run best with 4 waves each holding
+// two subtiles in flight (2 waves per SIMD).
+struct MfmaShape { int nw, u; };
+MfmaShape mfma_shape(int P) {
   const int nsub = (P + 31) / 32;
-  return nsub >= 16 ? 8 : 4;
+  if (nsub > 16) return {4, 2};
+  if (nsub > 8) return {8, 1};
+  return {4, 1};
 }
 
 template <int D, bool PAGED, int GM>
-void launch_mfma_gm(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
-  switch (nw) {
-    case 16:
-      hipLaunchKernelGGL((split_mfma<D, 16, GM, PAGED>), grid, dim3(1024), 0, st, a);
-      break;
-    case 8:
-      hipLaunchKernelGGL((split_mfma<D, 8, GM, PAGED>), grid, dim3(512), 0, st, a);
-      break;
-    default:
-      hipLaunchKernelGGL((split_mfma<D, 4, GM, PAGED>), grid, dim3(256), 0, st, a);
-      break;
-  }
+void launch_mfma_gm(dim3 grid, MfmaShape m, const SplitArgs& a, hipStream_t st) {
+  if (m.nw == 8)
+    hipLaunchKernelGGL((split_mfma<D, 8, 1, GM, PAGED>), grid, dim3(512), 0, st, a);
+  else if (m.u == 2)
+    hipLaunchKernelGGL((split_mfma<D, 4, 2, GM, PAGED>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((split_mfma<D, 4, 1, GM, PAGED>), grid, dim3(256), 0, st, a);
 }
 
 template <int D, bool PAGED>
@@ -580,11 +625,11 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const int gm = s.G <= 8 ? 8 : 16;
   a.nhg = (s.G + gm - 1) / gm;
   const dim3 grid(a.S, s.Hkv * a.nhg, s.B);
-  const int nw = mfma_waves(a.P);
+  const MfmaShape m = mfma_shape(a.P);
   if (gm == 8)
-    launch_mfma_gm<D, PAGED, 8>(grid, nw, a, st);
+    launch_mfma_gm<D, PAGED, 8>(grid, m, a, st);
   else
-    launch_mfma_gm<D, PAGED, 16>(grid, nw, a, st);
+    launch_mfma_gm<D, PAGED, 16>(grid, m, a, st);
 }
 
 }  // namespace
@@ -613,11 +658,10 @@ int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
 
 int launch_combine(int D, const CombineArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(a.B * a.Hq));
   if (D == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(kCombThreads), 0, st, a);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)(a.B * a.Hq * 8)), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(kCombThreads), 0, st, a);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3((unsigned)(a.B * a.Hq * 4)), dim3(64), 0, st, a);
   return (int)hipGetLastError();
 }
 

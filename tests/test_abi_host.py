@@ -60,7 +60,7 @@ def plan(cus=256, sum_len=-1, **kw):
 def test_planner_regimes():
     # batch-one long history: spread over the CUs, 512-token splits
     assert plan() == 128
-    assert plan(num_q_heads=64, num_kv_heads=8, max_seq_len=262144) == 32
+    assert plan(num_q_heads=64, num_kv_heads=8, max_seq_len=262144) == 64
     # a batch that already fills the GPU: no split
     assert plan(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=1024) == 1
     # a short history: no split
