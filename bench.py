@@ -36,8 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 COUNTERS_FILE = os.path.join(ROOT, "profiles",
                              "split_mfma_long_gqa_64k_counters.md")
-KERNEL_SOURCE = os.path.join(ROOT, "split_kv_long_amd", "csrc",
-                             "fd_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "split_kv_long_amd", "csrc", f)
+                  for f in ("fd_kernels.hip", "fd_host.cpp")]
 
 
 def parse_args():
@@ -61,7 +61,12 @@ def parse_args():
 
 
 def kernel_source_digest() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    """Digest of the sources that decide what the split kernel does and how
+    it is launched; counters taken on other sources are not reported."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
