@@ -54,6 +54,9 @@ def parse_args():
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (for "
                         "scaling HBM byte counters)")
+    p.add_argument("--set", action="append", default=[], metavar="KEY=VALUE",
+                   help="override a workload recipe field, e.g. "
+                        "--set batch=8 --set max_seq_len=131072")
     p.add_argument("--all", action="store_true",
                    help="also time every workload (extra JSON lines, "
                         "stderr)")
@@ -82,13 +85,27 @@ def read_traffic():
     return float(t.group(1))
 
 
+def parse_overrides(items):
+    out = {}
+    for it in items:
+        k, v = it.split("=", 1)
+        if v.lower() in ("true", "false"):
+            out[k] = v.lower() == "true"
+        else:
+            try:
+                out[k] = int(v)
+            except ValueError:
+                out[k] = float(v) if v.replace(".", "", 1).isdigit() else v
+    return out
+
+
 class Bench:
-    def __init__(self, name, splits, steps):
+    def __init__(self, name, splits, steps, overrides=None):
         import torch
         import workloads
         from split_kv_long_amd import binding as fb
         self.torch, self.fb = torch, fb
-        self.w = w = workloads.make(name)
+        self.w = w = workloads.make(name, **(overrides or {}))
         self.shape = fb.make_shape(**w.shape_dict())
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         self.cus = cus
@@ -216,7 +233,8 @@ def cpu_baseline(w, target_s):
 
 def run_one(args, name, steps, warmup, with_cpu):
     import torch
-    b = Bench(name, args.splits if name == args.workload else 0, steps)
+    b = Bench(name, args.splits if name == args.workload else 0, steps,
+              parse_overrides(args.set) if name == args.workload else None)
     ms, wall = b.time_graph(b.step, steps, warmup)
     us_call = ms * 1e3 / steps
     ms_split, _ = b.time_graph(b.split_only, steps, warmup)
@@ -250,6 +268,8 @@ def run_one(args, name, steps, warmup, with_cpu):
             "paged": w.paged, "num_splits": b.S, "tokens_per_split": b.P,
             "kv_copies_rotated": b.R, "timing": "hip graph replay of all "
             "timed steps between two events",
+            "overrides": parse_overrides(args.set) if name == args.workload
+            else {},
         },
         "achieved_GBps": round(gbps, 1),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),

@@ -18,6 +18,8 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     # Keep the compiler from forming packed fp32 (v_pk_*_f32) instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Preload the first 16 kernel-argument dwords into SGPRs at dispatch.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -29,7 +29,7 @@ int check_shape(const fd_shape* s, Shape* out) {
   if (s->dtype != FD_DTYPE_F32 && s->dtype != FD_DTYPE_BF16)
     return FD_ERR_UNSUPPORTED;
   if (!isfinite(s->scale)) return FD_ERR_INVALID_ARG;
-  if (s->batch > 65535) return FD_ERR_UNSUPPORTED;       // grid z
+  if (s->batch > 65535) return FD_ERR_UNSUPPORTED;       // grid y
   if (s->block_size != 0) {
     if (s->block_size < 0 || s->block_size % 16 != 0 ||
         s->block_size > kMaxBlockSize)
@@ -51,7 +51,7 @@ int check_shape(const fd_shape* s, Shape* out) {
   r.num_blocks = s->block_size ? s->num_blocks : 0;
   r.dtype = s->dtype;
   r.scale = s->scale > 0.f ? s->scale : (float)(1.0 / sqrt((double)s->head_dim));
-  if ((int64_t)r.Hkv * head_groups(r) > 65535) return FD_ERR_UNSUPPORTED;  // grid y
+  if ((int64_t)r.Hkv * head_groups(r) > INT32_MAX) return FD_ERR_UNSUPPORTED;  // grid x
   if (out) *out = r;
   return FD_OK;
 }

@@ -113,9 +113,9 @@ __global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
   __shared__ float m_s[GH], l_s[GH], al_s[GH];
 
   const int tid = threadIdx.x;
-  const int s = blockIdx.x, b = blockIdx.z;
-  const int kvh = blockIdx.y / a.nhg;
-  const int hg = blockIdx.y - kvh * a.nhg;
+  const int s = blockIdx.z, b = blockIdx.y;
+  const int kvh = blockIdx.x / a.nhg;
+  const int hg = blockIdx.x - kvh * a.nhg;
   const int h0 = kvh * a.G + hg * GH;
   const int nh = min(GH, a.G - hg * GH);
   const int len = clamp_len(a, b);
@@ -266,6 +266,10 @@ __device__ __forceinline__ int out_dim(int cc, int i, int j) {
   return D == 128 ? 8 * m + cc : 8 * (m & 7) + 4 * (m >> 3) + cc;
 }
 
+// K and V are read with non-temporal loads: every byte is used once, and
+// keeping it out of the caches' retained set measured 10-12 % faster on
+// long histories.
+//
 // One workgroup = NW waves on one split of one (sequence, kv head, group of
 // at most GM query heads). Wave w owns the 32-token subtiles w, w+NW, ... of
 // the split, each loaded and then consumed; the other resident waves cover
@@ -277,9 +281,19 @@ __device__ __forceinline__ int out_dim(int cc, int i, int j) {
 // its (O, m, l) in LDS and the whole workgroup merges them in one pass.
 constexpr int kMaxPages = 1024;   // page ids a workgroup stages in LDS
 
-template <int D, int NW, int U, int GM, bool PAGED>
+// 16-byte cache load; NT marks it non-temporal (streamed once).
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool NT = true>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a) {
+__attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
+    const int32_t* __restrict__ bt, int bs, SplitArgs a) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int NV = MfmaCfg<D>::NV;
   constexpr int DP = D + 4;                 // padded LDS row
@@ -290,19 +304,13 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, j = lane >> 4;
-  const int s = blockIdx.x, b = blockIdx.z;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* V = static_cast<const uint16_t*>(a.v);
-  // Fetch every kernel argument in one batch before the first branch, so the
-  // first K/V requests wait for one argument round trip, not two.
-  asm volatile("" ::"s"(K), "s"(V), "s"(a.q), "s"(a.seq_lens), "s"(a.o_dst),
-               "s"(a.lse_dst), "s"(a.block_table));
-  const int kvh = blockIdx.y / a.nhg;
-  const int hg = blockIdx.y - kvh * a.nhg;
-  const int h0 = kvh * a.G + hg * GM;
-  const int nh = min(GM, a.G - hg * GM);
-  const int lo = s * a.P;
-  const int hi_max = min(lo + a.P, a.L);    // split end for a full history
+  const int s = blockIdx.z, b = blockIdx.y;
+  const int kvh = blockIdx.x / nhg;
+  const int hg = blockIdx.x - kvh * nhg;
+  const int h0 = kvh * G + hg * GM;
+  const int nh = min(GM, G - hg * GM);
+  const int lo = s * P;
+  const int hi_max = min(lo + P, L);        // split end for a full history
   if (__builtin_expect(lo >= hi_max, 0)) {  // no sequence reaches this split
     write_empty<D>(a, b, h0, nh, s);
     return;
@@ -313,30 +321,30 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a
   // Paged cache: the block ids of the pages this split can reach are staged
   // in LDS once (one round trip), so no cache request waits on a table read.
   // A split spanning more than kMaxPages pages reads the table directly.
-  const int pg0 = PAGED ? lo / a.bs : 0;
-  const int npg = PAGED ? (hi_max - 1) / a.bs - pg0 + 1 : 0;
+  const int max_blocks = a.max_blocks, num_blocks = a.num_blocks;
+  const int pg0 = PAGED ? lo / bs : 0;
+  const int npg = PAGED ? (hi_max - 1) / bs - pg0 + 1 : 0;
   const bool staged = PAGED && npg <= kMaxPages;
   if (PAGED && staged) {
-    const int32_t* row = a.block_table + (size_t)b * a.max_blocks + pg0;
+    const int32_t* row = bt + (size_t)b * max_blocks + pg0;
     for (int i = threadIdx.x; i < npg; i += NW * 64) {
       const int blk = row[i];
-      pg_s[i] = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+      pg_s[i] = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
     }
     __syncthreads();
   }
 
   auto group_base = [&](int t) -> size_t {
-    if (!PAGED) return ((size_t)(b * a.Hkv + kvh) * a.L + t) * D;
-    const int page = t / a.bs;
+    if (!PAGED) return ((size_t)(b * Hkv + kvh) * L + t) * D;
+    const int page = t / bs;
     int blk;
     if (staged) {
       blk = __builtin_amdgcn_readfirstlane(pg_s[page - pg0]);
     } else {
-      blk = __builtin_amdgcn_readfirstlane(
-          a.block_table[(size_t)b * a.max_blocks + page]);
-      blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+      blk = __builtin_amdgcn_readfirstlane(bt[(size_t)b * max_blocks + page]);
+      blk = blk < 0 ? 0 : (blk >= num_blocks ? num_blocks - 1 : blk);
     }
-    return (((size_t)blk * a.Hkv + kvh) * a.bs + (t - page * a.bs)) * D;
+    return (((size_t)blk * Hkv + kvh) * bs + (t - page * bs)) * D;
   };
 
   // Requests the subtile starting at t0 with every row clamped below `end`.
@@ -363,46 +371,57 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a
     const unsigned r1 = (unsigned)(min(n, cap1) * D + 8 * j);
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      kr[0][c] = *reinterpret_cast<const u32x4*>(K0 + r0 + 32 * c);
-      kr[1][c] = *reinterpret_cast<const u32x4*>(K1 + r1 + 32 * c);
+      kr[0][c] = ld16<NT>(K0 + r0 + 32 * c);
+      kr[1][c] = ld16<NT>(K1 + r1 + 32 * c);
     }
     const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const unsigned v0 = (unsigned)(min(4 * j + e, last0) * D + vcol);
       const unsigned v1 = (unsigned)(min(4 * j + e, cap1) * D + vcol);
-      vr[e] = *reinterpret_cast<const u32x4*>(V0 + v0);
-      vr[4 + e] = *reinterpret_cast<const u32x4*>(V1 + v1);
+      vr[e] = ld16<NT>(V0 + v0);
+      vr[4 + e] = ld16<NT>(V1 + v1);
     }
   };
 
-  // The wave's first U subtiles go out before anything else.
+  // With SPEC the wave's first U subtiles go out before anything else,
+  // clamped to the split's full-history end; without it (batches whose
+  // lengths vary, where many splits are empty or short) the length comes
+  // first and nothing past it is read.
+  int hi = hi_max;
+  if (!SPEC) {
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > L ? L : len);
+    hi = min(lo + P, len);
+    if (__builtin_expect(lo >= hi, 0)) {
+      write_empty<D>(a, b, h0, nh, s);
+      return;
+    }
+  }
   const int t_first = lo + 32 * w;
   u32x4 kp[U][2][KC], vp[U][8];
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    load_subtile(min(t_first + 32 * NW * u, (hi_max - 1) & ~15), hi_max,
-                 kp[u], vp[u]);
-  // Keep the compiler from moving the length load (and its wait) above
-  // these requests.
-  asm volatile("" ::: "memory");
+    load_subtile(min(t_first + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u]);
 
   // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
   // scores are computed and never used.
   bf16x8 qf[KC];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         ((size_t)b * a.Hq + h0 + (n < nh ? n : 0)) * D + 8 * j;
+    const uint16_t* qp =
+        Q + ((size_t)b * G * Hkv + h0 + (n < nh ? n : 0)) * D + 8 * j;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 32 * c));
   }
 
-  const int len = clamp_len(a, b);
-  const int hi = min(lo + a.P, len);
-  if (__builtin_expect(lo >= hi, 0)) {      // uniform over the workgroup
-    write_empty<D>(a, b, h0, nh, s);
-    return;
+  // With SPEC nothing branches on the length before the compute: a split
+  // past the end of its sequence computes nothing and is written as empty
+  // at the merge.
+  if (SPEC) {
+    int len = a.seq_lens[b];
+    len = len < 0 ? 0 : (len > L ? L : len);
+    hi = min(lo + P, len);
   }
 
   f32x4 o[NV];
@@ -435,13 +454,16 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(m_run, mx);
-    const float alpha = fexp2(m_run - mn);
+    // A subtile with no valid token before any valid one (mn = -inf) must
+    // leave (O, l) at zero: shift by 0 instead of -inf, so alpha = p = 0.
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fexp2(m_run - mref);
     m_run = mn;
     bf16x8 ph, pl;
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = fexp2(sv[e] - mn);
+      const float p = fexp2(sv[e] - mref);
       psum += p;
       const __bf16 hb = (__bf16)p;
       ph[e] = hb;
@@ -457,20 +479,21 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a
     }
   };
 
+  // The first U subtiles are consumed without a branch on the length (a
+  // branch would let the compiler sink their loads behind the length load).
+  // A subtile past hi is fully masked and changes nothing.
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t0 = t_first + 32 * NW * u;
-    if (t0 < hi) {
-      if (hi < hi_max && t0 + 32 > hi) {
-        // Rows at or past hi were read speculatively: zero their V.
+    // Rows at or past hi were read speculatively: zero their V.
+    if (SPEC) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
-          if (t >= hi) vp[u][e] = u32x4{0u, 0u, 0u, 0u};
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
+        if (t >= hi) vp[u][e] = u32x4{0u, 0u, 0u, 0u};
       }
-      compute_subtile(t0, kp[u], vp[u]);
     }
+    compute_subtile(t0, kp[u], vp[u]);
   }
   for (int t0 = t_first + 32 * NW * U; t0 < hi; t0 += 32 * NW * U) {
 #pragma unroll
@@ -510,16 +533,19 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(SplitArgs a
     for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, mm[ww][g]);
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
+    const float Ms = M == -INFINITY ? 0.f : M;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const float wt = fexp2(mm[ww][g] - M);
+      const float wt = fexp2(mm[ww][g] - Ms);
       acc += wt * *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
       lsum += wt * ml[ww][g];
     }
-    *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) = acc * (1.f / lsum);
+    const bool none = M == -INFINITY;       // no token in this split
+    *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) =
+        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / lsum);
     if (d == 0) {
       float* l = lse_dst(a, b, h0 + g, s);
-      if (l) *l = (M + flog2(lsum)) * kLn2;
+      if (l) *l = none ? -INFINITY : (M + flog2(lsum)) * kLn2;
     }
   }
 }
@@ -597,11 +623,21 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     a.lse_out[bh] = M == -INFINITY ? -INFINITY : M + flog2(z) * kLn2;
 }
 
+// Grid of the split kernels: x = kv head (x head group), y = sequence,
+// z = split. Workgroups are dispatched x-fastest and dealt round-robin to the
+// 8 XCDs, so this order puts every split index on every XCD (with the split
+// index fastest, XCD i would get only splits s = i mod 8: in a batch of
+// unequal lengths the low splits, which every sequence fills, would all land
+// on the same XCDs) and dispatches the always-full low splits first.
+dim3 split_grid(int units, int B, int S) {
+  return dim3((unsigned)units, (unsigned)B, (unsigned)S);
+}
+
 // Launch shape of the MFMA kernel for a split of P tokens: waves per
 // workgroup and subtiles each wave requests at once. Measured on MI355X
-// (64K, 256K and batch-64 histories): short splits want about two subtiles
-// per wave (4 or 8 waves); long splits run best with 4 waves each holding
-// two subtiles in flight (2 waves per SIMD).
+// (64K, 256K and batch-64 histories, non-temporal K/V loads): short splits
+// want about two subtiles per wave (4 or 8 waves); long splits run best with
+// 4 waves each holding two subtiles in flight (2 waves per SIMD).
 struct MfmaShape { int nw, u; };
 MfmaShape mfma_shape(int P) {
   const int nsub = (P + 31) / 32;
@@ -610,21 +646,46 @@ MfmaShape mfma_shape(int P) {
   return {4, 1};
 }
 
+// The leading scalar arguments are what a wave needs before its first K/V
+// request; they fit the 14 kernel-argument dwords gfx950 preloads into SGPRs
+// at dispatch, so no wave waits on an argument load before its first
+// request (such loads queue behind other waves' K/V traffic).
+template <int D, int NW, int U, int GM, bool PAGED, bool SPEC>
+void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((split_mfma<D, NW, U, GM, PAGED, SPEC>), grid, dim3(NW * 64), 0,
+                     st, static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
+                     a.nhg, a.G, a.block_table, a.bs, a);
+}
+
+template <int D, bool PAGED, int GM, bool SPEC>
+void launch_mfma_spec(dim3 grid, MfmaShape m, const SplitArgs& a,
+                      hipStream_t st) {
+  if (m.nw == 8)
+    launch_one<D, 8, 1, GM, PAGED, SPEC>(grid, a, st);
+  else if (m.u == 2)
+    launch_one<D, 4, 2, GM, PAGED, SPEC>(grid, a, st);
+  else
+    launch_one<D, 4, 1, GM, PAGED, SPEC>(grid, a, st);
+}
+
+// Speculative first loads pay off for a single sequence (its splits are all
+// full when the caller's bound is its length); for a batch, whose lengths
+// may differ, they could read splits that turn out empty.
 template <int D, bool PAGED, int GM>
 void launch_mfma_gm(dim3 grid, MfmaShape m, const SplitArgs& a, hipStream_t st) {
-  if (m.nw == 8)
-    hipLaunchKernelGGL((split_mfma<D, 8, 1, GM, PAGED>), grid, dim3(512), 0, st, a);
-  else if (m.u == 2)
-    hipLaunchKernelGGL((split_mfma<D, 4, 2, GM, PAGED>), grid, dim3(256), 0, st, a);
+  if (a.B == 1)
+    launch_mfma_spec<D, PAGED, GM, true>(grid, m, a, st);
   else
-    hipLaunchKernelGGL((split_mfma<D, 4, 1, GM, PAGED>), grid, dim3(256), 0, st, a);
+    launch_mfma_spec<D, PAGED, GM, false>(grid, m, a, st);
 }
 
 template <int D, bool PAGED>
 void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const int gm = s.G <= 8 ? 8 : 16;
   a.nhg = (s.G + gm - 1) / gm;
-  const dim3 grid(a.S, s.Hkv * a.nhg, s.B);
+  const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
   const MfmaShape m = mfma_shape(a.P);
   if (gm == 8)
     launch_mfma_gm<D, PAGED, 8>(grid, m, a, st);
@@ -646,7 +707,7 @@ int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
       else launch_mfma<64, false>(s, a, st);
     }
   } else {
-    const dim3 grid(a.S, s.Hkv * a.nhg, s.B);
+    const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
     const dim3 block(kGenThreads);
     if (s.D == 128)
       hipLaunchKernelGGL((split_generic<float, 128>), grid, block, 0, st, a);

@@ -45,6 +45,12 @@ SPECS = {
     "short_batch": dict(
         wid=5, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
         max_seq_len=1024, dtype=BF16, scale=None, paged=False),
+    # The ragged batch's lengths in a contiguous [B, Hkv, L, D] cache, to
+    # separate paging cost from ragged-length imbalance when measuring.
+    "ragged_contig": dict(
+        wid=4, batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        max_seq_len=32768, min_seq_len=512, dtype=BF16, scale=None,
+        paged=False),
 }
 
 ORDER = ["tiny_mha", "long_gqa_64k", "ultra_long_256k", "ragged_paged",
