@@ -43,6 +43,35 @@ __device__ __forceinline__ float flog2(float x) {
   return __builtin_amdgcn_logf(x);    // v_log_f32
 }
 
+// Butterfly exchanges across lanes l ^ 16 and l ^ 32 with gfx950's
+// v_permlane16_swap / v_permlane32_swap (plain VALU, no LDS round trip):
+// with both operands equal to x, the two results hold x from each half, so
+// combining them gives every lane the pair's reduction.
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int clamp_len(const SplitArgs& a, int b) {
   int n = a.seq_lens[b];
   n = n < 0 ? 0 : n;
@@ -451,8 +480,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
         sv[4 * tg + i] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_x32(max_x16(mx));
     const float mn = fmaxf(m_run, mx);
     // A subtile with no valid token before any valid one (mn = -inf) must
     // leave (O, l) at zero: shift by 0 instead of -inf, so alpha = p = 0.
@@ -507,8 +535,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   }
 
   // Per-head sum over the 4 lane groups; then park (O, m, l) in LDS.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_x32(sum_x16(l_run));
   if (n < nh) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
