@@ -154,7 +154,9 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
   if (sum_seq_len < -1 || sum_seq_len > (int64_t)s.B * s.L)
     return FD_ERR_INVALID_ARG;
   const int64_t units = (int64_t)s.B * s.Hkv * head_groups(s);
-  if (units >= num_cus || s.L < 2 * kMinSplitTokens) {
+  const int64_t cmin =
+      s.dtype == FD_DTYPE_F32 ? kMinSplitTokensF32 : kMinSplitTokens;
+  if (units >= num_cus || s.L < 2 * cmin) {
     *num_splits = 1;
     return FD_OK;
   }
@@ -165,7 +167,7 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
   // Long splits: two workgroups per CU balance better and the extra
   // partials cost nothing measurable.
   if (per > kLongSplitTokens) per = (per + 1) / 2;
-  if (per < kMinSplitTokens) per = kMinSplitTokens;
+  if (per < cmin) per = cmin;
   const int64_t g = s.bs > 16 ? s.bs : 16;
   per = (per + g - 1) / g * g;
   int64_t S = (s.L + per - 1) / per;

@@ -9,10 +9,12 @@
 
 namespace fd {
 
-// Planner constants. A split is never shorter than kMinSplitTokens; the
+// Planner constants. A split is never shorter than kMinSplitTokens
+// (kMinSplitTokensF32 for fp32 caches); the
 // attended tokens are spread over about kOccupancy * num_cus workgroups,
 // twice that when the resulting splits exceed kLongSplitTokens.
 constexpr int kMinSplitTokens = 256;
+constexpr int kMinSplitTokensF32 = 64;   // fp32 path: latency-bound, split finer
 constexpr int kOccupancy = 1;
 constexpr int kLongSplitTokens = 2048;
 constexpr int kMaxSplits = 65535;

@@ -124,24 +124,30 @@ __device__ __forceinline__ size_t row_offset(const SplitArgs& a, int b, int kvh,
 // Generic LDS-tiled split kernel (fp32 FMA).
 
 constexpr int kGenThreads = 256;
-constexpr int kGenTile = 32;
 
 __device__ __forceinline__ float load_f32(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ float load_f32(const uint16_t* p, size_t i) {
   return __uint_as_float((unsigned)p[i] << 16);
 }
 
+// One workgroup per (split, kv head, group of <= 16 query heads, sequence).
+// A tile of TILE tokens (64 for D = 64, 32 for D = 128) is staged in LDS with
+// coalesced loads; scores are per-(head, token) fp32 dot products, the
+// online-softmax update is wave-parallel (one wave per head, lanes = tokens)
+// and the PV update is per-(head, dim).
 template <typename T, int D>
 __global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
   constexpr int GH = kHeadsPerGroup;
+  constexpr int TILE = D == 64 ? 64 : 32;
   __shared__ float q_s[GH][D];
   __shared__ float acc_s[GH][D];
-  __shared__ float k_s[kGenTile][D + 1];
-  __shared__ float v_s[kGenTile][D + 1];
-  __shared__ float p_s[GH][kGenTile + 1];
+  __shared__ float k_s[TILE][D + 1];
+  __shared__ float v_s[TILE][D + 1];
+  __shared__ float p_s[GH][TILE + 1];
   __shared__ float m_s[GH], l_s[GH], al_s[GH];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int s = blockIdx.z, b = blockIdx.y;
   const int kvh = blockIdx.x / a.nhg;
   const int hg = blockIdx.x - kvh * a.nhg;
@@ -166,10 +172,9 @@ __global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
     m_s[tid] = -INFINITY;
     l_s[tid] = 0.f;
   }
-  __syncthreads();
 
-  for (int t0 = lo; t0 < hi; t0 += kGenTile) {
-    const int nt = min(kGenTile, hi - t0);
+  for (int t0 = lo; t0 < hi; t0 += TILE) {
+    const int nt = min(TILE, hi - t0);
     for (int i = tid; i < nt * D; i += kGenThreads) {
       const int r = i / D, d = i - r * D;
       const size_t off = row_offset<D>(a, b, kvh, t0 + r);
@@ -177,8 +182,8 @@ __global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
       v_s[r][d] = load_f32(V, off + d);
     }
     __syncthreads();
-    for (int i = tid; i < nh * kGenTile; i += kGenThreads) {
-      const int g = i / kGenTile, jj = i - g * kGenTile;
+    for (int i = tid; i < nh * TILE; i += kGenThreads) {
+      const int g = i / TILE, jj = i - g * TILE;
       float sc = -INFINITY;
       if (jj < nt) {
         float acc = 0.f;
@@ -189,20 +194,23 @@ __global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
       p_s[g][jj] = sc;
     }
     __syncthreads();
-    if (tid < nh) {
-      float mx = -INFINITY;
-      for (int jj = 0; jj < nt; ++jj) mx = fmaxf(mx, p_s[tid][jj]);
-      const float mn = fmaxf(m_s[tid], mx);
-      const float al = fexp2(m_s[tid] - mn);
-      float sum = 0.f;
-      for (int jj = 0; jj < kGenTile; ++jj) {
-        const float e = jj < nt ? fexp2(p_s[tid][jj] - mn) : 0.f;
-        p_s[tid][jj] = e;
-        sum += e;
+    for (int g = wave; g < nh; g += kGenThreads / 64) {
+      const float x = lane < nt ? p_s[g][lane] : -INFINITY;
+      float mx = x;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mn = fmaxf(m_s[g], mx);
+      const float e = lane < nt ? fexp2(x - mn) : 0.f;
+      if (lane < TILE) p_s[g][lane] = e;
+      float sum = e;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      if (lane == 0) {
+        const float al = fexp2(m_s[g] - mn);
+        l_s[g] = l_s[g] * al + sum;
+        m_s[g] = mn;
+        al_s[g] = al;
       }
-      l_s[tid] = l_s[tid] * al + sum;
-      m_s[tid] = mn;
-      al_s[tid] = al;
     }
     __syncthreads();
     for (int i = tid; i < nh * D; i += kGenThreads) {

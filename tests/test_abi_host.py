@@ -65,9 +65,12 @@ def test_planner_regimes():
     assert plan(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=1024) == 1
     # a short history: no split
     assert plan(max_seq_len=400) == 1
-    # tiny MHA history of 512 tokens: at most 2 minimum-length splits
+    # tiny fp32 MHA history of 512 tokens: the fp32 path is latency-bound,
+    # so it takes the shorter fp32 minimum split (64 tokens) -> 8 splits
     assert plan(num_q_heads=8, num_kv_heads=8, head_dim=64, max_seq_len=512,
-                dtype="f32") <= 2
+                dtype="f32") == 8
+    assert plan(num_q_heads=8, num_kv_heads=8, head_dim=64, max_seq_len=100,
+                dtype="f32") == 1
 
 
 def test_planner_properties():
