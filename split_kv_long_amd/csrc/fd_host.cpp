@@ -227,12 +227,9 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
   c.lse_part = lse_part;
   c.out = out;
   c.lse_out = lse_out;
-  c.seq_lens = seq_lens;
   c.B = s.B;
   c.Hq = s.Hq;
   c.S = num_splits;
-  c.P = a.P;
-  c.L = s.L;
   return launch_combine(s.D, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
@@ -278,12 +275,9 @@ int fd_combine_partials(int batch, int num_q_heads, int head_dim,
   c.lse_part = lse_part;
   c.out = out;
   c.lse_out = lse_out;
-  c.seq_lens = nullptr;
   c.B = batch;
   c.Hq = num_q_heads;
   c.S = num_splits;
-  c.P = 0;
-  c.L = 0;
   return launch_combine(head_dim, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 

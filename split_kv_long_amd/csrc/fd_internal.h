@@ -56,8 +56,7 @@ struct CombineArgs {
   const float* lse_part;
   float* out;
   float* lse_out;     // may be null
-  const int32_t* seq_lens;   // may be null: then all S splits are read
-  int B, Hq, S, P, L;
+  int B, Hq, S;
 };
 
 // Launchers (fd_kernels.hip). Return hipError_t as int.

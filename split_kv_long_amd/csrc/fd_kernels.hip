@@ -592,34 +592,32 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
 // split group g = l/4 and dims 4*(l%4) of the slice; group g reads splits
 // g, g+16, g+32, ... . A chunk's loads (8 splits per lane) are all issued
 // before any is used, so a chunk costs one memory round trip; chunks merge
-// online, and the 16 groups are reduced with cross-lane shuffles.
+// online, and the 16 groups are reduced with cross-lane exchanges. Every
+// split slot holds a valid partial (empty splits are o = 0, lse = -inf and
+// get weight 0), so no length is needed, and the arguments are scalars the
+// hardware preloads: the kernel waits on nothing before its data loads.
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(64) void combine_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    float* __restrict__ out_base, float* __restrict__ lse_out, int S) {
   constexpr int SL = D / 16;                // slices per head
   constexpr int CH = 8;                     // splits per lane per chunk
   const int lane = threadIdx.x;
   const int bh = blockIdx.x / SL;
   const int sl = blockIdx.x - bh * SL;
-  const int b = bh / a.Hq;
   const int g = lane >> 2, qd = lane & 3;
-  int n = a.S;
-  if (a.seq_lens) {
-    int len = a.seq_lens[b];
-    len = len < 0 ? 0 : (len > a.L ? a.L : len);
-    n = min(a.S, (len + a.P - 1) / a.P);
-  }
-  const float* lse = a.lse_part + (size_t)bh * a.S;
-  const float* op = a.o_part + (size_t)bh * a.S * D + 16 * sl + 4 * qd;
+  const float* lse = lse_part + (size_t)bh * S;
+  const float* op = o_part + (size_t)bh * S * D + 16 * sl + 4 * qd;
 
   float M = -INFINITY, z = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < n; base += 16 * CH) {
+  for (int base = 0; base < S; base += 16 * CH) {
     float lv[CH];
     f32x4 ov[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int sp = base + g + 16 * k;
-      const bool ok = sp < n;
+      const bool ok = sp < S;
       lv[k] = ok ? lse[sp] : -INFINITY;
       ov[k] = ok ? *reinterpret_cast<const f32x4*>(op + (size_t)sp * D)
                  : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -627,8 +625,9 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     float mx = lv[0];
 #pragma unroll
     for (int k = 1; k < CH; ++k) mx = fmaxf(mx, lv[k]);
-#pragma unroll
-    for (int off = 4; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    mx = fmaxf(mx, __shfl_xor(mx, 8));
+    mx = max_x32(max_x16(mx));
     const float Mn = fmaxf(M, mx);           // wave-uniform
     if (Mn == -INFINITY) continue;
     const float f = fexp2((M - Mn) * kLog2e);
@@ -643,19 +642,21 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     M = Mn;
   }
 #pragma unroll
-  for (int off = 4; off < 64; off <<= 1) {
-    acc[0] += __shfl_xor(acc[0], off);
-    acc[1] += __shfl_xor(acc[1], off);
-    acc[2] += __shfl_xor(acc[2], off);
-    acc[3] += __shfl_xor(acc[3], off);
-    z += __shfl_xor(z, off);
+  for (int i = 0; i < 4; ++i) {
+    float x = acc[i];
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    acc[i] = sum_x32(sum_x16(x));
   }
-  float* out = a.out + (size_t)bh * D + 16 * sl + 4 * qd;
+  z += __shfl_xor(z, 4);
+  z += __shfl_xor(z, 8);
+  z = sum_x32(sum_x16(z));
+  float* out = out_base + (size_t)bh * D + 16 * sl + 4 * qd;
   if (g == 0)
     *reinterpret_cast<f32x4*>(out) =
         M == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / z);
-  if (lane == 0 && sl == 0 && a.lse_out)
-    a.lse_out[bh] = M == -INFINITY ? -INFINITY : M + flog2(z) * kLn2;
+  if (lane == 0 && sl == 0 && lse_out)
+    lse_out[bh] = M == -INFINITY ? -INFINITY : M + flog2(z) * kLn2;
 }
 
 // Grid of the split kernels: x = kv head (x head group), y = sequence,
@@ -755,9 +756,13 @@ int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
 int launch_combine(int D, const CombineArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (D == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)(a.B * a.Hq * 8)), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)(a.B * a.Hq * 8)),
+                       dim3(64), 0, st, a.o_part, a.lse_part, a.out,
+                       a.lse_out, a.S);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3((unsigned)(a.B * a.Hq * 4)), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3((unsigned)(a.B * a.Hq * 4)),
+                       dim3(64), 0, st, a.o_part, a.lse_part, a.out,
+                       a.lse_out, a.S);
   return (int)hipGetLastError();
 }
 
