@@ -317,6 +317,7 @@ __device__ __forceinline__ int out_dim(int cc, int i, int j) {
 // NaN included, and are multiplied by p = 0). At the end every wave parks
 // its (O, m, l) in LDS and the whole workgroup merges them in one pass.
 constexpr int kMaxPages = 1024;   // page ids a workgroup stages in LDS
+constexpr float kRefSlack = 8.f;  // exponent-reference slack, base 2
 
 // 16-byte cache load; NT marks it non-temporal (streamed once).
 template <bool NT>
@@ -466,6 +467,14 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // With one subtile in flight per wave the compute tail is on the critical
+  // path, and it branches (uniformly) around the masking of full subtiles
+  // and around unneeded rescales. With two in flight the branches would
+  // split the block the scheduler overlaps, and the register allocator then
+  // holds both subtiles' operands across them (lower occupancy): straight
+  // line code instead.
+  constexpr bool kSkip = U == 1;
+
   auto compute_subtile = [&](int t0, const u32x4 (&kr)[2][KC],
                              const u32x4 (&vr)[8]) {
     f32x4 sacc[2];
@@ -479,22 +488,41 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     }
     float sv[8];
     float mx = -INFINITY;
+    if (kSkip && t0 + 32 <= hi) {           // every token valid (uniform)
 #pragma unroll
-    for (int tg = 0; tg < 2; ++tg)
+      for (int tg = 0; tg < 2; ++tg)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * tg + 4 * j + i;
-        const float x = tok < hi ? sacc[tg][i] * a.scale_log2 : -INFINITY;
-        sv[4 * tg + i] = x;
-        mx = fmaxf(mx, x);
-      }
+        for (int i = 0; i < 4; ++i) {
+          const float x = sacc[tg][i] * a.scale_log2;
+          sv[4 * tg + i] = x;
+          mx = fmaxf(mx, x);
+        }
+    } else {
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = t0 + 16 * tg + 4 * j + i;
+          const float x = tok < hi ? sacc[tg][i] * a.scale_log2 : -INFINITY;
+          sv[4 * tg + i] = x;
+          mx = fmaxf(mx, x);
+        }
+    }
     mx = max_x32(max_x16(mx));
-    const float mn = fmaxf(m_run, mx);
-    // A subtile with no valid token before any valid one (mn = -inf) must
-    // leave (O, l) at zero: shift by 0 instead of -inf, so alpha = p = 0.
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float alpha = fexp2(m_run - mref);
-    m_run = mn;
+    // The exponent reference m_run moves only when the max grows by more
+    // than kRefSlack (base 2): p = 2^(s - m_run) then stays below
+    // 2^kRefSlack, exact in fp32 and as a bf16 hi/lo pair, and O and l are
+    // rescaled only when some lane's reference moves (wave-uniform skip).
+    // Before any valid token m_run = -inf; the first valid subtile moves it
+    // (alpha = 0 on the still-zero O and l).
+    const float mcand = fmaxf(m_run, mx);
+    const bool upd = mcand > m_run + kRefSlack;
+    float alpha = 1.f;
+    if (!kSkip || __builtin_amdgcn_ballot_w64(upd) != 0) {
+      alpha = upd ? fexp2(m_run - mcand) : 1.f;
+      m_run = upd ? mcand : m_run;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
     bf16x8 ph, pl;
     float psum = 0.f;
 #pragma unroll
@@ -506,9 +534,12 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
       pl[e] = (__bf16)(p - (float)hb);
     }
     l_run = l_run * alpha + psum;
+    if (!kSkip || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int cc = 0; cc < NV; ++cc) o[cc] *= alpha;
+    }
 #pragma unroll
     for (int cc = 0; cc < NV; ++cc) {
-      o[cc] *= alpha;
       const bf16x8 vk = v_kvec<D>(vr, cc, n);
       o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, ph, o[cc], 0, 0, 0);
       o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, pl, o[cc], 0, 0, 0);
@@ -522,7 +553,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   for (int u = 0; u < U; ++u) {
     const int t0 = t_first + 32 * NW * u;
     // Rows at or past hi were read speculatively: zero their V.
-    if (SPEC) {
+    if (SPEC && (!kSkip || t0 + 32 > hi)) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
