@@ -207,6 +207,38 @@ def test_custom_scale_and_large_logits():
     check(w, 16)
 
 
+@pytest.mark.parametrize("rise,period", [(30.0, 8192), (-40.0, 8192),
+                                         (200.0, 512)])
+def test_drifting_logits(rise, period):
+    """Logits that drift along the history: the first head of each group
+    gains `rise` (natural-log units) over every `period` tokens, so the
+    running maximum creeps up in small steps (30 over the whole history),
+    only falls (-40), or jumps on every 32-token tile and drops at each
+    period boundary (a sawtooth of 200 per 512 tokens)."""
+    import dataclasses
+    L = 8192
+    w = workloads.make("drift", seed=29, batch=2, num_q_heads=16,
+                       num_kv_heads=2, head_dim=128, max_seq_len=L,
+                       seq_lens=[L, 5000])
+    G = 8
+    scl = w.effective_scale
+    k = w.k.float()
+    q = w.q.float()
+    ramp = (torch.arange(L) % period).float() / (period - 1)
+    for b in range(2):
+        for h in range(2):
+            qv = q[b, h * G]
+            u = qv / float(qv @ qv)             # q.u = 1 for the first head
+            k[b, h] += (rise / scl) * ramp[:, None] * u[None, :]
+    w = dataclasses.replace(w, k=k.to(torch.bfloat16).contiguous())
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    for S in (1, 4, 32):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"drift{rise}/{period}/S={S}", "bf16", out, lse,
+                      ref_out, ref_lse)
+
+
 def test_partials_and_combine_entry_points():
     w = workloads.make("ragged_paged", seed=28, batch=3, num_q_heads=16,
                        num_kv_heads=4, head_dim=128, max_seq_len=900,
