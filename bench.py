@@ -246,7 +246,10 @@ def run_one(args, name, steps, warmup, with_cpu):
     gbps = b.bytes_alg / (us_call * 1e3)
     split_gbps = b.bytes_split / (us_split * 1e3)
     w = b.w
-    traffic = read_traffic() if name == "long_gqa_64k" else None
+    # The counters were taken on the default 64K launch (planned splits).
+    custom = name == args.workload and (args.splits or args.set)
+    traffic = (read_traffic() if name == "long_gqa_64k" and not custom
+               else None)
     rec = {
         "metric": ("decode-attn us/call + achieved HBM GB/s (% of peak), "
                    "B=1 L=64K GQA 16/2 d128"),
