@@ -281,7 +281,7 @@ def run_one(args, name, steps, warmup, with_cpu):
         "split_kernel_us": round(us_split, 3),
         "combine_kernel_us": None if us_comb is None else round(us_comb, 3),
         "roofline": {
-            "kernel": "split_mfma" if w.dtype == "bf16" else "split_generic",
+            "kernel": "split_mfma" if w.dtype == "bf16" else "split_f32",
             "bound": "hbm",
             "achieved": round(split_gbps, 1),
             "peak": HBM_PEAK_GBPS,

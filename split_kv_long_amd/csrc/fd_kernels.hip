@@ -16,8 +16,8 @@
 //                        subtiles straight from HBM into registers, and the
 //                        GQA group's QK^T and PV tile products run on the
 //                        16x16x32 bf16 matrix cores.
-//   split_generic<T, D>  fp32 (and any shape the MFMA path does not take):
-//                        LDS-tiled, plain fp32 FMA, exact fp32 products.
+//   split_f32<D>         fp32 caches: LDS-tiled, plain fp32 FMA, exact fp32
+//                        products.
 //   combine_kernel<D>    log-sum-exp reduction of the split partials.
 
 #include <hip/hip_runtime.h>
@@ -121,28 +121,29 @@ __device__ __forceinline__ size_t row_offset(const SplitArgs& a, int b, int kvh,
 }
 
 // ----------------------------------------------------------------------------
-// Generic LDS-tiled split kernel (fp32 FMA).
+// fp32 split kernel (LDS-tiled, plain fp32 FMA).
 
 constexpr int kGenThreads = 256;
 
-__device__ __forceinline__ float load_f32(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float load_f32(const uint16_t* p, size_t i) {
-  return __uint_as_float((unsigned)p[i] << 16);
-}
-
 // One workgroup per (split, kv head, group of <= 16 query heads, sequence).
-// A tile of TILE tokens (64 for D = 64, 32 for D = 128) is staged in LDS with
-// coalesced loads; scores are per-(head, token) fp32 dot products, the
-// online-softmax update is wave-parallel (one wave per head, lanes = tokens)
-// and the PV update is per-(head, dim).
-template <typename T, int D>
-__global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
+// A tile is 16 KB of K and 16 KB of V (64 tokens at D = 64, 32 at D = 128):
+// each thread requests its four 16-byte pieces of each at once, the next
+// tile's requests go out while the current one is computed, and rows past
+// the split's end are never read (zero in LDS). Scores are per-(head, token)
+// fp32 dot products, the online-softmax update is wave-parallel (one wave
+// per head, lanes = tokens) and the PV update is per-(head, dim).
+template <int D>
+__global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
   constexpr int GH = kHeadsPerGroup;
-  constexpr int TILE = D == 64 ? 64 : 32;
-  __shared__ float q_s[GH][D];
-  __shared__ float acc_s[GH][D];
-  __shared__ float k_s[TILE][D + 1];
-  __shared__ float v_s[TILE][D + 1];
+  constexpr int TILE = 4096 / D;
+  constexpr int DP = D + 4;                       // padded K row (b128 reads)
+  constexpr int C4 = D / 4;                       // 16-byte pieces per row
+  constexpr int NL = TILE * C4 / kGenThreads;     // pieces per thread: 4
+  static_assert(NL * kGenThreads == TILE * C4, "tile split");
+  __shared__ __align__(16) float q_s[GH][D];
+  __shared__ __align__(16) float acc_s[GH][D];
+  __shared__ __align__(16) float k_s[TILE][DP];
+  __shared__ __align__(16) float v_s[TILE][D];
   __shared__ float p_s[GH][TILE + 1];
   __shared__ float m_s[GH], l_s[GH], al_s[GH];
 
@@ -160,35 +161,66 @@ __global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
     write_empty<D>(a, b, h0, nh, s);
     return;
   }
-  const T* K = static_cast<const T*>(a.k);
-  const T* V = static_cast<const T*>(a.v);
-  const T* Q = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + h0) * D;
+  const float* K = static_cast<const float*>(a.k);
+  const float* V = static_cast<const float*>(a.v);
+  const float* Q = static_cast<const float*>(a.q) + ((size_t)b * a.Hq + h0) * D;
 
-  for (int i = tid; i < nh * D; i += kGenThreads) {
-    q_s[i / D][i % D] = load_f32(Q, i);
-    acc_s[i / D][i % D] = 0.f;
+  f32x4 kr[NL], vr[NL];
+  auto load_tile = [&](int t0, int nt) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int idx = tid + i * kGenThreads;
+      const int r = idx / C4, c = idx - r * C4;
+      if (r < nt) {
+        const size_t off = row_offset<D>(a, b, kvh, t0 + r) + 4 * c;
+        kr[i] = *reinterpret_cast<const f32x4*>(K + off);
+        vr[i] = *reinterpret_cast<const f32x4*>(V + off);
+      } else {
+        kr[i] = vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  int t0 = lo;
+  int nt = min(TILE, hi - t0);
+  load_tile(t0, nt);
+
+  for (int i = tid; i < nh * C4; i += kGenThreads) {
+    const int g = i / C4, c = i - g * C4;
+    *reinterpret_cast<f32x4*>(&q_s[g][4 * c]) =
+        *reinterpret_cast<const f32x4*>(Q + (size_t)g * D + 4 * c);
   }
+  for (int i = tid; i < nh * D; i += kGenThreads) acc_s[i / D][i % D] = 0.f;
   if (tid < GH) {
     m_s[tid] = -INFINITY;
     l_s[tid] = 0.f;
   }
 
-  for (int t0 = lo; t0 < hi; t0 += TILE) {
-    const int nt = min(TILE, hi - t0);
-    for (int i = tid; i < nt * D; i += kGenThreads) {
-      const int r = i / D, d = i - r * D;
-      const size_t off = row_offset<D>(a, b, kvh, t0 + r);
-      k_s[r][d] = load_f32(K, off + d);
-      v_s[r][d] = load_f32(V, off + d);
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int idx = tid + i * kGenThreads;
+      const int r = idx / C4, c = idx - r * C4;
+      *reinterpret_cast<f32x4*>(&k_s[r][4 * c]) = kr[i];
+      *reinterpret_cast<f32x4*>(&v_s[r][4 * c]) = vr[i];
     }
     __syncthreads();
+    const int t1 = t0 + TILE;
+    if (t1 < hi) load_tile(t1, min(TILE, hi - t1));   // prefetch
+
     for (int i = tid; i < nh * TILE; i += kGenThreads) {
       const int g = i / TILE, jj = i - g * TILE;
       float sc = -INFINITY;
       if (jj < nt) {
         float acc = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < D; ++d) acc = fmaf(q_s[g][d], k_s[jj][d], acc);
+#pragma unroll
+        for (int c = 0; c < C4; ++c) {
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(&q_s[g][4 * c]);
+          const f32x4 kv = *reinterpret_cast<const f32x4*>(&k_s[jj][4 * c]);
+          acc = fmaf(qv[0], kv[0], acc);
+          acc = fmaf(qv[1], kv[1], acc);
+          acc = fmaf(qv[2], kv[2], acc);
+          acc = fmaf(qv[3], kv[3], acc);
+        }
         sc = acc * a.scale_log2;
       }
       p_s[g][jj] = sc;
@@ -213,13 +245,31 @@ __global__ __launch_bounds__(kGenThreads) void split_generic(SplitArgs a) {
       }
     }
     __syncthreads();
-    for (int i = tid; i < nh * D; i += kGenThreads) {
-      const int g = i / D, d = i - g * D;
-      float acc = acc_s[g][d] * al_s[g];
-      for (int jj = 0; jj < nt; ++jj) acc = fmaf(p_s[g][jj], v_s[jj][d], acc);
-      acc_s[g][d] = acc;
+    // Rows past nt hold zeros in v_s and p_s, so the loop runs the full
+    // tile with a constant trip count and its LDS reads batch up.
+    for (int i = tid; i < nh * C4; i += kGenThreads) {
+      const int g = i / C4, c = i - g * C4;
+      const float al = al_s[g];
+      f32x4 acc = *reinterpret_cast<const f32x4*>(&acc_s[g][4 * c]);
+      acc[0] *= al;
+      acc[1] *= al;
+      acc[2] *= al;
+      acc[3] *= al;
+#pragma unroll 16
+      for (int jj = 0; jj < TILE; ++jj) {
+        const float pj = p_s[g][jj];
+        const f32x4 vv = *reinterpret_cast<const f32x4*>(&v_s[jj][4 * c]);
+        acc[0] = fmaf(pj, vv[0], acc[0]);
+        acc[1] = fmaf(pj, vv[1], acc[1]);
+        acc[2] = fmaf(pj, vv[2], acc[2]);
+        acc[3] = fmaf(pj, vv[3], acc[3]);
+      }
+      *reinterpret_cast<f32x4*>(&acc_s[g][4 * c]) = acc;
     }
     __syncthreads();
+    if (t1 >= hi) break;
+    t0 = t1;
+    nt = min(TILE, hi - t0);
   }
 
   for (int i = tid; i < nh * D; i += kGenThreads) {
@@ -310,12 +360,14 @@ __device__ __forceinline__ int out_dim(int cc, int i, int j) {
 // One workgroup = NW waves on one split of one (sequence, kv head, group of
 // at most GM query heads). Wave w owns the 32-token subtiles w, w+NW, ... of
 // the split, each loaded and then consumed; the other resident waves cover
-// the latency. A wave's first subtile is requested before the sequence
-// length is known: its rows are clamped to the split's range for a
-// full-length history, which is always inside the cache, and V rows past the
-// true length are zeroed once the length arrives (they may hold anything,
-// NaN included, and are multiplied by p = 0). At the end every wave parks
-// its (O, m, l) in LDS and the whole workgroup merges them in one pass.
+// the latency. With SPEC (batch 1) a wave's first subtiles are requested
+// before the sequence length is known: their rows are clamped to the
+// split's range for a full-length history, which is always inside the
+// cache, and V rows past the true length are zeroed once the length arrives
+// (they may hold anything, NaN included, and are multiplied by p = 0).
+// Without SPEC the length comes first and nothing past it is read. At the
+// end every wave parks its (O, m, l) in LDS and the whole workgroup merges
+// them in one pass.
 constexpr int kMaxPages = 1024;   // page ids a workgroup stages in LDS
 constexpr float kRefSlack = 8.f;  // exponent-reference slack, base 2
 
@@ -777,9 +829,9 @@ int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
     const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
     const dim3 block(kGenThreads);
     if (s.D == 128)
-      hipLaunchKernelGGL((split_generic<float, 128>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((split_f32<128>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((split_generic<float, 64>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((split_f32<64>), grid, block, 0, st, a);
   }
   return (int)hipGetLastError();
 }
