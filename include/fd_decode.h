@@ -3,14 +3,15 @@
  *
  * The operation (slavadubrov.com, "What is Flash-Decoding, and when does it
  * speed up LLMs?", sections "What is Flash-Decoding" and "Why decode needs a
- * different schedule"): during decode each active sequence contributes one
- * new query position, which attends over the sequence's whole cached key /
- * value history. Flash-Decoding cuts that history into parts handled by
- * separate workgroups; each part yields a partial output and its
- * log-sum-exp, and a reduction combines the parts, with a correct
- * normalization, into the output that attention over the complete history
- * gives. The aiexpertsdirectory.org summary of the method calls the second
- * step the "split-KV cache reduction" and warns that it costs a little for
+ * different schedule"): at each decode step a sequence adds a single query
+ * position, and that query attends over every key / value the sequence has
+ * cached so far. Flash-Decoding cuts the cached history into pieces that
+ * separate workgroups process in parallel; every piece produces its own
+ * partial result together with the log-sum-exp of its scores, and a final
+ * reduction merges the pieces, renormalising them, so that the result is
+ * exactly unsplit attention over the whole history. The
+ * aiexpertsdirectory.org summary of the method (operational constraints)
+ * notes that this reduction is a small extra cost that matters only for
  * very short histories, which the planner below accounts for.
  *
  * Per sequence b and query head h (kv head h / (Hq/Hkv)):
@@ -150,9 +151,8 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
 /*
  * The split step alone: per split s, the partial output of attention over
  * that split's positions, normalised by its own softmax sum, and its
- * log-sum-exp ("each unit computes a partial output and a log-sum-exp
- * normalization value", slavadubrov.com, "Why decode needs a different
- * schedule"). Empty splits get o = 0, lse = -inf. These partials can be
+ * log-sum-exp (the per-piece result of slavadubrov.com, "Why decode needs a
+ * different schedule"). Empty splits get o = 0, lse = -inf. These partials can be
  * combined with fd_combine_partials, also after gathering partials computed
  * over different shards of a history.
  *
@@ -171,8 +171,8 @@ int fd_decode_partials(const fd_shape* shape, const void* q,
  *   out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M},
  *   lse = M + ln sum_s e^{lse_s - M};
  * splits with lse = -inf contribute nothing; if all are -inf, out = 0 and
- * lse = -inf. ("A reduction combines them into the output that attention
- * over the complete history requires", slavadubrov.com, same section.)
+ * lse = -inf. (The merging step of slavadubrov.com, same section: it
+ * turns the pieces back into the full-history result.)
  *
  *   batch, num_q_heads, head_dim (64 or 128), num_splits >= 1
  *   o_part, lse_part  device fp32, layouts as for fd_decode_partials

@@ -7,25 +7,30 @@ library never calls it, and it imports nothing from the library.
 What it computes, and where each step comes from:
 
 * ``decode_attention`` -- the plain definition of what Flash-Decoding must
-  reproduce: softmax attention of one new query position per sequence over
-  its whole cached key/value history (slavadubrov.com, "What is
-  Flash-Decoding": "Why decode needs a different schedule" -- the partials are
-  reduced into the output that attention over the complete history requires;
-  the INT-FlashAttention related-papers page, last abstract: online softmax
-  with a running maximum and normalizer gives exact attention). It is the
-  unsplit definition, not the split algorithm.
+  reproduce: softmax attention of a sequence's single new query over its
+  whole cached key/value history (slavadubrov.com, "What is Flash-Decoding":
+  "Why decode needs a different schedule" -- merging the split results has
+  to give exactly the unsplit attention; the INT-FlashAttention
+  related-papers page, last abstract: streaming softmax that tracks the
+  running maximum and the running sum is exact, not an approximation). It is
+  the unsplit definition, not the split algorithm.
 * ``split_partials`` / ``combine_partials`` -- the two steps of the method
-  as the same page states them: each split of the history yields a partial
-  output plus its log-sum-exp, and a reduction combines them with a correct
-  normalization. These exist to check the library's split-only and
+  as the same page describes them: every piece of the history gives a
+  partial result and its log-sum-exp, and a merge renormalises and adds
+  them. These exist to check the library's split-only and
   combine-only entry points; their agreement with ``decode_attention`` is
   pinned by brute force in the tests.
+
+``fp8_e4m3_to_f64`` decodes 8-bit E4M3 cache codes from the format's
+definition; ``decode_attention`` with ``kv_dtype="fp8_e4m3"`` and per-kv-head
+scales is the definition over the dequantized cache.
 
 Every function is float64 NumPy, one (sequence, kv head) at a time.
 """
 
 from .attention import (  # noqa: F401
     bf16_bits_to_f64,
+    fp8_e4m3_to_f64,
     decode_values,
     history_rows,
     softmax_attention,

@@ -8,7 +8,9 @@ implements, written independently there):
 * positions ``0 .. seq_lens[b]-1`` are all attended, no mask inside them;
 * a history of length 0 gives output 0 and log-sum-exp -inf;
 * exposed log-sum-exp values are natural logarithms;
-* splits are contiguous token ranges of ``split_length(L, S)`` tokens.
+* splits are contiguous token ranges of ``split_length(L, S)`` tokens;
+* a quantized (8-bit float E4M3) cache is read as its decoded codes times a
+  per-kv-head scale, and attention runs over those dequantized values.
 """
 
 from __future__ import annotations
@@ -32,12 +34,33 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
         return u.view(np.float32).astype(np.float64)
 
 
+def fp8_e4m3_to_f64(codes) -> np.ndarray:
+    """8-bit E4M3 floating-point codes (OCP 8-bit float format) -> float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent field e (bias 7), bits 2..0
+    the mantissa field m. e = 0: subnormal, (m / 8) * 2^-6. e in 1..15:
+    (1 + m / 8) * 2^(e - 7), except e = 15 with m = 7, which is NaN (the
+    format has no infinities; its largest finite magnitude is 448).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6,
+                   (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (c & 0x7 == 7), np.nan, mag)
+    return sign * mag
+
+
 def decode_values(arr, dtype: str) -> np.ndarray:
-    """Raw input array -> float64 ('bf16': uint16 bit patterns; 'f32')."""
+    """Raw input array -> float64 ('bf16': uint16 bit patterns; 'f32';
+    'fp8_e4m3': uint8 codes)."""
     if dtype == "bf16":
         return bf16_bits_to_f64(arr)
     if dtype == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if dtype == "fp8_e4m3":
+        return fp8_e4m3_to_f64(arr)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -84,8 +107,9 @@ def softmax_attention(scores: np.ndarray, values: np.ndarray
 
 def decode_attention(q, k, v, seq_lens, *, dtype: str,
                      scale: Optional[float] = None, block_table=None,
-                     block_size: int = 0, token_range=None
-                     ) -> Tuple[np.ndarray, np.ndarray]:
+                     block_size: int = 0, token_range=None,
+                     kv_dtype: Optional[str] = None, k_scale=None,
+                     v_scale=None) -> Tuple[np.ndarray, np.ndarray]:
     """Decode attention of one query per (sequence, head) over its history.
 
     q [B, Hq, D]; k, v contiguous [B, Hkv, L, D] or paged pools
@@ -93,8 +117,14 @@ def decode_attention(q, k, v, seq_lens, *, dtype: str,
     Raw inputs (bf16 as uint16 bits, or float32) are decoded to float64.
     token_range=(lo, hi) restricts every sequence to positions
     lo .. min(hi, seq_lens[b]) - 1 (used for split partials).
+    Quantized caches: kv_dtype names the cache's encoding (default: dtype),
+    and k_scale / v_scale [Hkv] multiply every decoded key / value of that
+    kv head, so attention runs over the dequantized cache (the cache
+    precision the "What is Flash-Decoding" page asks comparisons to hold
+    fixed, in the low-bit form the "Faster Than Flash" abstract scans).
     Returns out [B, Hq, D] and lse [B, Hq] (natural log), float64.
     """
+    kvd = kv_dtype or dtype
     qf = decode_values(q, dtype)
     B, Hq, D = qf.shape
     Hkv = k.shape[1]
@@ -112,9 +142,13 @@ def decode_attention(q, k, v, seq_lens, *, dtype: str,
             continue
         for kvh in range(Hkv):
             kr = decode_values(history_rows(k, b, kvh, lo, hi, block_table,
-                                            block_size), dtype)
+                                            block_size), kvd)
             vr = decode_values(history_rows(v, b, kvh, lo, hi, block_table,
-                                            block_size), dtype)
+                                            block_size), kvd)
+            if k_scale is not None:
+                kr = kr * float(k_scale[kvh])
+            if v_scale is not None:
+                vr = vr * float(v_scale[kvh])
             heads = slice(kvh * G, (kvh + 1) * G)
             scores = sc * (qf[b, heads] @ kr.T)
             o, l = softmax_attention(scores, vr)
@@ -138,7 +172,9 @@ def split_length(max_seq_len: int, num_splits: int, granule: int = 16) -> int:
 
 def split_partials(q, k, v, seq_lens, num_splits: int, *, dtype: str,
                    max_seq_len: int, scale: Optional[float] = None,
-                   block_table=None, block_size: int = 0, granule: int = 16):
+                   block_table=None, block_size: int = 0, granule: int = 16,
+                   kv_dtype: Optional[str] = None, k_scale=None,
+                   v_scale=None):
     """Per-split partial outputs and log-sum-exps (the method's first step).
 
     Split s covers positions [s*P, (s+1)*P) clipped to the history, with
@@ -156,7 +192,9 @@ def split_partials(q, k, v, seq_lens, num_splits: int, *, dtype: str,
         o, l = decode_attention(q, k, v, seq_lens, dtype=dtype, scale=scale,
                                 block_table=block_table,
                                 block_size=block_size,
-                                token_range=(s * P, (s + 1) * P))
+                                token_range=(s * P, (s + 1) * P),
+                                kv_dtype=kv_dtype, k_scale=k_scale,
+                                v_scale=v_scale)
         o_part[:, :, s] = o
         lse_part[:, :, s] = l
     return o_part, lse_part

@@ -372,3 +372,176 @@ def test_planted_mistake_is_caught(kind):
         except (AssertionError, IndexError, ValueError, FloatingPointError):
             failed.append(chk.__name__)
     assert failed, f"mutant {kind} passed every pin"
+
+
+# ----------------------------------------------- 8-bit float (E4M3) caches
+
+FP8_HAND = {
+    # code: value, each derived by hand from the E4M3 layout
+    # (sign | 4-bit exponent, bias 7 | 3-bit mantissa).
+    0x00: 0.0,
+    0x38: 1.0,                 # e = 7, m = 0
+    0x3C: 1.5,                 # e = 7, m = 4
+    0x40: 2.0,                 # e = 8
+    0x7E: 448.0,               # e = 15, m = 6: largest finite
+    0x08: 2.0 ** -6,           # smallest normal
+    0x01: 2.0 ** -9,           # smallest subnormal: (1/8) * 2^-6
+    0x07: 7 * 2.0 ** -9,       # largest subnormal
+    0xB8: -1.0,
+    0xC4: -3.0,                # e = 8, m = 4
+}
+
+
+def test_fp8_decode_hand_values():
+    got = oracle.fp8_e4m3_to_f64(np.array(list(FP8_HAND), dtype=np.uint8))
+    assert np.array_equal(got, np.array(list(FP8_HAND.values())))
+    nan = oracle.fp8_e4m3_to_f64(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.all(np.isnan(nan))
+    neg0 = oracle.fp8_e4m3_to_f64(np.array([0x80], dtype=np.uint8))
+    assert neg0[0] == 0.0 and math.copysign(1.0, neg0[0]) < 0
+
+
+def check_fp8_codes(decode):
+    """Every code against torch's float8_e4m3fn (the same OCP format)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = decode(codes.numpy())
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def _fp8_case(seed, B=2, Hq=8, Hkv=2, D=16, L=29):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    k8 = (torch.randn(B, Hkv, L, D, generator=g) * 3).to(torch.float8_e4m3fn)
+    v8 = (torch.randn(B, Hkv, L, D, generator=g) * 3).to(torch.float8_e4m3fn)
+    ks = torch.rand(Hkv, generator=g) * 0.5 + 0.05
+    vs = torch.rand(Hkv, generator=g) * 2.0 + 0.5
+    lens = np.array([L, L // 2 + 1][:B])
+    return q, k8, v8, ks, vs, lens
+
+
+def check_fp8_sdpa(attn_q8, seed=30):
+    """Attention over an E4M3 cache with per-kv-head scales against torch's
+    float64 scaled_dot_product_attention on the cache torch dequantizes."""
+    q, k8, v8, ks, vs, lens = _fp8_case(seed)
+    B, Hq, D = q.shape
+    Hkv = k8.shape[1]
+    G = Hq // Hkv
+    out, lse = attn_q8(q.view(torch.uint16).numpy(),
+                       k8.view(torch.uint8).numpy(),
+                       v8.view(torch.uint8).numpy(), lens,
+                       ks.numpy(), vs.numpy())
+    kd = k8.to(torch.float64) * ks.double()[None, :, None, None]
+    vd = v8.to(torch.float64) * vs.double()[None, :, None, None]
+    for b in range(B):
+        n = int(lens[b])
+        qt = q[b].double()[None, :, None, :]
+        kt = kd[b, :, :n].repeat_interleave(G, dim=0)[None]
+        vt = vd[b, :, :n].repeat_interleave(G, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+        assert np.allclose(out[b], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+        s = (qt[0, :, 0, None, :] * kt[0]).sum(-1) / math.sqrt(D)
+        assert np.allclose(lse[b], torch.logsumexp(s, -1).numpy(), atol=1e-12)
+
+
+def check_fp8_equals_bf16_of_same_values(attn_q8, seed=31):
+    """Power-of-two scales: every dequantized value is exact in bf16, so the
+    quantized path must equal the (separately pinned) bf16 path on it."""
+    q, k8, v8, _, _, lens = _fp8_case(seed)
+    Hkv = k8.shape[1]
+    ks = torch.tensor([0.25, 2.0])[:Hkv]
+    vs = torch.tensor([4.0, 0.5])[:Hkv]
+    out, lse = attn_q8(q.view(torch.uint16).numpy(),
+                       k8.view(torch.uint8).numpy(),
+                       v8.view(torch.uint8).numpy(), lens,
+                       ks.numpy(), vs.numpy())
+    kb = (k8.to(torch.float32) * ks[None, :, None, None]).to(torch.bfloat16)
+    vb = (v8.to(torch.float32) * vs[None, :, None, None]).to(torch.bfloat16)
+    assert torch.equal(kb.float(), k8.float() * ks[None, :, None, None])
+    o2, l2 = oracle.decode_attention(q.view(torch.uint16).numpy(),
+                                     kb.view(torch.uint16).numpy(),
+                                     vb.view(torch.uint16).numpy(), lens,
+                                     dtype="bf16")
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+
+
+def _attn_q8(q, k, v, lens, ks, vs):
+    return oracle.decode_attention(q, k, v, lens, dtype="bf16",
+                                   kv_dtype="fp8_e4m3", k_scale=ks,
+                                   v_scale=vs)
+
+
+def test_fp8_codes_match_torch():
+    check_fp8_codes(oracle.fp8_e4m3_to_f64)
+
+
+def test_fp8_attention_matches_torch_sdpa():
+    check_fp8_sdpa(_attn_q8)
+
+
+def test_fp8_attention_equals_bf16_on_exact_values():
+    check_fp8_equals_bf16_of_same_values(_attn_q8)
+
+
+def test_fp8_split_partials_recombine():
+    q, k8, v8, ks, vs, lens = _fp8_case(32, L=100)
+    args = (q.view(torch.uint16).numpy(), k8.view(torch.uint8).numpy(),
+            v8.view(torch.uint8).numpy(), lens)
+    ref = _attn_q8(*args, ks.numpy(), vs.numpy())
+    op, lp = oracle.split_partials(*args, 7, dtype="bf16", max_seq_len=100,
+                                   kv_dtype="fp8_e4m3", k_scale=ks.numpy(),
+                                   v_scale=vs.numpy())
+    out, lse = oracle.combine_partials(op, lp)
+    assert np.allclose(out, ref[0], atol=1e-13)
+    assert np.allclose(lse, ref[1], atol=1e-13)
+
+
+def _fp8_decode_mutant(kind):
+    def decode(codes):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        e = (c >> 3) & 0xF
+        m = (c & 0x7).astype(np.float64)
+        bias = 8 if kind == "bias8" else 7
+        if kind == "subnormal_as_normal":
+            mag = (1.0 + m / 8.0) * np.exp2((e - bias).astype(np.float64))
+        else:
+            mag = np.where(e == 0, (m / 8.0) * 2.0 ** (1 - bias),
+                           (1.0 + m / 8.0) * np.exp2((e - bias).astype(np.float64)))
+        if kind != "no_nan":
+            mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+        return sign * mag
+    return decode
+
+
+FP8_MUTANTS = ["bias8", "subnormal_as_normal", "no_nan", "scale_swap",
+               "no_v_scale", "k_scale_on_both"]
+
+
+@pytest.mark.parametrize("kind", FP8_MUTANTS)
+def test_fp8_planted_mistake_is_caught(kind, monkeypatch):
+    decode = oracle.fp8_e4m3_to_f64
+    if kind in ("bias8", "subnormal_as_normal", "no_nan"):
+        decode = _fp8_decode_mutant(kind)
+        monkeypatch.setattr(oa, "fp8_e4m3_to_f64", decode)
+
+    def attn(q, k, v, lens, ks, vs):
+        if kind == "scale_swap":
+            ks, vs = vs, ks
+        elif kind == "no_v_scale":
+            vs = None
+        elif kind == "k_scale_on_both":
+            vs = ks
+        return _attn_q8(q, k, v, lens, ks, vs)
+
+    failed = []
+    for chk, arg in ((check_fp8_codes, decode), (check_fp8_sdpa, attn),
+                     (check_fp8_equals_bf16_of_same_values, attn)):
+        try:
+            with np.errstate(all="ignore"):
+                chk(arg)
+        except AssertionError:
+            failed.append(chk.__name__)
+    assert failed, f"mutant {kind} passed every fp8 pin"
