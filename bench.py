@@ -120,6 +120,9 @@ class Bench:
         self.bt = None if w.block_table is None else w.block_table.to(dev)
         self.ks = [w.k.to(dev) for _ in range(self.R)]
         self.vs = [w.v.to(dev) for _ in range(self.R)]
+        self.fp8 = w.cache_dtype == "fp8_e4m3"
+        self.kscale = None if w.k_scale is None else w.k_scale.to(dev)
+        self.vscale = None if w.v_scale is None else w.v_scale.to(dev)
         B, Hq, D = w.batch, w.num_q_heads, w.head_dim
         self.out = torch.empty(B, Hq, D, device=dev)
         self.lse = torch.empty(B, Hq, device=dev)
@@ -135,15 +138,27 @@ class Bench:
 
     def step(self, i):
         r = i % self.R
-        self.fb.fd_decode_attn(self.shape, self.q, self.ks[r], self.vs[r],
-                               self.bt, self.lens, self.S, self.ws, self.out,
-                               self.lse)
+        if self.fp8:
+            self.fb.fd_decode_attn_fp8(self.shape, self.q, self.ks[r],
+                                       self.vs[r], self.kscale, self.vscale,
+                                       self.bt, self.lens, self.S, self.ws,
+                                       self.out, self.lse)
+        else:
+            self.fb.fd_decode_attn(self.shape, self.q, self.ks[r], self.vs[r],
+                                   self.bt, self.lens, self.S, self.ws,
+                                   self.out, self.lse)
 
     def split_only(self, i):
         r = i % self.R
-        self.fb.fd_decode_partials(self.shape, self.q, self.ks[r], self.vs[r],
-                                   self.bt, self.lens, self.S, self.op,
-                                   self.lp)
+        if self.fp8:
+            self.fb.fd_decode_partials_fp8(self.shape, self.q, self.ks[r],
+                                           self.vs[r], self.kscale,
+                                           self.vscale, self.bt, self.lens,
+                                           self.S, self.op, self.lp)
+        else:
+            self.fb.fd_decode_partials(self.shape, self.q, self.ks[r],
+                                       self.vs[r], self.bt, self.lens, self.S,
+                                       self.op, self.lp)
 
     def combine_only(self, i):
         w = self.w
@@ -220,7 +235,9 @@ def cpu_baseline(w, target_s):
         oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
                                 dtype=a["dtype"], scale=a["scale"],
                                 block_table=a["block_table"],
-                                block_size=a["block_size"])
+                                block_size=a["block_size"],
+                                kv_dtype=a["kv_dtype"], k_scale=a["k_scale"],
+                                v_scale=a["v_scale"])
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= target_s or len(times) >= 50:
             break
@@ -268,7 +285,8 @@ def run_one(args, name, steps, warmup, with_cpu):
             "workload": name, "batch": w.batch, "num_q_heads": w.num_q_heads,
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "max_seq_len": w.max_seq_len, "sum_seq_len": w.sum_seq_len(),
-            "paged": w.paged, "num_splits": b.S, "tokens_per_split": b.P,
+            "paged": w.paged, "kv_dtype": w.cache_dtype,
+            "num_splits": b.S, "tokens_per_split": b.P,
             "kv_copies_rotated": b.R, "timing": "hip graph replay of all "
             "timed steps between two events",
             "overrides": parse_overrides(args.set) if name == args.workload
@@ -318,7 +336,7 @@ def main():
                   not args.no_cpu_baseline)
     if args.all:
         import workloads
-        for name in workloads.ORDER:
+        for name in workloads.ORDER + workloads.EXTRA:
             if name == args.workload:
                 continue
             r = run_one(args, name, args.steps, args.warmup, False)

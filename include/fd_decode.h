@@ -59,7 +59,12 @@ typedef enum fd_status {
 
 typedef enum fd_dtype {
   FD_DTYPE_F32 = 0,         /* q, k, v are IEEE float32 */
-  FD_DTYPE_BF16 = 1         /* q, k, v are bfloat16; math in fp32 */
+  FD_DTYPE_BF16 = 1,        /* q, k, v are bfloat16; math in fp32 */
+  FD_DTYPE_FP8_E4M3 = 2     /* q bfloat16; k, v 8-bit E4M3 codes (OCP 8-bit
+                               float: sign, 4-bit exponent with bias 7,
+                               3-bit mantissa, no infinities) with one fp32
+                               scale per kv head for K and one for V; only
+                               the *_fp8 entry points take it */
 } fd_dtype;
 
 /*
@@ -147,6 +152,8 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
                    const int32_t* seq_lens, int num_splits, void* workspace,
                    size_t workspace_bytes, float* out, float* lse_out,
                    void* stream);
+/* (shape->dtype FD_DTYPE_FP8_E4M3 is rejected here with
+ * FD_ERR_INVALID_ARG: such a cache needs its scales, fd_decode_attn_fp8.) */
 
 /*
  * The split step alone: per split s, the partial output of attention over
@@ -165,6 +172,39 @@ int fd_decode_partials(const fd_shape* shape, const void* q,
                        const int32_t* block_table, const int32_t* seq_lens,
                        int num_splits, float* o_part, float* lse_part,
                        void* stream);
+
+/*
+ * Decode attention over an 8-bit float cache (shape->dtype must be
+ * FD_DTYPE_FP8_E4M3): every key of kv head g is decode(code) * k_scale[g]
+ * and every value decode(code) * v_scale[g], and the result is the
+ * attention above over those dequantized values, in fp32 (the comparison
+ * the slavadubrov.com page asks for holds the cache precision fixed,
+ * section "Interpret the reported result"; the "Faster Than Flash" page's
+ * abstract reads its cache in low-bit form). Half the bytes of a bf16 cache
+ * per token, so about half the time on this memory-bound path.
+ *
+ *   q                 device bf16 [batch, Hq, head_dim], 16-byte aligned
+ *   k_cache, v_cache  device uint8 codes, layouts as for fd_decode_attn
+ *                     (one byte per element), 16-byte aligned
+ *   k_scale, v_scale  device fp32 [num_kv_heads], 4-byte aligned
+ * Other arguments, outputs and errors as for fd_decode_attn.
+ */
+int fd_decode_attn_fp8(const fd_shape* shape, const void* q,
+                       const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int num_splits, void* workspace,
+                       size_t workspace_bytes, float* out, float* lse_out,
+                       void* stream);
+
+/* The split step alone over an 8-bit float cache: as fd_decode_partials,
+ * with the cache and scales of fd_decode_attn_fp8. */
+int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table,
+                           const int32_t* seq_lens, int num_splits,
+                           float* o_part, float* lse_part, void* stream);
 
 /*
  * The reduction step alone: for each (b, h), with M = max_s lse_part[b,h,s],

@@ -22,10 +22,13 @@ FD_ERR_HIP = -4
 
 FD_DTYPE_F32 = 0
 FD_DTYPE_BF16 = 1
-_DTYPES = {"f32": FD_DTYPE_F32, "bf16": FD_DTYPE_BF16}
+FD_DTYPE_FP8_E4M3 = 2
+_DTYPES = {"f32": FD_DTYPE_F32, "bf16": FD_DTYPE_BF16,
+           "fp8_e4m3": FD_DTYPE_FP8_E4M3}
 
 SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_decode_attn",
-           "fd_decode_partials", "fd_combine_partials", "fd_status_str",
+           "fd_decode_partials", "fd_decode_attn_fp8",
+           "fd_decode_partials_fp8", "fd_combine_partials", "fd_status_str",
            "fd_version"]
 
 
@@ -68,6 +71,10 @@ def load() -> ctypes.CDLL:
     lib.fd_workspace_size.argtypes = [SH, I, ctypes.POINTER(SZ)]
     lib.fd_decode_attn.argtypes = [SH, P, P, P, P, P, I, P, SZ, P, P, P]
     lib.fd_decode_partials.argtypes = [SH, P, P, P, P, P, I, P, P, P]
+    lib.fd_decode_attn_fp8.argtypes = [SH, P, P, P, P, P, P, P, I, P, SZ, P,
+                                       P, P]
+    lib.fd_decode_partials_fp8.argtypes = [SH, P, P, P, P, P, P, P, I, P, P,
+                                           P]
     lib.fd_combine_partials.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.fd_status_str.argtypes = [I]
     lib.fd_status_str.restype = ctypes.c_char_p
@@ -150,6 +157,31 @@ def fd_decode_partials(shape: FdShape, q, k_cache, v_cache, block_table,
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_table), _ptr(seq_lens), int(num_splits), _ptr(o_part),
         _ptr(lse_part), _stream(stream)))
+
+
+def fd_decode_attn_fp8(shape: FdShape, q, k_cache, v_cache, k_scale, v_scale,
+                       block_table, seq_lens, num_splits: int, workspace,
+                       out, lse_out=None, stream=None,
+                       workspace_bytes: Optional[int] = None) -> None:
+    """Enqueue decode attention over an 8-bit E4M3 cache with per-kv-head
+    fp32 scales (shape dtype "fp8_e4m3", q bf16)."""
+    ws_bytes = (workspace_bytes if workspace_bytes is not None else
+                (0 if workspace is None or isinstance(workspace, int)
+                 else workspace.numel() * workspace.element_size()))
+    _check("fd_decode_attn_fp8", load().fd_decode_attn_fp8(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+        int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse_out),
+        _stream(stream)))
+
+
+def fd_decode_partials_fp8(shape: FdShape, q, k_cache, v_cache, k_scale,
+                           v_scale, block_table, seq_lens, num_splits: int,
+                           o_part, lse_part, stream=None) -> None:
+    _check("fd_decode_partials_fp8", load().fd_decode_partials_fp8(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+        int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(stream)))
 
 
 def fd_combine_partials(batch: int, num_q_heads: int, head_dim: int,

@@ -26,7 +26,8 @@ int check_shape(const fd_shape* s, Shape* out) {
   if (s->max_seq_len < 0) return FD_ERR_INVALID_ARG;
   if (s->head_dim <= 0 || (s->head_dim % 16) != 0) return FD_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return FD_ERR_UNSUPPORTED;
-  if (s->dtype != FD_DTYPE_F32 && s->dtype != FD_DTYPE_BF16)
+  if (s->dtype != FD_DTYPE_F32 && s->dtype != FD_DTYPE_BF16 &&
+      s->dtype != FD_DTYPE_FP8_E4M3)
     return FD_ERR_UNSUPPORTED;
   if (!isfinite(s->scale)) return FD_ERR_INVALID_ARG;
   if (s->batch > 65535) return FD_ERR_UNSUPPORTED;       // grid y
@@ -98,6 +99,18 @@ static int check_inputs(const Shape& s, const void* q, const void* k,
   } else if (block_table) {
     return FD_ERR_INVALID_ARG;
   }
+  return FD_OK;
+}
+
+// E4M3 caches come with their scales and only through the *_fp8 calls.
+static int check_scales(const Shape& s, const float* ks, const float* vs,
+                        bool fp8_call) {
+  if ((s.dtype == FD_DTYPE_FP8_E4M3) != fp8_call) return FD_ERR_INVALID_ARG;
+  if (!fp8_call) return FD_OK;
+  if (!ks || !vs) return FD_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ks) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(vs) & 3u) != 0)
+    return FD_ERR_INVALID_ARG;
   return FD_OK;
 }
 
@@ -188,16 +201,25 @@ int fd_workspace_size(const fd_shape* shape, int num_splits, size_t* bytes) {
   return FD_OK;
 }
 
-int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
-                   const void* v_cache, const int32_t* block_table,
-                   const int32_t* seq_lens, int num_splits, void* workspace,
-                   size_t ws_bytes, float* out, float* lse_out, void* stream) {
+}  // extern "C"
+
+namespace fd {
+
+static int decode_attn(const fd_shape* shape, const void* q,
+                       const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale,
+                       bool fp8_call, const int32_t* block_table,
+                       const int32_t* seq_lens, int num_splits,
+                       void* workspace, size_t ws_bytes, float* out,
+                       float* lse_out, void* stream) {
   Shape s;
   int st = check_shape(shape, &s);
   if (st != FD_OK) return st;
   st = check_splits(s, num_splits);
   if (st != FD_OK) return st;
   st = check_inputs(s, q, k_cache, v_cache, block_table, seq_lens);
+  if (st != FD_OK) return st;
+  st = check_scales(s, k_scale, v_scale, fp8_call);
   if (st != FD_OK) return st;
   if (!out || !aligned16(out)) return FD_ERR_INVALID_ARG;
   if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0)
@@ -209,6 +231,8 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
   }
   SplitArgs a = make_split_args(s, q, k_cache, v_cache, block_table, seq_lens,
                                 num_splits);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   if (num_splits == 1) {
     a.o_dst = out;
     a.lse_dst = lse_out;
@@ -233,11 +257,12 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
   return launch_combine(s.D, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
-int fd_decode_partials(const fd_shape* shape, const void* q,
-                       const void* k_cache, const void* v_cache,
-                       const int32_t* block_table, const int32_t* seq_lens,
-                       int num_splits, float* o_part, float* lse_part,
-                       void* stream) {
+static int decode_partials(const fd_shape* shape, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           bool fp8_call, const int32_t* block_table,
+                           const int32_t* seq_lens, int num_splits,
+                           float* o_part, float* lse_part, void* stream) {
   Shape s;
   int st = check_shape(shape, &s);
   if (st != FD_OK) return st;
@@ -245,15 +270,64 @@ int fd_decode_partials(const fd_shape* shape, const void* q,
   if (st != FD_OK) return st;
   st = check_inputs(s, q, k_cache, v_cache, block_table, seq_lens);
   if (st != FD_OK) return st;
+  st = check_scales(s, k_scale, v_scale, fp8_call);
+  if (st != FD_OK) return st;
   if (!o_part || !lse_part || !aligned16(o_part) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0)
     return FD_ERR_INVALID_ARG;
   SplitArgs a = make_split_args(s, q, k_cache, v_cache, block_table, seq_lens,
                                 num_splits);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.o_dst = o_part;
   a.lse_dst = lse_part;
   a.final_out = 0;
   return launch_split(s, a, stream) == 0 ? FD_OK : FD_ERR_HIP;
+}
+
+}  // namespace fd
+
+extern "C" {
+
+int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* block_table,
+                   const int32_t* seq_lens, int num_splits, void* workspace,
+                   size_t ws_bytes, float* out, float* lse_out, void* stream) {
+  return decode_attn(shape, q, k_cache, v_cache, nullptr, nullptr, false,
+                     block_table, seq_lens, num_splits, workspace, ws_bytes,
+                     out, lse_out, stream);
+}
+
+int fd_decode_attn_fp8(const fd_shape* shape, const void* q,
+                       const void* k_cache, const void* v_cache,
+                       const float* k_scale, const float* v_scale,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int num_splits, void* workspace, size_t ws_bytes,
+                       float* out, float* lse_out, void* stream) {
+  return decode_attn(shape, q, k_cache, v_cache, k_scale, v_scale, true,
+                     block_table, seq_lens, num_splits, workspace, ws_bytes,
+                     out, lse_out, stream);
+}
+
+int fd_decode_partials(const fd_shape* shape, const void* q,
+                       const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int num_splits, float* o_part, float* lse_part,
+                       void* stream) {
+  return decode_partials(shape, q, k_cache, v_cache, nullptr, nullptr, false,
+                         block_table, seq_lens, num_splits, o_part, lse_part,
+                         stream);
+}
+
+int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_table,
+                           const int32_t* seq_lens, int num_splits,
+                           float* o_part, float* lse_part, void* stream) {
+  return decode_partials(shape, q, k_cache, v_cache, k_scale, v_scale, true,
+                         block_table, seq_lens, num_splits, o_part, lse_part,
+                         stream);
 }
 
 int fd_combine_partials(int batch, int num_q_heads, int head_dim,

@@ -24,6 +24,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fd_internal.h"
 
 namespace fd {
@@ -32,6 +34,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.44269504088896341f;
@@ -371,21 +375,47 @@ __device__ __forceinline__ int out_dim(int cc, int i, int j) {
 constexpr int kMaxPages = 1024;   // page ids a workgroup stages in LDS
 constexpr float kRefSlack = 8.f;  // exponent-reference slack, base 2
 
-// 16-byte cache load; NT marks it non-temporal (streamed once).
-template <bool NT>
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+// 16- and 8-byte cache loads; NT marks them non-temporal (streamed once).
+template <bool NT, typename T>
+__device__ __forceinline__ u32x4 ld16(const T* p) {
   if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return *reinterpret_cast<const u32x4*>(p);
 }
+template <bool NT, typename T>
+__device__ __forceinline__ u32x2 ld8(const T* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return *reinterpret_cast<const u32x2*>(p);
+}
 
-template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool NT = true>
+// Four 8-bit E4M3 codes (one dword, lowest byte first) -> four bf16, exact
+// (every E4M3 value is a bf16 value), with gfx950's packed conversion.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16x4(unsigned w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return uint2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
+// F8: the cache holds 8-bit E4M3 codes with one scale per kv head for K and
+// one for V. A lane then reads 16 bytes = 16 dims of a key row per request
+// (dims 16(j + 4c)..+15) and 8 bytes = 8 dims of a value row, converts them
+// to bf16 in registers (exact) and runs the same bf16 products; the key
+// scale is folded into the logit scale and the value scale into the final
+// normalisation. The QK contraction order is free, so Q's fragments simply
+// follow the same dim order.
+template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8,
+          bool NT = true>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+__attribute__((amdgpu_waves_per_eu(U >= (F8 ? 4 : 2) ? 2 : 3))) void split_mfma(
+    const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
     const int32_t* __restrict__ bt, int bs, SplitArgs a) {
+  using KT = typename std::conditional<F8, uint8_t, uint16_t>::type;
+  using VT = typename std::conditional<F8, u32x2, u32x4>::type;
+  const KT* __restrict__ K = static_cast<const KT*>(Kp);
+  const KT* __restrict__ V = static_cast<const KT*>(Vp);
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int NV = MfmaCfg<D>::NV;
+  constexpr int KL = F8 ? D / 64 : D / 32;   // 16-byte K requests per row
   constexpr int DP = D + 4;                 // padded LDS row
   __shared__ float mo[NW][GM][DP];
   __shared__ int pg_s[PAGED ? kMaxPages : 1];
@@ -438,14 +468,14 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   };
 
   // Requests the subtile starting at t0 with every row clamped below `end`.
-  auto load_subtile = [&](int t0, int end, u32x4 (&kr)[2][KC],
-                          u32x4 (&vr)[8]) {
+  auto load_subtile = [&](int t0, int end, u32x4 (&kr)[2][KL],
+                          VT (&vr)[8]) {
     const int last0 = min(15, end - 1 - t0);
     const int last1 = end - 1 - (t0 + 16);
-    const uint16_t* K0 = K + group_base(t0);
-    const uint16_t* V0 = V + group_base(t0);
-    const uint16_t* K1;
-    const uint16_t* V1;
+    const KT* K0 = K + group_base(t0);
+    const KT* V0 = V + group_base(t0);
+    const KT* K1;
+    const KT* V1;
     int cap1;
     if (last1 >= 0) {
       const size_t g1 = group_base(t0 + 16);
@@ -457,20 +487,28 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
       V1 = V0 + (size_t)last0 * D;
       cap1 = 0;
     }
-    const unsigned r0 = (unsigned)(min(n, last0) * D + 8 * j);
-    const unsigned r1 = (unsigned)(min(n, cap1) * D + 8 * j);
+    // Element offsets (16-byte requests): bf16 K dims 8j + 32c, E4M3 K
+    // dims 16j + 64c.
+    constexpr int KJ = F8 ? 16 : 8, KS = F8 ? 64 : 32;
+    const unsigned r0 = (unsigned)(min(n, last0) * D + KJ * j);
+    const unsigned r1 = (unsigned)(min(n, cap1) * D + KJ * j);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      kr[0][c] = ld16<NT>(K0 + r0 + 32 * c);
-      kr[1][c] = ld16<NT>(K1 + r1 + 32 * c);
+    for (int c = 0; c < KL; ++c) {
+      kr[0][c] = ld16<NT>(K0 + r0 + KS * c);
+      kr[1][c] = ld16<NT>(K1 + r1 + KS * c);
     }
     const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const unsigned v0 = (unsigned)(min(4 * j + e, last0) * D + vcol);
       const unsigned v1 = (unsigned)(min(4 * j + e, cap1) * D + vcol);
-      vr[e] = ld16<NT>(V0 + v0);
-      vr[4 + e] = ld16<NT>(V1 + v1);
+      if constexpr (F8) {
+        vr[e] = ld8<NT>(V0 + v0);
+        vr[4 + e] = ld8<NT>(V1 + v1);
+      } else {
+        vr[e] = ld16<NT>(V0 + v0);
+        vr[4 + e] = ld16<NT>(V1 + v1);
+      }
     }
   };
 
@@ -489,7 +527,8 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     }
   }
   const int t_first = lo + 32 * w;
-  u32x4 kp[U][2][KC], vp[U][8];
+  u32x4 kp[U][2][KL];
+  VT vp[U][8];
 #pragma unroll
   for (int u = 0; u < U; ++u)
     load_subtile(min(t_first + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u]);
@@ -499,10 +538,12 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   bf16x8 qf[KC];
   {
     const uint16_t* qp =
-        Q + ((size_t)b * G * Hkv + h0 + (n < nh ? n : 0)) * D + 8 * j;
+        Q + ((size_t)b * G * Hkv + h0 + (n < nh ? n : 0)) * D;
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 32 * c));
+    for (int c = 0; c < KC; ++c) {
+      const int d0 = F8 ? 16 * j + 64 * (c >> 1) + 8 * (c & 1) : 8 * j + 32 * c;
+      qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + d0));
+    }
   }
 
   // With SPEC nothing branches on the length before the compute: a split
@@ -513,6 +554,8 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     len = len < 0 ? 0 : (len > L ? L : len);
     hi = min(lo + P, len);
   }
+  // Logit scale (base 2), with the key scale of a quantized cache folded in.
+  const float sl2 = F8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
 
   f32x4 o[NV];
 #pragma unroll
@@ -525,10 +568,22 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   // split the block the scheduler overlaps, and the register allocator then
   // holds both subtiles' operands across them (lower occupancy): straight
   // line code instead.
-  constexpr bool kSkip = U == 1;
+  constexpr bool kSkip = U == (F8 ? 2 : 1) || U == 1;
 
-  auto compute_subtile = [&](int t0, const u32x4 (&kr)[2][KC],
-                             const u32x4 (&vr)[8]) {
+  // The k-vector of QK call c for token group tg (bf16 operands).
+  auto k_operand = [&](const u32x4 (&kr)[2][KL], int tg, int c) -> bf16x8 {
+    if constexpr (F8) {
+      const u32x4 x = kr[tg][c >> 1];
+      const uint2 p = e4m3x4_to_bf16x4(x[2 * (c & 1)]);
+      const uint2 q = e4m3x4_to_bf16x4(x[2 * (c & 1) + 1]);
+      return as_bf16x8(u32x4{p.x, p.y, q.x, q.y});
+    } else {
+      return as_bf16x8(kr[tg][c]);
+    }
+  };
+
+  auto compute_subtile = [&](int t0, const u32x4 (&kr)[2][KL],
+                             const VT (&vraw)[8]) {
     f32x4 sacc[2];
 #pragma unroll
     for (int tg = 0; tg < 2; ++tg) {
@@ -536,7 +591,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
 #pragma unroll
       for (int c = 0; c < KC; ++c)
         sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(kr[tg][c]), qf[c], sacc[tg], 0, 0, 0);
+            k_operand(kr, tg, c), qf[c], sacc[tg], 0, 0, 0);
     }
     float sv[8];
     float mx = -INFINITY;
@@ -545,7 +600,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
       for (int tg = 0; tg < 2; ++tg)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = sacc[tg][i] * a.scale_log2;
+          const float x = sacc[tg][i] * sl2;
           sv[4 * tg + i] = x;
           mx = fmaxf(mx, x);
         }
@@ -555,7 +610,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = t0 + 16 * tg + 4 * j + i;
-          const float x = tok < hi ? sacc[tg][i] * a.scale_log2 : -INFINITY;
+          const float x = tok < hi ? sacc[tg][i] * sl2 : -INFINITY;
           sv[4 * tg + i] = x;
           mx = fmaxf(mx, x);
         }
@@ -590,6 +645,17 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
 #pragma unroll
       for (int cc = 0; cc < NV; ++cc) o[cc] *= alpha;
     }
+    u32x4 vr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (F8) {
+        const uint2 p = e4m3x4_to_bf16x4(vraw[e][0]);
+        const uint2 q = e4m3x4_to_bf16x4(vraw[e][1]);
+        vr[e] = u32x4{p.x, p.y, q.x, q.y};
+      } else {
+        vr[e] = vraw[e];
+      }
+    }
 #pragma unroll
     for (int cc = 0; cc < NV; ++cc) {
       const bf16x8 vk = v_kvec<D>(vr, cc, n);
@@ -609,7 +675,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
-        if (t >= hi) vp[u][e] = u32x4{0u, 0u, 0u, 0u};
+        if (t >= hi) vp[u][e] = VT{};
       }
     }
     compute_subtile(t0, kp[u], vp[u]);
@@ -643,6 +709,8 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   __syncthreads();
 
   // Merge: thread -> (head g, 4 dims); waves that saw no token carry m = -inf.
+  // A quantized cache's value scale multiplies the normalised output.
+  const float vsc = F8 ? a.v_scale[kvh] : 1.f;
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
     const int g = idx / (D / 4);
     const int d = 4 * (idx - g * (D / 4));
@@ -660,7 +728,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     }
     const bool none = M == -INFINITY;       // no token in this split
     *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) =
-        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / lsum);
+        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (vsc / lsum);
     if (d == 0) {
       float* l = lse_dst(a, b, h0 + g, s);
       if (l) *l = none ? -INFINITY : (M + flog2(lsum)) * kLn2;
@@ -756,60 +824,74 @@ dim3 split_grid(int units, int B, int S) {
 // workgroup and subtiles each wave requests at once. Measured on MI355X
 // (64K, 256K and batch-64 histories, non-temporal K/V loads): short splits
 // want about two subtiles per wave (4 or 8 waves); long splits run best with
-// 4 waves each holding two subtiles in flight (2 waves per SIMD).
+// 4 waves each holding two subtiles in flight (2 waves per SIMD). An E4M3
+// subtile is half the bytes, so a wave holds twice as many.
 struct MfmaShape { int nw, u; };
-MfmaShape mfma_shape(int P) {
+MfmaShape mfma_shape(int P, bool f8) {
   const int nsub = (P + 31) / 32;
-  if (nsub > 16) return {4, 2};
-  if (nsub > 8) return {8, 1};
-  return {4, 1};
+  const int k = f8 ? 2 : 1;
+  if (nsub > 16) return {4, 2 * k};
+  if (nsub > 8) return {8, k};
+  return {4, k};
 }
 
 // The leading scalar arguments are what a wave needs before its first K/V
 // request; they fit the 14 kernel-argument dwords gfx950 preloads into SGPRs
 // at dispatch, so no wave waits on an argument load before its first
 // request (such loads queue behind other waves' K/V traffic).
-template <int D, int NW, int U, int GM, bool PAGED, bool SPEC>
+template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8>
 void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_mfma<D, NW, U, GM, PAGED, SPEC>), grid, dim3(NW * 64), 0,
-                     st, static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v),
+  hipLaunchKernelGGL((split_mfma<D, NW, U, GM, PAGED, SPEC, F8>), grid,
+                     dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
                      a.nhg, a.G, a.block_table, a.bs, a);
 }
 
-template <int D, bool PAGED, int GM, bool SPEC>
+template <int D, bool PAGED, int GM, bool SPEC, bool F8>
 void launch_mfma_spec(dim3 grid, MfmaShape m, const SplitArgs& a,
                       hipStream_t st) {
+  constexpr int k = F8 ? 2 : 1;
   if (m.nw == 8)
-    launch_one<D, 8, 1, GM, PAGED, SPEC>(grid, a, st);
-  else if (m.u == 2)
-    launch_one<D, 4, 2, GM, PAGED, SPEC>(grid, a, st);
+    launch_one<D, 8, k, GM, PAGED, SPEC, F8>(grid, a, st);
+  else if (m.u == 2 * k)
+    launch_one<D, 4, 2 * k, GM, PAGED, SPEC, F8>(grid, a, st);
   else
-    launch_one<D, 4, 1, GM, PAGED, SPEC>(grid, a, st);
+    launch_one<D, 4, k, GM, PAGED, SPEC, F8>(grid, a, st);
 }
 
 // Speculative first loads pay off for a single sequence (its splits are all
 // full when the caller's bound is its length); for a batch, whose lengths
 // may differ, they could read splits that turn out empty.
-template <int D, bool PAGED, int GM>
+template <int D, bool PAGED, int GM, bool F8>
 void launch_mfma_gm(dim3 grid, MfmaShape m, const SplitArgs& a, hipStream_t st) {
   if (a.B == 1)
-    launch_mfma_spec<D, PAGED, GM, true>(grid, m, a, st);
+    launch_mfma_spec<D, PAGED, GM, true, F8>(grid, m, a, st);
   else
-    launch_mfma_spec<D, PAGED, GM, false>(grid, m, a, st);
+    launch_mfma_spec<D, PAGED, GM, false, F8>(grid, m, a, st);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool F8>
 void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const int gm = s.G <= 8 ? 8 : 16;
   a.nhg = (s.G + gm - 1) / gm;
   const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
-  const MfmaShape m = mfma_shape(a.P);
+  const MfmaShape m = mfma_shape(a.P, F8);
   if (gm == 8)
-    launch_mfma_gm<D, PAGED, 8>(grid, m, a, st);
+    launch_mfma_gm<D, PAGED, 8, F8>(grid, m, a, st);
   else
-    launch_mfma_gm<D, PAGED, 16>(grid, m, a, st);
+    launch_mfma_gm<D, PAGED, 16, F8>(grid, m, a, st);
+}
+
+template <bool F8>
+void launch_mfma_dtype(const Shape& s, const SplitArgs& a, hipStream_t st) {
+  const bool paged = s.bs > 0;
+  if (s.D == 128) {
+    if (paged) launch_mfma<128, true, F8>(s, a, st);
+    else launch_mfma<128, false, F8>(s, a, st);
+  } else {
+    if (paged) launch_mfma<64, true, F8>(s, a, st);
+    else launch_mfma<64, false, F8>(s, a, st);
+  }
 }
 
 }  // namespace
@@ -817,14 +899,9 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
 int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.dtype == FD_DTYPE_BF16) {
-    const bool paged = s.bs > 0;
-    if (s.D == 128) {
-      if (paged) launch_mfma<128, true>(s, a, st);
-      else launch_mfma<128, false>(s, a, st);
-    } else {
-      if (paged) launch_mfma<64, true>(s, a, st);
-      else launch_mfma<64, false>(s, a, st);
-    }
+    launch_mfma_dtype<false>(s, a, st);
+  } else if (s.dtype == FD_DTYPE_FP8_E4M3) {
+    launch_mfma_dtype<true>(s, a, st);
   } else {
     const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
     const dim3 block(kGenThreads);

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(fb.LIB_PATH),
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fd_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -182,3 +182,48 @@ def test_partials_and_combine_reject_bad_args():
                                    None) == fb.FD_ERR_INVALID_ARG
     assert lib.fd_combine_partials(1, 16, 128, 4, FAKE + 4, FAKE, FAKE, None,
                                    None) == fb.FD_ERR_INVALID_ARG
+
+
+def call_fp8(**kw):
+    lib = fb.load()
+    args = dict(shape=shp(dtype="fp8_e4m3"), q=FAKE, k=FAKE, v=FAKE,
+                ks=FAKE, vs=FAKE, bt=None, lens=FAKE, S=4, ws=FAKE,
+                ws_bytes=1 << 30, out=FAKE, lse=None)
+    args.update(kw)
+    return lib.fd_decode_attn_fp8(ctypes.byref(args["shape"]), args["q"],
+                                  args["k"], args["v"], args["ks"], args["vs"],
+                                  args["bt"], args["lens"], args["S"],
+                                  args["ws"], args["ws_bytes"], args["out"],
+                                  args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), fb.FD_ERR_INVALID_ARG),
+    (dict(vs=None), fb.FD_ERR_INVALID_ARG),
+    (dict(ks=FAKE + 2), fb.FD_ERR_INVALID_ARG),
+    (dict(shape=shp()), fb.FD_ERR_INVALID_ARG),           # bf16 shape
+    (dict(shape=shp(dtype="f32")), fb.FD_ERR_INVALID_ARG),
+    (dict(k=FAKE + 8), fb.FD_ERR_INVALID_ARG),
+    (dict(ws_bytes=100), fb.FD_ERR_WORKSPACE),
+    (dict(shape=shp(dtype="fp8_e4m3", head_dim=96)), fb.FD_ERR_UNSUPPORTED),
+])
+def test_fp8_calls_are_rejected_on_the_host(kw, status):
+    assert call_fp8(**kw) == status
+
+
+def test_fp8_shape_needs_the_fp8_entry_points():
+    lib = fb.load()
+    s = shp(dtype="fp8_e4m3")
+    # the plain entry points have no scales: an E4M3 shape is refused there
+    assert call(shape=s) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_decode_partials(ctypes.byref(s), FAKE, FAKE, FAKE, None,
+                                  FAKE, 4, FAKE, FAKE, None) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_decode_partials_fp8(ctypes.byref(shp()), FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, None, FAKE, 4, FAKE, FAKE,
+                                      None) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_decode_partials_fp8(ctypes.byref(s), FAKE, FAKE, FAKE,
+                                      None, FAKE, None, FAKE, 4, FAKE, FAKE,
+                                      None) == fb.FD_ERR_INVALID_ARG
+    # planning and workspace sizing accept it
+    assert fb.fd_plan_splits(s, 256, -1) >= 1
+    assert fb.fd_workspace_size(s, 8) == fb.fd_workspace_size(shp(), 8)

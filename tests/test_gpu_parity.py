@@ -24,7 +24,9 @@ pytestmark = [
     pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
 ]
 
-TOL = {"f32": 1e-5, "bf16": 2e-3}
+# fp8_e4m3: bf16 query against an E4M3 cache, fp32 accumulation -- the
+# dequantized values are exact bf16 values, so the bf16 bar applies.
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3": 2e-3}
 LSE_TOL = 1e-4
 LOG = os.environ.get("FD_PARITY_LOG")
 
@@ -41,7 +43,9 @@ def device_inputs(w):
     d = torch.device("cuda")
     return dict(q=w.q.to(d), k=w.k.to(d), v=w.v.to(d),
                 seq_lens=w.seq_lens.to(d),
-                bt=None if w.block_table is None else w.block_table.to(d))
+                bt=None if w.block_table is None else w.block_table.to(d),
+                ks=None if w.k_scale is None else w.k_scale.to(d),
+                vs=None if w.v_scale is None else w.v_scale.to(d))
 
 
 def gpu_attention(w, S, t=None):
@@ -52,9 +56,14 @@ def gpu_attention(w, S, t=None):
     lse = torch.full((w.batch, w.num_q_heads), float("nan"), device="cuda")
     nbytes = fb.fd_workspace_size(shape, S)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
-    print(f"[gpu] {w.name} S={S}", flush=True)
-    fb.fd_decode_attn(shape, t["q"], t["k"], t["v"], t["bt"], t["seq_lens"],
-                      S, ws, out, lse)
+    print(f"[gpu] {w.name} {w.cache_dtype} S={S}", flush=True)
+    if w.cache_dtype == "fp8_e4m3":
+        fb.fd_decode_attn_fp8(shape, t["q"], t["k"], t["v"], t["ks"],
+                              t["vs"], t["bt"], t["seq_lens"], S, ws, out,
+                              lse)
+    else:
+        fb.fd_decode_attn(shape, t["q"], t["k"], t["v"], t["bt"],
+                          t["seq_lens"], S, ws, out, lse)
     torch.cuda.synchronize()
     return out.cpu().double().numpy(), lse.cpu().double().numpy()
 
@@ -64,7 +73,9 @@ def oracle_attention(w):
     return oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
                                    dtype=a["dtype"], scale=a["scale"],
                                    block_table=a["block_table"],
-                                   block_size=a["block_size"])
+                                   block_size=a["block_size"],
+                                   kv_dtype=a["kv_dtype"],
+                                   k_scale=a["k_scale"], v_scale=a["v_scale"])
 
 
 def assert_parity(name, dtype, out, lse, ref_out, ref_lse):
@@ -87,7 +98,8 @@ def assert_parity(name, dtype, out, lse, ref_out, ref_lse):
 def check(w, S):
     out, lse = gpu_attention(w, S)
     ref_out, ref_lse = oracle_attention(w)
-    assert_parity(f"{w.name}/S={S}", w.dtype, out, lse, ref_out, ref_lse)
+    assert_parity(f"{w.name}/{w.cache_dtype}/S={S}", w.cache_dtype, out, lse,
+                  ref_out, ref_lse)
     return out, lse
 
 
@@ -112,7 +124,8 @@ def test_workload_at_forced_splits(name, splits):
     t = device_inputs(w)
     for S in splits:
         out, lse = gpu_attention(w, S, t)
-        assert_parity(f"{name}/S={S}", w.dtype, out, lse, ref_out, ref_lse)
+        assert_parity(f"{name}/S={S}", w.cache_dtype, out, lse, ref_out,
+                      ref_lse)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -292,3 +305,79 @@ def test_convenience_wrapper_plans_and_allocates():
     ref_out, ref_lse = oracle_attention(w)
     assert_parity("wrapper", "bf16", out.cpu().double().numpy(),
                   lse.cpu().double().numpy(), ref_out, ref_lse)
+
+
+# ------------------------------------------------- 8-bit E4M3 cache (fp8)
+
+def test_fp8_64k_at_planned_and_forced_splits():
+    w = workloads.make("long_gqa_64k_fp8")
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    planned = fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len())
+    for S in sorted({planned, 1, 8, 64, 512}):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"fp8-64k/S={S}", "fp8_e4m3", out, lse, ref_out,
+                      ref_lse)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_ragged_tails_with_poisoned_cache(paged, d):
+    lens = [1, 15, 16, 17, 31, 33, 100, 511, 0, 257, 1000]
+    w = workloads.make("ragged8", seed=41, batch=len(lens), num_q_heads=16,
+                       num_kv_heads=2, head_dim=d, max_seq_len=1000,
+                       paged=paged, seq_lens=lens, poison_tail=True,
+                       kv_dtype="fp8_e4m3")
+    for S in (1, 3, 8, 32):
+        check(w, S)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (12, 3, 128),
+                                      (64, 2, 128), (40, 2, 64), (4, 4, 64)])
+def test_fp8_head_layouts(hq, hkv, d):
+    w = workloads.make("heads8", seed=42, batch=2, num_q_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, max_seq_len=2100,
+                       seq_lens=[2100, 777], kv_dtype="fp8_e4m3")
+    for S in (1, 5):
+        check(w, S)
+
+
+def test_fp8_long_ragged_paged_batch():
+    w = workloads.make("ragged_paged", seed=43, batch=6, max_seq_len=20000,
+                       kv_dtype="fp8_e4m3")
+    check(w, fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len()))
+    check(w, 1)
+
+
+def test_fp8_partials_entry_point():
+    w = workloads.make("ragged_paged", seed=44, batch=3, num_q_heads=16,
+                       num_kv_heads=4, head_dim=128, max_seq_len=900,
+                       min_seq_len=1, poison_tail=True, kv_dtype="fp8_e4m3")
+    S = 7
+    t = device_inputs(w)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    op = torch.empty(B, Hq, S, D, device="cuda")
+    lp = torch.empty(B, Hq, S, device="cuda")
+    fb.fd_decode_partials_fp8(shape_of(w), t["q"], t["k"], t["v"], t["ks"],
+                              t["vs"], t["bt"], t["seq_lens"], S, op, lp)
+    torch.cuda.synchronize()
+    a = w.numpy_view()
+    ref_op, ref_lp = oracle.split_partials(
+        a["q"], a["k"], a["v"], a["seq_lens"], S, dtype="bf16",
+        max_seq_len=900, block_table=a["block_table"],
+        block_size=a["block_size"], kv_dtype="fp8_e4m3",
+        k_scale=a["k_scale"], v_scale=a["v_scale"])
+    assert_parity("fp8-partials", "fp8_e4m3",
+                  op.cpu().double().numpy().reshape(B, Hq * S, D),
+                  lp.cpu().double().numpy().reshape(B, Hq * S),
+                  ref_op.reshape(B, Hq * S, D), ref_lp.reshape(B, Hq * S))
+
+
+def test_fp8_paged_matches_contiguous_bitwise():
+    w = workloads.make("ragged_paged", seed=45, batch=5, max_seq_len=3000,
+                       min_seq_len=1, kv_dtype="fp8_e4m3")
+    c = workloads.to_contiguous(w)
+    for S in (1, 6):
+        o1, l1 = gpu_attention(w, S)
+        o2, l2 = gpu_attention(c, S)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

@@ -25,6 +25,8 @@ import torch
 
 F32 = "f32"
 BF16 = "bf16"
+FP8 = "fp8_e4m3"
+FP8_MAX = 448.0   # largest finite E4M3 magnitude
 
 # name -> recipe. seed = workload id.
 SPECS = {
@@ -42,6 +44,12 @@ SPECS = {
         wid=4, batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
         max_seq_len=32768, min_seq_len=512, dtype=BF16, scale=None,
         paged=True, block_size=16),
+    # The 64K history in an 8-bit E4M3 cache: the same draws as long_gqa_64k,
+    # each kv head's K and V divided by amax/448 and rounded to E4M3.
+    "long_gqa_64k_fp8": dict(
+        wid=2, batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
+        max_seq_len=65536, dtype=BF16, kv_dtype=FP8, scale=None,
+        paged=False),
     "short_batch": dict(
         wid=5, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
         max_seq_len=1024, dtype=BF16, scale=None, paged=False),
@@ -55,6 +63,8 @@ SPECS = {
 
 ORDER = ["tiny_mha", "long_gqa_64k", "ultra_long_256k", "ragged_paged",
          "short_batch"]
+# Further measured workloads (variants of the above).
+EXTRA = ["long_gqa_64k_fp8"]
 
 
 @dataclasses.dataclass
@@ -82,6 +92,13 @@ class Workload:
     seq_lens: torch.Tensor
     block_table: Optional[torch.Tensor]
     hot_positions: Optional[torch.Tensor] = None   # [B, Hkv, n_hot]
+    kv_dtype: Optional[str] = None                 # None: same as dtype
+    k_scale: Optional[torch.Tensor] = None         # fp32 [Hkv] (E4M3 cache)
+    v_scale: Optional[torch.Tensor] = None
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def paged(self) -> bool:
@@ -104,14 +121,17 @@ class Workload:
 
     def kv_bytes(self) -> int:
         """K+V bytes the call must read: every attended row, once."""
-        esz = 4 if self.dtype == F32 else 2
+        esz = {F32: 4, BF16: 2, FP8: 1}[self.cache_dtype]
         return self.sum_seq_len() * self.num_kv_heads * 2 * self.head_dim * esz
 
     def numpy_view(self) -> dict:
-        """Raw arrays for the oracle: bf16 as uint16 bit patterns, f32 as is."""
+        """Raw arrays for the oracle: bf16 as uint16 bit patterns, E4M3 as
+        uint8 codes, f32 as is."""
         def raw(t):
             if t.dtype == torch.bfloat16:
                 return t.view(torch.int16).numpy().view(np.uint16)
+            if t.dtype == torch.float8_e4m3fn:
+                return t.view(torch.uint8).numpy()
             return t.numpy()
         return dict(
             q=raw(self.q), k=raw(self.k), v=raw(self.v),
@@ -119,14 +139,18 @@ class Workload:
             block_table=(None if self.block_table is None
                          else self.block_table.numpy().astype(np.int64)),
             block_size=self.block_size, dtype=self.dtype,
-            scale=self.effective_scale)
+            scale=self.effective_scale, kv_dtype=self.cache_dtype,
+            k_scale=(None if self.k_scale is None
+                     else self.k_scale.numpy().astype(np.float64)),
+            v_scale=(None if self.v_scale is None
+                     else self.v_scale.numpy().astype(np.float64)))
 
     def shape_dict(self) -> dict:
         return dict(batch=self.batch, num_q_heads=self.num_q_heads,
                     num_kv_heads=self.num_kv_heads, head_dim=self.head_dim,
                     max_seq_len=self.max_seq_len, block_size=self.block_size,
                     max_blocks_per_seq=self.max_blocks_per_seq,
-                    num_blocks=self.num_blocks, dtype=self.dtype,
+                    num_blocks=self.num_blocks, dtype=self.cache_dtype,
                     scale=self.scale or 0.0)
 
 
@@ -144,7 +168,8 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
          hot_key_fraction: float = None, hot_key_gain: float = None,
          poison_tail: bool = False,
          needles: Optional[Sequence[int]] = None,
-         needle_logit: float = 40.0) -> Workload:
+         needle_logit: float = 40.0,
+         kv_dtype: Optional[str] = None) -> Workload:
     """Build a workload from a named recipe, with optional overrides.
 
     Draw order on one CPU generator: seq_lens (ragged recipes only), q, k, v,
@@ -157,6 +182,9 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
     needles: token positions p; for every (b, kv head) the key at p is set to
       c * q[b, first head of the group] with c chosen so that head's logit is
       ``needle_logit``, far above the N(0, 1)-scale logits of the other keys.
+    kv_dtype: "fp8_e4m3" stores K and V as 8-bit E4M3 codes: per kv head,
+      scale = amax / 448 over that head's whole pool (fp32), codes =
+      E4M3(x / scale) rounded by torch; q stays bf16.
     """
     spec = dict(SPECS.get(name, {}))
     wid = spec.get("wid", 0)
@@ -167,6 +195,8 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
     D = head_dim or spec.get("head_dim", 128)
     L = max_seq_len if max_seq_len is not None else spec.get("max_seq_len", 512)
     dt = dtype or spec.get("dtype", BF16)
+    kvd = kv_dtype or spec.get("kv_dtype")
+    assert kvd in (None, FP8) and (kvd is None or dt == BF16)
     sc = spec.get("scale") if scale == "spec" else scale
     pg = spec.get("paged", False) if paged is None else paged
     bs = (spec.get("block_size", block_size) if pg else 0)
@@ -237,11 +267,24 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
                         k32[blk, h, p % bs] = c * qv
                     else:
                         k32[b, h, p] = c * qv
-    k = _cast(k32, dt)
-    v = _cast(v32, dt)
+    ks = vs = None
+    if kvd == FP8:
+        def quant(x):
+            amax = x.abs().amax(dim=(0, 2, 3))
+            sc = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+            sc = sc.to(torch.float32)
+            return (x / sc[None, :, None, None]).to(torch.float8_e4m3fn), sc
+        k, ks = quant(k32)
+        v, vs = quant(v32)
+    else:
+        k = _cast(k32, dt)
+        v = _cast(v32, dt)
 
     if poison_tail:
         nan = float("nan")
+        if kvd == FP8:     # poison through the byte view (0x7F is NaN)
+            k = k.view(torch.uint8).to(torch.float32)
+            v = v.view(torch.uint8).to(torch.float32)
         if pg:
             used = torch.zeros(k.shape[0], dtype=torch.bool)
             for b in range(B):
@@ -260,12 +303,17 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
                 n = int(lens[b])
                 k[b, :, n:] = nan
                 v[b, :, n:] = nan
+        if kvd == FP8:
+            k = torch.where(torch.isnan(k), 0x7F, k).to(torch.uint8).view(
+                torch.float8_e4m3fn)
+            v = torch.where(torch.isnan(v), 0x7F, v).to(torch.uint8).view(
+                torch.float8_e4m3fn)
 
     return Workload(name=name, batch=B, num_q_heads=Hq, num_kv_heads=Hkv,
                     head_dim=D, max_seq_len=L, dtype=dt, scale=sc,
                     block_size=bs, q=q.contiguous(), k=k.contiguous(),
                     v=v.contiguous(), seq_lens=lens, block_table=bt,
-                    hot_positions=hot)
+                    hot_positions=hot, kv_dtype=kvd, k_scale=ks, v_scale=vs)
 
 
 def to_contiguous(w: Workload) -> Workload:
