@@ -405,7 +405,7 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(unsigned w) {
 template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8,
           bool NT = true>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(U >= (F8 ? 4 : 2) ? 2 : 3))) void split_mfma(
+__attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
     const int32_t* __restrict__ bt, int bs, SplitArgs a) {
@@ -568,7 +568,7 @@ __attribute__((amdgpu_waves_per_eu(U >= (F8 ? 4 : 2) ? 2 : 3))) void split_mfma(
   // split the block the scheduler overlaps, and the register allocator then
   // holds both subtiles' operands across them (lower occupancy): straight
   // line code instead.
-  constexpr bool kSkip = U == (F8 ? 2 : 1) || U == 1;
+  constexpr bool kSkip = U == 1;
 
   // The k-vector of QK call c for token group tg (bf16 operands).
   auto k_operand = [&](const u32x4 (&kr)[2][KL], int tg, int c) -> bf16x8 {
@@ -824,15 +824,17 @@ dim3 split_grid(int units, int B, int S) {
 // workgroup and subtiles each wave requests at once. Measured on MI355X
 // (64K, 256K and batch-64 histories, non-temporal K/V loads): short splits
 // want about two subtiles per wave (4 or 8 waves); long splits run best with
-// 4 waves each holding two subtiles in flight (2 waves per SIMD). An E4M3
-// subtile is half the bytes, so a wave holds twice as many.
+// 4 waves each holding two subtiles in flight (2 waves per SIMD). E4M3
+// caches (64K and 256K histories, S = 64..256): one subtile in flight per
+// wave wins at every split length (the in-register conversion lengthens
+// the compute tail more than extra requests help), 8 waves from 9 subtiles.
 struct MfmaShape { int nw, u; };
 MfmaShape mfma_shape(int P, bool f8) {
   const int nsub = (P + 31) / 32;
-  const int k = f8 ? 2 : 1;
-  if (nsub > 16) return {4, 2 * k};
-  if (nsub > 8) return {8, k};
-  return {4, k};
+  if (f8) return nsub > 8 ? MfmaShape{8, 1} : MfmaShape{4, 1};
+  if (nsub > 16) return {4, 2};
+  if (nsub > 8) return {8, 1};
+  return {4, 1};
 }
 
 // The leading scalar arguments are what a wave needs before its first K/V
@@ -850,13 +852,12 @@ void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
 template <int D, bool PAGED, int GM, bool SPEC, bool F8>
 void launch_mfma_spec(dim3 grid, MfmaShape m, const SplitArgs& a,
                       hipStream_t st) {
-  constexpr int k = F8 ? 2 : 1;
   if (m.nw == 8)
-    launch_one<D, 8, k, GM, PAGED, SPEC, F8>(grid, a, st);
-  else if (m.u == 2 * k)
-    launch_one<D, 4, 2 * k, GM, PAGED, SPEC, F8>(grid, a, st);
+    launch_one<D, 8, 1, GM, PAGED, SPEC, F8>(grid, a, st);
+  else if (!F8 && m.u == 2)
+    launch_one<D, 4, F8 ? 1 : 2, GM, PAGED, SPEC, F8>(grid, a, st);
   else
-    launch_one<D, 4, k, GM, PAGED, SPEC, F8>(grid, a, st);
+    launch_one<D, 4, 1, GM, PAGED, SPEC, F8>(grid, a, st);
 }
 
 // Speculative first loads pay off for a single sequence (its splits are all
