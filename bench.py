@@ -60,6 +60,10 @@ def parse_args():
     p.add_argument("--all", action="store_true",
                    help="also time every workload (extra JSON lines, "
                         "stderr)")
+    p.add_argument("--frontier", action="store_true",
+                   help="instead of the metric: sweep batch x history x "
+                        "splits (uniform lengths, 16q/2kv d128 bf16) and "
+                        "print one JSON line per point")
     return p.parse_args()
 
 
@@ -167,32 +171,35 @@ class Bench:
                                     self.lse)
 
     def time_graph(self, fn, steps, warmup):
-        """Eager warmup, capture `steps` calls in a graph, replay once
-        untimed, then time one replay. Returns (ms total, wall ms)."""
-        torch = self.torch
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(steps):
-                    fn(i)
-        torch.cuda.current_stream().wait_stream(s)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3
-        return e0.elapsed_time(e1), wall
+        return time_graph(self.torch, fn, steps, warmup)
+
+
+def time_graph(torch, fn, steps, warmup):
+    """Eager warmup, capture `steps` calls in a graph, replay once untimed,
+    then time one replay. Returns (ms total, wall ms)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return e0.elapsed_time(e1), wall
 
 
 def copy_probe(torch):
@@ -319,6 +326,65 @@ def run_one(args, name, steps, warmup, with_cpu):
     return rec
 
 
+FRONTIER_B = (1, 4, 16, 64, 256)
+FRONTIER_L = (512, 2048, 8192, 32768, 131072, 262144)
+FRONTIER_S = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+FRONTIER_MAX_TOKENS = 1 << 24          # B * L cap: 17 GB of bf16 K/V
+
+
+def frontier(args):
+    """Where splitting pays: every (batch, history) point of the grid at
+    every split count, plus the planner's choice. Inputs are drawn on the
+    device from a seeded generator (timing only; parity is the tests')."""
+    import torch
+    from split_kv_long_amd import binding as fb
+    Hq, Hkv, D = 16, 2, 128
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    gen = torch.Generator(device=dev)
+    for B in FRONTIER_B:
+        for L in FRONTIER_L:
+            if B * L > FRONTIER_MAX_TOKENS:
+                continue
+            gen.manual_seed(1000 * B + L // 512)
+            kv = B * Hkv * L * D * 2
+            R = max(1, min(args.steps, math.ceil(2 * MALL_BYTES / kv)))
+            q = torch.randn(B, Hq, D, generator=gen, device=dev).to(
+                torch.bfloat16)
+            ks = [torch.randn(B, Hkv, L, D, generator=gen, device=dev).to(
+                torch.bfloat16) for _ in range(R)]
+            vs = [torch.randn(B, Hkv, L, D, generator=gen, device=dev).to(
+                torch.bfloat16) for _ in range(R)]
+            lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+            out = torch.empty(B, Hq, D, device=dev)
+            shape = fb.make_shape(B, Hq, Hkv, D, L, "bf16")
+            planned = fb.fd_plan_splits(shape, cus, B * L)
+            res = {}
+            for S in sorted(set(FRONTIER_S) | {planned}):
+                if S > 1 and -(-L // S) < 16:
+                    continue
+                nb = fb.fd_workspace_size(shape, S)
+                ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+                def step(i, S=S, ws=ws):
+                    r = i % R
+                    fb.fd_decode_attn(shape, q, ks[r], vs[r], None, lens, S,
+                                      ws, out)
+                ms, _ = time_graph(torch, step, args.steps, 3)
+                res[S] = ms * 1e3 / args.steps
+            best = min(res, key=res.get)
+            rec = dict(batch=B, max_seq_len=L, num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, dtype="bf16",
+                       kv_bytes=kv, us_per_call={str(k): round(v, 3)
+                                                 for k, v in res.items()},
+                       best_splits=best, planned_splits=planned,
+                       planned_over_best=round(res[planned] / res[best], 4),
+                       split_gain=round(res[1] / res[best], 4))
+            print(json.dumps(rec), flush=True)
+            del q, ks, vs, out
+            torch.cuda.empty_cache()
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -332,6 +398,9 @@ def main():
         sys.exit(1)
     from split_kv_long_amd import binding
     binding.load()     # fails loudly if the HIP library is missing
+    if args.frontier:
+        frontier(args)
+        return
     rec = run_one(args, args.workload, args.steps, args.warmup,
                   not args.no_cpu_baseline)
     if args.all:

@@ -63,8 +63,13 @@ def test_planner_regimes():
     assert plan(num_q_heads=64, num_kv_heads=8, max_seq_len=262144) == 64
     # a batch that already fills the GPU: no split
     assert plan(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=1024) == 1
-    # a short history: no split
-    assert plan(max_seq_len=400) == 1
+    # a short history: no split below two minimum-length (128-token) splits
+    assert plan(max_seq_len=200) == 1
+    # ... but a batch-one 512-token history already gains from 4 splits
+    assert plan(max_seq_len=512) == 4
+    # splits longer than 1024 tokens are halved (two workgroups per CU)
+    assert plan(max_seq_len=262144) == 256
+    assert plan(max_seq_len=131072) == 128
     # tiny fp32 MHA history of 512 tokens: the fp32 path is latency-bound,
     # so it takes the shorter fp32 minimum split (64 tokens) -> 8 splits
     assert plan(num_q_heads=8, num_kv_heads=8, head_dim=64, max_seq_len=512,
@@ -81,7 +86,7 @@ def test_planner_properties():
             P = -(-(-(-L // S)) // 16) * 16
             assert S * P >= L
             if S > 1:
-                assert P >= 256 and B * 2 * S >= 1
+                assert P >= 128 and B * 2 * S >= 1
             assert S == plan(batch=B, max_seq_len=L)   # deterministic
     # splits never grow as the batch grows at fixed L
     prev = 10 ** 9
