@@ -25,6 +25,11 @@ What it computes, and where each step comes from:
 definition; ``decode_attention`` with ``kv_dtype="fp8_e4m3"`` and per-kv-head
 scales is the definition over the dequantized cache.
 
+``oracle.sparse`` holds the block-sparse variant (a low-bit key summary,
+a top-delta block filter per split, exact attention over the kept blocks),
+after the abstract of the "Faster Than Flash" page; its module docstring
+lists the readings taken where that page is silent.
+
 Every function is float64 NumPy, one (sequence, kv head) at a time.
 """
 
@@ -38,4 +43,11 @@ from .attention import (  # noqa: F401
     split_length,
     split_partials,
     combine_partials,
+)
+from .sparse import (  # noqa: F401
+    quantize_block,
+    key_summary,
+    pack_int4,
+    unpack_int4,
+    sparse_decode_attention,
 )

@@ -1,0 +1,169 @@
+"""Float64 reference for block-sparse decode over a low-bit key summary
+(test infrastructure only; "parity" for the selection step is pinned by
+invariants and brute force, not by values the pages print).
+
+The "Faster Than Flash" page (abstract) describes decoding that first scans
+a low-bit quantized copy of the keys to judge which blocks of the history
+matter, keeps the blocks a "top-delta" rule admits (without global
+synchronization), and computes exact attention over the kept blocks only.
+The page defines neither the quantizer nor the rule; the readings taken here
+(each implemented independently in the library) are:
+
+* key summary: the history is cut into 16-token blocks (one page of a paged
+  cache). For each block and kv head, amax = the largest |k| over the
+  block's attended rows and all dims (exact in float32: the keys are bf16);
+  inv = float32(7 / amax) and scale = float32(amax / 7) (both rounded once to
+  float32; amax = 0 gives inv = scale = 0); every attended element gets the
+  4-bit code rint(float32(k * inv)) (round half to even), which lies in
+  [-7, 7]. Rows past the length get code 0.
+* estimate: for block j and query head h, est[j, h] = attention scale *
+  scale_j * max over the block's attended tokens i of sum_d q[h, d] *
+  code[i, d] -- the block's largest logit as the summary sees it.
+* top-delta, per split (no cross-split synchronization): with M[h] the
+  largest est over the split's blocks, block j is kept when
+  est[j, h] >= M[h] - delta for at least one query head h of its kv head.
+* result: exact softmax attention (as ``decode_attention``) over the tokens
+  of every kept block; delta = +inf keeps every block and gives the dense
+  result.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+from .attention import decode_values, history_rows, softmax_attention, \
+    split_length
+
+BLOCK = 16
+
+
+def quantize_block(rows_bf16_bits) -> Tuple[np.ndarray, np.float32]:
+    """One block's attended key rows (bf16 bit patterns, [n, D]) ->
+    (int codes [n, D], float32 scale), per the reading above."""
+    x = decode_values(rows_bf16_bits, "bf16").astype(np.float32)
+    amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x.shape, dtype=np.int64), np.float32(0)
+    inv = np.float32(np.float32(7) / amax)
+    scale = np.float32(amax / np.float32(7))
+    codes = np.rint((x * inv).astype(np.float32)).astype(np.int64)
+    return codes, scale
+
+
+def key_summary(k, seq_lens, block_table=None, block_size: int = 0):
+    """Codes (int, same layout as k) and scales for every attended block.
+
+    Contiguous k [B, Hkv, L, D]: scales [B, Hkv, ceil(L/16)].
+    Paged pool [NB, Hkv, bs, D]: scales [NB, Hkv, bs/16] (sub-block s of a
+    page covers its slots 16s..16s+15). Unattended rows/blocks stay 0.
+    """
+    paged = block_table is not None and block_size
+    codes = np.zeros(k.shape, dtype=np.int64)
+    if paged:
+        scales = np.zeros((k.shape[0], k.shape[1], block_size // BLOCK),
+                          dtype=np.float32)
+    else:
+        scales = np.zeros((k.shape[0], k.shape[1], -(-k.shape[2] // BLOCK)),
+                          dtype=np.float32)
+    B = len(seq_lens)
+    for b in range(B):
+        n = int(seq_lens[b])
+        for kvh in range(k.shape[1]):
+            for j in range(-(-n // BLOCK)):
+                lo, hi = j * BLOCK, min((j + 1) * BLOCK, n)
+                rows = history_rows(k, b, kvh, lo, hi, block_table,
+                                    block_size)
+                c, s = quantize_block(rows)
+                if paged:
+                    pos = np.arange(lo, hi)
+                    blk = np.asarray(block_table)[b, pos // block_size]
+                    codes[blk, kvh, pos % block_size] = c
+                    scales[blk[0], kvh, (lo % block_size) // BLOCK] = s
+                else:
+                    codes[b, kvh, lo:hi] = c
+                    scales[b, kvh, j] = s
+    return codes, scales
+
+
+def pack_int4(codes) -> np.ndarray:
+    """Int codes in [-8, 7], last axis D -> uint8 [..., D/2]: dim 2m in the
+    low nibble of byte m, dim 2m+1 in the high nibble (two's complement)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.int64)
+    lo, hi = p & 0xF, (p >> 4) & 0xF
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int64)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    return np.where(out >= 8, out - 16, out)
+
+
+def block_scale(scales, b, kvh, j, block_table=None, block_size: int = 0):
+    if block_table is None or not block_size:
+        return float(scales[b, kvh, j])
+    pos = j * BLOCK
+    blk = int(np.asarray(block_table)[b, pos // block_size])
+    return float(scales[blk, kvh, (pos % block_size) // BLOCK])
+
+
+def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
+                            num_splits: int, max_seq_len: int,
+                            scale: Optional[float] = None, block_table=None,
+                            block_size: int = 0):
+    """Block-sparse decode (readings in the module docstring).
+
+    q [B, Hq, D] bf16 bits; k, v bf16 bits (contiguous or paged);
+    codes int (layout of k), scales as ``key_summary`` returns.
+    Returns out [B, Hq, D], lse [B, Hq], est [B, Hq, nblk] (NaN where no
+    block), kept [B, Hkv, nblk] (bool), with nblk = ceil(L / 16).
+    """
+    qf = decode_values(q, "bf16")
+    B, Hq, D = qf.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = scale if scale else 1.0 / math.sqrt(D)
+    P = split_length(max_seq_len, num_splits)
+    nblk = -(-max(max_seq_len, 1) // BLOCK)
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    est = np.full((B, Hq, nblk), np.nan)
+    kept = np.zeros((B, Hkv, nblk), dtype=bool)
+    for b in range(B):
+        n = int(seq_lens[b])
+        for kvh in range(Hkv):
+            heads = slice(kvh * G, (kvh + 1) * G)
+            # 1. estimates from the summary
+            for j in range(-(-n // BLOCK)):
+                lo, hi = j * BLOCK, min((j + 1) * BLOCK, n)
+                c = history_rows(codes, b, kvh, lo, hi, block_table,
+                                 block_size).astype(np.float64)
+                s = block_scale(scales, b, kvh, j, block_table, block_size)
+                est[b, heads, j] = sc * s * (qf[b, heads] @ c.T).max(axis=1)
+            # 2./3. top-delta inside each split
+            for s_ in range(num_splits):
+                j0, j1 = s_ * P // BLOCK, min((s_ + 1) * P, n)
+                j1 = -(-j1 // BLOCK)
+                if j1 <= j0:
+                    continue
+                e = est[b, heads, j0:j1]
+                M = e.max(axis=1, keepdims=True)
+                kept[b, kvh, j0:j1] = (e >= M - delta).any(axis=0)
+            # 4. exact attention over the kept tokens
+            toks = [t for t in range(n) if kept[b, kvh, t // BLOCK]]
+            if not toks:
+                continue
+            kr = np.concatenate([decode_values(history_rows(
+                k, b, kvh, t, t + 1, block_table, block_size), "bf16")
+                for t in toks])
+            vr = np.concatenate([decode_values(history_rows(
+                v, b, kvh, t, t + 1, block_table, block_size), "bf16")
+                for t in toks])
+            o, l = softmax_attention(sc * (qf[b, heads] @ kr.T), vr)
+            out[b, heads] = o
+            lse[b, heads] = l
+    return out, lse, est, kept

@@ -1,0 +1,270 @@
+"""Pins for the block-sparse oracle (low-bit key summary, top-delta block
+filter per split, exact attention over the kept blocks).
+
+The "Faster Than Flash" page prints no worked example, so each pin checks
+the oracle against something it does not compute itself: the nearest-integer
+property of the quantizer, hand-packed nibbles, the dense oracle (delta =
+inf, one block per split), torch's float64 SDPA with a mask built from the
+kept blocks, brute-force estimates by explicit loops, and invariants of the
+keep rule. The last test plants plausible mistakes in copies of the keep
+step and shows each is caught.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import sparse as osp
+import workloads
+
+
+def _bf16(x):
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------- quantizer
+
+def test_quantizer_nearest_integer_and_range():
+    rng = np.random.default_rng(0)
+    for trial in range(50):
+        n = int(rng.integers(1, 17))
+        x = rng.standard_normal((n, 64)) * 10 ** rng.uniform(-3, 3)
+        bits = _bf16(x)
+        xv = oracle.decode_values(bits, "bf16")
+        codes, scale = osp.quantize_block(bits)
+        amax = np.abs(xv).max()
+        assert codes.min() >= -7 and codes.max() <= 7
+        # nearest integer to 7 x / amax (float64; ties may go either way)
+        assert np.all(np.abs(7.0 * xv / amax - codes) <= 0.5 + 1e-6)
+        i = np.unravel_index(np.abs(xv).argmax(), xv.shape)
+        assert abs(codes[i]) == 7
+        assert abs(float(scale) * 7 - amax) <= 1e-6 * amax
+
+
+def test_quantizer_zero_block():
+    codes, scale = osp.quantize_block(_bf16(np.zeros((16, 8))))
+    assert not codes.any() and scale == 0
+
+
+def test_int4_packing_by_hand():
+    assert osp.pack_int4(np.array([1, -1])).tolist() == [0xF1]
+    assert osp.pack_int4(np.array([-8, 7])).tolist() == [0x78]
+    assert osp.pack_int4(np.array([0, 3, -2, 5])).tolist() == [0x30, 0x5E]
+    allc = np.arange(-8, 8)
+    pairs = np.stack(np.meshgrid(allc, allc), -1).reshape(-1, 2)
+    assert np.array_equal(osp.unpack_int4(osp.pack_int4(pairs)), pairs)
+
+
+def test_key_summary_paged_equals_contiguous():
+    w = workloads.make("ragged_paged", seed=51, batch=3, num_q_heads=4,
+                       num_kv_heads=2, head_dim=32, max_seq_len=100,
+                       min_seq_len=1)
+    c = workloads.to_contiguous(w)
+    a, b = w.numpy_view(), c.numpy_view()
+    cp, sp = osp.key_summary(a["k"], a["seq_lens"], a["block_table"], 16)
+    cc, sc = osp.key_summary(b["k"], b["seq_lens"])
+    for bb in range(3):
+        n = int(a["seq_lens"][bb])
+        for h in range(2):
+            rows = oracle.history_rows(cp, bb, h, 0, n, a["block_table"], 16)
+            assert np.array_equal(rows, cc[bb, h, :n])
+            for j in range(-(-n // 16)):
+                blk = a["block_table"][bb, j]
+                assert sp[blk, h, 0] == sc[bb, h, j]
+
+
+# ---------------------------------------------------------- checks proper
+
+def _case(seed, B=2, Hq=4, Hkv=2, D=32, L=200, lens=(200, 77), needles=None):
+    w = workloads.make("sp", seed=seed, batch=B, num_q_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=D, max_seq_len=L,
+                       seq_lens=list(lens), needles=needles,
+                       needle_logit=12.0)
+    a = w.numpy_view()
+    codes, scales = osp.key_summary(a["k"], a["seq_lens"])
+    return a, codes, scales
+
+
+def check_dense_limit(fn):
+    """delta = inf keeps everything: the dense oracle's result."""
+    a, codes, scales = _case(60)
+    for S in (1, 3):
+        out, lse, _, kept = fn(a["q"], a["k"], a["v"], a["seq_lens"], codes,
+                               scales, delta=math.inf, num_splits=S,
+                               max_seq_len=200)
+        ref = oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                      dtype="bf16")
+        assert np.allclose(out, ref[0], atol=1e-13)
+        assert np.allclose(lse, ref[1], atol=1e-13)
+
+
+def check_one_block_per_split_is_dense(fn):
+    """With one 16-token block per split every split keeps its only block."""
+    a, codes, scales = _case(61, L=96, lens=(96, 50))
+    out, lse, _, kept = fn(a["q"], a["k"], a["v"], a["seq_lens"], codes,
+                           scales, delta=0.0, num_splits=6, max_seq_len=96)
+    ref = oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                  dtype="bf16")
+    assert np.allclose(out, ref[0], atol=1e-13)
+
+
+def check_brute_force_keep(fn):
+    """Estimates by explicit loops and the keep rule written out per block."""
+    a, codes, scales = _case(62, B=1, Hq=4, Hkv=2, D=16, L=80, lens=(75,))
+    q = oracle.decode_values(a["q"], "bf16")
+    sc = 1.0 / math.sqrt(16)
+    for delta in (0.0, 0.3, 1.0):
+        out, lse, est, kept = fn(a["q"], a["k"], a["v"], a["seq_lens"],
+                                 codes, scales, delta=delta, num_splits=2,
+                                 max_seq_len=80)
+        # P = 48: split 0 = blocks 0..2, split 1 = blocks 3..4 (75 tokens)
+        for kvh in range(2):
+            e = {}
+            for h in (2 * kvh, 2 * kvh + 1):
+                for j in range(5):
+                    best = -math.inf
+                    for t in range(16 * j, min(16 * j + 16, 75)):
+                        acc = 0.0
+                        for d in range(16):
+                            acc += q[0, h, d] * codes[0, kvh, t, d]
+                        best = max(best, acc)
+                    e[h, j] = sc * float(scales[0, kvh, j]) * best
+                    assert abs(est[0, h, j] - e[h, j]) < 1e-12
+            for blocks in ((0, 1, 2), (3, 4)):
+                for j in blocks:
+                    want = any(e[h, j] >= max(e[h, i] for i in blocks) - delta
+                               for h in (2 * kvh, 2 * kvh + 1))
+                    assert kept[0, kvh, j] == want, (delta, kvh, j)
+
+
+def check_masked_sdpa(fn):
+    """The result is torch's float64 SDPA restricted to the kept tokens."""
+    a, codes, scales = _case(63, needles=[5, 130])
+    out, lse, _, kept = fn(a["q"], a["k"], a["v"], a["seq_lens"], codes,
+                           scales, delta=1.5, num_splits=4, max_seq_len=200)
+    q = torch.from_numpy(oracle.decode_values(a["q"], "bf16"))
+    k = torch.from_numpy(oracle.decode_values(a["k"], "bf16"))
+    v = torch.from_numpy(oracle.decode_values(a["v"], "bf16"))
+    assert 0 < kept.sum() < kept.size
+    for b in range(2):
+        n = int(a["seq_lens"][b])
+        for h in range(4):
+            kvh = h // 2
+            mask = torch.tensor([bool(kept[b, kvh, t // 16]) for t in range(n)])
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[b, h][None, None, None], k[b, kvh, :n][None, None],
+                v[b, kvh, :n][None, None], attn_mask=mask[None, None, None])
+            assert np.allclose(out[b, h], ref[0, 0, 0].numpy(), atol=1e-12)
+
+
+def check_keep_invariants(fn):
+    a, codes, scales = _case(64, L=512, lens=(512, 300), needles=[200])
+    prev = None
+    for delta in (0.0, 0.5, 2.0, 8.0):
+        _, _, est, kept = fn(a["q"], a["k"], a["v"], a["seq_lens"], codes,
+                             scales, delta=delta, num_splits=4,
+                             max_seq_len=512)
+        if prev is not None:
+            assert np.all(kept >= prev)            # monotone in delta
+        prev = kept
+        for b, n in ((0, 512), (1, 300)):
+            for s in range(4):
+                j0, j1 = 8 * s, min(8 * s + 8, -(-n // 16))
+                if j1 <= j0:
+                    continue
+                for h in range(4):           # every head's top block kept
+                    top = j0 + int(np.nanargmax(est[b, h, j0:j1]))
+                    assert kept[b, h // 2, top]
+    # the needle (logit 12 for head 0) dominates its split at delta 0
+    _, _, est, kept = fn(a["q"], a["k"], a["v"], a["seq_lens"], codes,
+                         scales, delta=0.0, num_splits=4, max_seq_len=512)
+    assert kept[0, 0, 200 // 16] and kept[1, 0, 200 // 16]
+
+
+CHECKS = [check_dense_limit, check_one_block_per_split_is_dense,
+          check_brute_force_keep, check_masked_sdpa, check_keep_invariants]
+
+
+def test_reference_passes_every_check():
+    for chk in CHECKS:
+        chk(osp.sparse_decode_attention)
+
+
+def _mutant(kind):
+    """sparse_decode_attention with one plausible mistake in the keep step."""
+    def fn(q, k, v, seq_lens, codes, scales, *, delta, num_splits,
+           max_seq_len, scale=None, block_table=None, block_size=0):
+        qf = oracle.decode_values(q, "bf16")
+        B, Hq, D = qf.shape
+        Hkv = k.shape[1]
+        G = Hq // Hkv
+        sc = 1.0 / math.sqrt(D)
+        P = oracle.split_length(max_seq_len, num_splits)
+        nblk = -(-max_seq_len // 16)
+        out = np.zeros((B, Hq, D))
+        lse = np.full((B, Hq), -np.inf)
+        est = np.full((B, Hq, nblk), np.nan)
+        kept = np.zeros((B, Hkv, nblk), dtype=bool)
+        for b in range(B):
+            n = int(seq_lens[b])
+            for kvh in range(Hkv):
+                heads = slice(kvh * G, (kvh + 1) * G)
+                for j in range(-(-n // 16)):
+                    c = codes[b, kvh, 16 * j:min(16 * j + 16, n)].astype(float)
+                    sj = 1.0 if kind == "no_block_scale" else float(
+                        scales[b, kvh, j])
+                    sc_all = qf[b, heads] @ c.T
+                    red = sc_all.mean(axis=1) if kind == "mean_not_max" \
+                        else sc_all.max(axis=1)
+                    est[b, heads, j] = sc * sj * red
+                for s_ in range(num_splits):
+                    j0 = s_ * P // 16
+                    j1 = -(-min((s_ + 1) * P, n) // 16)
+                    if kind == "split_off_by_one":
+                        j1 = max(j0, j1 - 1)
+                    if j1 <= j0:
+                        continue
+                    e = est[b, heads, j0:j1]
+                    M = e.max(axis=1, keepdims=True)
+                    if kind == "global_threshold":
+                        M = np.nanmax(est[b, heads], axis=1, keepdims=True)
+                    ok = e >= M - delta
+                    kept[b, kvh, j0:j1] = (ok.all(axis=0) if kind == "all_heads"
+                                           else ok.any(axis=0))
+                toks = [t for t in range(n) if kept[b, kvh, t // 16]]
+                if not toks:
+                    continue
+                kr = oracle.decode_values(k[b, kvh, toks], "bf16")
+                vr = oracle.decode_values(v[b, kvh, toks], "bf16")
+                o, l = oracle.softmax_attention(sc * (qf[b, heads] @ kr.T), vr)
+                out[b, heads] = o
+                lse[b, heads] = l
+        return out, lse, est, kept
+    return fn
+
+
+MUTANTS = ["no_block_scale", "mean_not_max", "split_off_by_one",
+           "global_threshold", "all_heads"]
+
+
+def test_mutant_copy_without_mistake_passes():
+    fn = _mutant("none")
+    for chk in CHECKS:
+        chk(fn)
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_planted_mistake_is_caught(kind):
+    fn = _mutant(kind)
+    failed = []
+    for chk in CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                chk(fn)
+        except (AssertionError, IndexError, ValueError):
+            failed.append(chk.__name__)
+    assert failed, f"mutant {kind} passed every sparse pin"
