@@ -207,6 +207,60 @@ int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
                            float* o_part, float* lse_part, void* stream);
 
 /*
+ * Block-sparse decode ("Faster Than Flash: Exploiting Attention Sparsity
+ * for Efficient Long-Context Decoding", abstract): a 4-bit copy of the keys
+ * is scanned to estimate each 16-token block's best logit, a top-delta rule
+ * keeps the blocks that matter, and exact attention runs over those only.
+ * The page defines neither the quantizer nor the rule; the readings here:
+ *
+ * Key summary (fd_build_key_summary), per 16-token block and kv head, over
+ * the block's attended rows: amax = max |k| (all dims); inv = 7 / amax and
+ * scale = amax / 7, each one correctly rounded fp32 operation (0 when
+ * amax = 0); code = rint(k * inv) (fp32 product, ties to even), in [-7, 7],
+ * stored as 4-bit two's complement, dim 2m in the low nibble of byte m of
+ * the row. Rows past a sequence's length get code 0.
+ *
+ *   codes   device uint8, the layout of k_cache with head_dim / 2 bytes per
+ *           row: contiguous [batch, Hkv, max_seq_len, head_dim/2], paged
+ *           [num_blocks, Hkv, block_size, head_dim/2]; 16-byte aligned
+ *   scales  device fp32: contiguous [batch, Hkv, ceil(max_seq_len/16)];
+ *           paged [num_blocks, Hkv, block_size/16]; 4-byte aligned
+ * Only blocks holding at least one attended token are written. bf16 keys
+ * only (shape->dtype FD_DTYPE_BF16); k_cache / block_table / seq_lens as
+ * for fd_decode_attn.
+ */
+int fd_build_key_summary(const fd_shape* shape, const void* k_cache,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         void* codes, float* scales, void* stream);
+
+/*
+ * Sparse decode over the summary: in split s of sequence b and kv head g,
+ * with est[j, h] = scale_attn * scales[j] * max over block j's attended
+ * tokens of <q[b,h], codes>, block j is kept when
+ * est[j, h] >= max_j' est[j', h] - delta for some query head h of g (the
+ * maximum taken over the split's blocks only: no workgroup waits on
+ * another). The result is exact attention over every kept block's tokens;
+ * delta = +INFINITY keeps every block (the dense result up to rounding).
+ *
+ *   delta      >= 0, natural-log units (not NaN)
+ *   num_splits as for fd_decode_attn, with at most 8192 tokens per split
+ *              (FD_ERR_UNSUPPORTED otherwise)
+ *   kept_out   device uint8 [batch, Hkv, ceil(max_seq_len/16)] receiving
+ *              1 (kept) / 0 for every block holding an attended token
+ *              (other entries untouched), or NULL
+ * Supported: bf16 (shape->dtype FD_DTYPE_BF16), head_dim 64 / 128, at most
+ * 16 query heads per kv head. Other arguments as for fd_decode_attn.
+ */
+int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          const void* codes, const float* scales,
+                          const int32_t* block_table,
+                          const int32_t* seq_lens, float delta,
+                          int num_splits, void* workspace,
+                          size_t workspace_bytes, float* out, float* lse_out,
+                          uint8_t* kept_out, void* stream);
+
+/*
  * The reduction step alone: for each (b, h), with M = max_s lse_part[b,h,s],
  *   out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M},
  *   lse = M + ln sum_s e^{lse_s - M};

@@ -28,7 +28,8 @@ _DTYPES = {"f32": FD_DTYPE_F32, "bf16": FD_DTYPE_BF16,
 
 SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_decode_attn",
            "fd_decode_partials", "fd_decode_attn_fp8",
-           "fd_decode_partials_fp8", "fd_combine_partials", "fd_status_str",
+           "fd_decode_partials_fp8", "fd_build_key_summary",
+           "fd_decode_attn_sparse", "fd_combine_partials", "fd_status_str",
            "fd_version"]
 
 
@@ -75,6 +76,10 @@ def load() -> ctypes.CDLL:
                                        P, P]
     lib.fd_decode_partials_fp8.argtypes = [SH, P, P, P, P, P, P, P, I, P, P,
                                            P]
+    lib.fd_build_key_summary.argtypes = [SH, P, P, P, P, P, P]
+    lib.fd_decode_attn_sparse.argtypes = [SH, P, P, P, P, P, P, P,
+                                          ctypes.c_float, I, P, SZ, P, P, P,
+                                          P]
     lib.fd_combine_partials.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.fd_status_str.argtypes = [I]
     lib.fd_status_str.restype = ctypes.c_char_p
@@ -182,6 +187,31 @@ def fd_decode_partials_fp8(shape: FdShape, q, k_cache, v_cache, k_scale,
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
         int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def fd_build_key_summary(shape: FdShape, k_cache, block_table, seq_lens,
+                         codes, scales, stream=None) -> None:
+    """4-bit key summary (codes + per-16-token-block scales) of bf16 keys."""
+    _check("fd_build_key_summary", load().fd_build_key_summary(
+        ctypes.byref(shape), _ptr(k_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def fd_decode_attn_sparse(shape: FdShape, q, k_cache, v_cache, codes, scales,
+                          block_table, seq_lens, delta: float,
+                          num_splits: int, workspace, out, lse_out=None,
+                          kept_out=None, stream=None,
+                          workspace_bytes: Optional[int] = None) -> None:
+    """Block-sparse decode: top-delta over the key summary, exact attention
+    over the kept 16-token blocks."""
+    ws_bytes = (workspace_bytes if workspace_bytes is not None else
+                (0 if workspace is None or isinstance(workspace, int)
+                 else workspace.numel() * workspace.element_size()))
+    _check("fd_decode_attn_sparse", load().fd_decode_attn_sparse(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(codes), _ptr(scales), _ptr(block_table), _ptr(seq_lens),
+        float(delta), int(num_splits), _ptr(workspace), ws_bytes, _ptr(out),
+        _ptr(lse_out), _ptr(kept_out), _stream(stream)))
 
 
 def fd_combine_partials(batch: int, num_q_heads: int, head_dim: int,

@@ -330,6 +330,99 @@ int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
                          stream);
 }
 
+int fd_build_key_summary(const fd_shape* shape, const void* k_cache,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         void* codes, float* scales, void* stream) {
+  Shape s;
+  int st = check_shape(shape, &s);
+  if (st != FD_OK) return st;
+  if (s.dtype != FD_DTYPE_BF16) return FD_ERR_UNSUPPORTED;
+  st = check_inputs(s, k_cache, k_cache, k_cache, block_table, seq_lens);
+  if (st != FD_OK) return st;
+  if (!codes || !scales || !aligned16(codes) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return FD_ERR_INVALID_ARG;
+  SummaryArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.scales = scales;
+  a.Hkv = s.Hkv;
+  a.L = s.L;
+  a.bs = s.bs;
+  a.max_blocks = s.max_blocks;
+  a.num_blocks = s.num_blocks;
+  a.nblk_row = (s.L + 15) / 16;
+  if ((int64_t)a.nblk_row > INT32_MAX - 1) return FD_ERR_UNSUPPORTED;
+  return launch_summary(s, a, stream) == 0 ? FD_OK : FD_ERR_HIP;
+}
+
+int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          const void* codes, const float* scales,
+                          const int32_t* block_table,
+                          const int32_t* seq_lens, float delta,
+                          int num_splits, void* workspace, size_t ws_bytes,
+                          float* out, float* lse_out, uint8_t* kept_out,
+                          void* stream) {
+  Shape s;
+  int st = check_shape(shape, &s);
+  if (st != FD_OK) return st;
+  if (s.dtype != FD_DTYPE_BF16 || s.G > kHeadsPerGroup)
+    return FD_ERR_UNSUPPORTED;
+  st = check_splits(s, num_splits);
+  if (st != FD_OK) return st;
+  if (tokens_per_split(s, num_splits) > kMaxSparseSplit)
+    return FD_ERR_UNSUPPORTED;
+  st = check_inputs(s, q, k_cache, v_cache, block_table, seq_lens);
+  if (st != FD_OK) return st;
+  if (!codes || !scales || !aligned16(codes) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return FD_ERR_INVALID_ARG;
+  if (isnan(delta) || delta < 0.f) return FD_ERR_INVALID_ARG;
+  if (!out || !aligned16(out)) return FD_ERR_INVALID_ARG;
+  if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0)
+    return FD_ERR_INVALID_ARG;
+  if (num_splits > 1) {
+    if (!workspace || ws_bytes < workspace_bytes(s, num_splits))
+      return FD_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FD_ERR_INVALID_ARG;
+  }
+  SplitArgs a = make_split_args(s, q, k_cache, v_cache, block_table, seq_lens,
+                                num_splits);
+  SparseArgs sp;
+  sp.codes = static_cast<const uint8_t*>(codes);
+  sp.scales = scales;
+  sp.kept_out = kept_out;
+  sp.delta_log2 = (float)((double)delta * 1.4426950408889634);
+  sp.nblk_row = (s.L + 15) / 16;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = nullptr;
+  if (num_splits == 1) {
+    a.o_dst = out;
+    a.lse_dst = lse_out;
+    a.final_out = 1;
+    return launch_sparse(s, a, sp, stream) == 0 ? FD_OK : FD_ERR_HIP;
+  }
+  lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      partial_o_bytes(s, num_splits));
+  a.o_dst = o_part;
+  a.lse_dst = lse_part;
+  a.final_out = 0;
+  if (launch_sparse(s, a, sp, stream) != 0) return FD_ERR_HIP;
+  CombineArgs c;
+  c.o_part = o_part;
+  c.lse_part = lse_part;
+  c.out = out;
+  c.lse_out = lse_out;
+  c.B = s.B;
+  c.Hq = s.Hq;
+  c.S = num_splits;
+  return launch_combine(s.D, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
+}
+
 int fd_combine_partials(int batch, int num_q_heads, int head_dim,
                         int num_splits, const float* o_part,
                         const float* lse_part, float* out, float* lse_out,

@@ -24,6 +24,7 @@ constexpr int kLongSplitTokens = 1024;
 constexpr int kMaxSplits = 65535;
 constexpr int kMaxBlockSize = 4096;
 constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves
+constexpr int kMaxSparseSplit = 8192;   // sparse path: tokens per split
 
 // A validated, resolved call shape.
 struct Shape {
@@ -65,9 +66,31 @@ struct CombineArgs {
   int B, Hq, S;
 };
 
-// Launchers (fd_kernels.hip). Return hipError_t as int.
+// Key summary builder (4-bit codes + per-16-token-block scales).
+struct SummaryArgs {
+  const uint16_t* k;            // bf16 keys, contiguous or paged
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  uint8_t* codes;               // layout of k with D/2 bytes per row
+  float* scales;                // [B,Hkv,nblk_row] or [NB,Hkv,bs/16]
+  int Hkv, L, bs, max_blocks, num_blocks, nblk_row;
+};
+
+// Extra arguments of the sparse split kernel.
+struct SparseArgs {
+  const uint8_t* codes;
+  const float* scales;
+  uint8_t* kept_out;            // [B,Hkv,nblk_row] or null
+  float delta_log2;             // top-delta in base-2 logit units (>= 0)
+  int nblk_row;                 // ceil(L / 16)
+};
+
+// Launchers (fd_kernels.hip, fd_sparse.hip). Return hipError_t as int.
 int launch_split(const Shape& s, const SplitArgs& a, void* stream);
 int launch_combine(int D, const CombineArgs& a, void* stream);
+int launch_summary(const Shape& s, const SummaryArgs& a, void* stream);
+int launch_sparse(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
+                  void* stream);
 
 }  // namespace fd
 

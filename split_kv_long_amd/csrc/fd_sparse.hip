@@ -1,0 +1,446 @@
+// Block-sparse decode over a 4-bit key summary, for gfx950.
+//
+// After the abstract of "Faster Than Flash: Exploiting Attention Sparsity
+// for Efficient Long-Context Decoding": a low-bit quantized copy of the keys
+// is scanned to judge which blocks of the history matter, a top-delta rule
+// keeps the blocks whose estimated best logit comes within delta of the
+// best one (decided inside each split, so no workgroup waits on another),
+// and exact attention runs over the kept blocks only. The partials then go
+// through the ordinary log-sum-exp combine.
+//
+// Kernels:
+//   summary_kernel<D>   bf16 keys -> 4-bit codes (two per byte, even dim in
+//                       the low nibble) + one fp32 scale per 16-token block
+//                       and kv head: scale = amax / 7, code =
+//                       rint(k * (7 / amax)).
+//   split_sparse<D, NW, GM, PAGED>
+//                       one workgroup per (split, kv head, sequence):
+//                       phase 1 scans the split's summary blocks (MFMA on the
+//                       codes), phase 2 keeps blocks per top-delta, phase 3
+//                       runs exact bf16 attention over the kept blocks.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fd_device.h"
+#include "fd_internal.h"
+
+namespace fd {
+namespace {
+
+constexpr int kSumBlock = 16;   // tokens per summary block
+
+// ----------------------------------------------------------------------------
+// Key summary.
+
+// One wave per (16-token block, kv head, sequence). Lane l takes row l / 4
+// of the block and the quarter l % 4 of its dims. Blocks with no attended
+// token are skipped; rows past the length get code 0.
+template <int D>
+__global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
+  constexpr int QD = D / 4;                  // dims per lane
+  const int lane = threadIdx.x;
+  const int blk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : (len > a.L ? a.L : len);
+  const int t0 = blk * kSumBlock;
+  if (t0 >= len) return;
+  const int r = lane >> 2, part = lane & 3;
+  const int t = t0 + r;
+  const bool valid = t < len;
+  const bool exists = a.bs > 0 || t < a.L;   // contiguous rows stop at L
+  size_t row;                                // element offset of row t
+  if (a.bs == 0) {
+    row = ((size_t)(b * a.Hkv + kvh) * a.L + t);
+  } else {
+    const int page = t / a.bs;
+    int pb = a.block_table[(size_t)b * a.max_blocks + page];
+    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    row = ((size_t)pb * a.Hkv + kvh) * a.bs + (t - page * a.bs);
+  }
+  float x[QD];
+  float amax = 0.f;
+  if (valid) {
+    const uint16_t* kp = a.k + row * D + part * QD;
+#pragma unroll
+    for (int c = 0; c < QD / 8; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(kp + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+        x[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < QD; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < QD; ++i) x[i] = 0.f;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  // Correctly rounded fp32 quotients (HIP's default division).
+  const float inv = amax > 0.f ? 7.0f / amax : 0.f;
+  const float scale = amax > 0.f ? amax / 7.0f : 0.f;
+  if (exists) {
+    unsigned packed[QD / 8];
+#pragma unroll
+    for (int wd = 0; wd < QD / 8; ++wd) {
+      unsigned v = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = (int)__builtin_rintf(x[8 * wd + e] * inv);
+        v |= ((unsigned)c & 0xFu) << (4 * e);
+      }
+      packed[wd] = v;
+    }
+    uint8_t* cp = a.codes + row * (D / 2) + part * (QD / 2);
+    if (QD == 32)
+      *reinterpret_cast<u32x4*>(cp) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    else
+      *reinterpret_cast<u32x2*>(cp) = u32x2{packed[0], packed[1]};
+  }
+  if (lane == 0) {
+    size_t si;
+    if (a.bs == 0) {
+      si = (size_t)(b * a.Hkv + kvh) * a.nblk_row + blk;
+    } else {
+      const int page = t0 / a.bs;
+      int pb = a.block_table[(size_t)b * a.max_blocks + page];
+      pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+      si = ((size_t)pb * a.Hkv + kvh) * (a.bs / kSumBlock) +
+           (t0 - page * a.bs) / kSumBlock;
+    }
+    a.scales[si] = scale;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Sparse split kernel.
+
+// 4-bit codes -> bf16 operands holding 136 + code (exact). A dword of 8
+// nibbles (dims 2m in low nibbles) becomes 4 dwords of bf16 pairs: flipping
+// bit 3 of each nibble turns code s into s + 8 in [0, 15], and 0x4300 | m
+// is the bf16 value 128 + m. The offset 136 times the query's dim sum is
+// subtracted after the product.
+__device__ __forceinline__ u32x4 nib8_to_bf16(unsigned w) {
+  const unsigned y = w ^ 0x88888888u;
+  const unsigned lo = y & 0x0F0F0F0Fu;          // even dims, one per byte
+  const unsigned hi = (y >> 4) & 0x0F0F0F0Fu;   // odd dims
+  // byte k of lo / hi -> bf16 mantissas of dims 2k / 2k+1
+  const unsigned d0 = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u);
+  const unsigned d1 = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u);
+  const unsigned d2 = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u);
+  const unsigned d3 = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u);
+  return u32x4{d0 | 0x43004300u, d1 | 0x43004300u, d2 | 0x43004300u,
+               d3 | 0x43004300u};
+}
+
+constexpr int kMaxSparseBlocks = kMaxSparseSplit / kSumBlock;
+
+// Lane layout as in the dense MFMA kernel (lane l: n = l % 16, j = l / 16;
+// S^T = K * Q^T so a lane holds one head n and tokens 4j..4j+3 of a 16-token
+// tile). Scan operand order: lane group j covers the code dims
+// [32j, 32j + 32) at D = 128 ([16j, 16j + 16) at D = 64), 8 per MFMA call;
+// the query fragments follow the same order.
+template <int D, int NW, int GM, bool PAGED>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void split_sparse(SplitArgs a, SparseArgs sp) {
+  constexpr int KC = D / 32;
+  constexpr int NV = D / 16;
+  constexpr int DP = D + 4;
+  constexpr int CB = D / 8;                    // code bytes per lane per row
+  __shared__ float est_s[kMaxSparseBlocks][GM];
+  __shared__ float wmax_s[NW][GM];
+  __shared__ uint8_t keep_s[kMaxSparseBlocks];
+  __shared__ float mo[NW][GM][DP];
+  __shared__ float mm[NW][GM], ml[NW][GM];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, j = lane >> 4;
+  const int s = blockIdx.z, b = blockIdx.y;
+  const int kvh = blockIdx.x;                  // one head group per kv head
+  const int G = a.G, Hkv = a.Hkv, L = a.L, bs = a.bs;
+  const int h0 = kvh * G;
+  const int nh = G;
+  const int lo = s * a.P;
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : (len > L ? L : len);
+  const int hi = min(lo + a.P, len);
+  if (lo >= hi) {
+    write_empty<D>(a, b, h0, nh, s);
+    return;
+  }
+  const int nb = (hi - lo + kSumBlock - 1) / kSumBlock;   // blocks here
+  const int jg0 = lo / kSumBlock;
+  const uint16_t* K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+
+  // Row index (not yet times D) of token t of (b, kvh).
+  auto row_of = [&](int t) -> size_t {
+    if (!PAGED) return (size_t)(b * Hkv + kvh) * L + t;
+    const int page = t / bs;
+    int pb = __builtin_amdgcn_readfirstlane(
+        a.block_table[(size_t)b * a.max_blocks + page]);
+    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    return ((size_t)pb * Hkv + kvh) * bs + (t - page * bs);
+  };
+  auto scale_index = [&](int t) -> size_t {   // t = a block's first token
+    if (!PAGED) return (size_t)(b * Hkv + kvh) * sp.nblk_row + t / kSumBlock;
+    const int page = t / bs;
+    int pb = __builtin_amdgcn_readfirstlane(
+        a.block_table[(size_t)b * a.max_blocks + page]);
+    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    return ((size_t)pb * Hkv + kvh) * (bs / kSumBlock) +
+           (t - page * bs) / kSumBlock;
+  };
+
+  const int qh = h0 + (n < nh ? n : 0);        // padded columns reuse head h0
+  const uint16_t* qrow = Q + ((size_t)b * a.Hq + qh) * D;
+
+  // ---- phase 1: scan the summary -----------------------------------------
+  {
+    constexpr int SD = D / 4;                  // scan dims per lane group
+    bf16x8 qs[KC];
+    float qsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + SD * j + 8 * c);
+      qs[c] = as_bf16x8(v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qsum += __uint_as_float(v[e] << 16) + __uint_as_float(v[e] & 0xffff0000u);
+    }
+    qsum = sum_x32(sum_x16(qsum));             // head n's sum over all dims
+    float wmax = -INFINITY;
+    for (int jl = w; jl < nb; jl += NW) {
+      const int t0 = lo + jl * kSumBlock;
+      const int last = min(kSumBlock, hi - t0) - 1;
+      const size_t rw = row_of(t0 + min(n, last));
+      const float bscale = sp.scales[scale_index(t0)];
+      const uint8_t* cp = sp.codes + rw * (D / 2) + CB * j;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (D == 128) {
+        const u32x4 cw = *reinterpret_cast<const u32x4*>(cp);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(nib8_to_bf16(cw[c])), qs[c], acc, 0, 0, 0);
+      } else {
+        const u32x2 cw = *reinterpret_cast<const u32x2*>(cp);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(nib8_to_bf16(cw[c])), qs[c], acc, 0, 0, 0);
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * j + i <= last) bm = fmaxf(bm, acc[i] - 136.f * qsum);
+      bm = max_x32(max_x16(bm));
+      const float e = bm * bscale * a.scale_log2;   // base-2 logit units
+      if (j == 0 && n < GM) est_s[jl][n] = e;
+      wmax = fmaxf(wmax, e);
+    }
+    if (j == 0 && n < GM) wmax_s[w][n] = wmax;
+  }
+  __syncthreads();
+
+  // ---- phase 2: top-delta inside the split --------------------------------
+  {
+    float M = wmax_s[0][n < GM ? n : 0];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, wmax_s[ww][n < GM ? n : 0]);
+    for (int jl = w; jl < nb; jl += NW) {
+      const bool mine = j == 0 && n < nh && est_s[jl][n] >= M - sp.delta_log2;
+      const bool keep = __builtin_amdgcn_ballot_w64(mine) != 0;
+      if (lane == 0) {
+        keep_s[jl] = keep ? 1 : 0;
+        if (sp.kept_out)
+          sp.kept_out[(size_t)(b * Hkv + kvh) * sp.nblk_row + jg0 + jl] =
+              keep ? 1 : 0;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: exact attention over the kept blocks ----------------------
+  bf16x8 qf[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+    qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 8 * j + 32 * c));
+  f32x4 o[NV];
+#pragma unroll
+  for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int jl = w;
+  auto next_kept = [&]() -> int {
+    while (jl < nb && !keep_s[jl]) jl += NW;
+    const int r = jl < nb ? jl : -1;
+    jl += NW;
+    return r;
+  };
+  for (;;) {
+    const int ja = next_kept();
+    if (ja < 0) break;
+    const int jb = next_kept();                // -1: second half masked
+    const int ta = lo + ja * kSumBlock;
+    const int tb = jb >= 0 ? lo + jb * kSumBlock : ta;
+    const int lasta = min(kSumBlock, hi - ta) - 1;
+    const int lastb = jb >= 0 ? min(kSumBlock, hi - tb) - 1 : lasta;
+    const size_t ra = row_of(ta), rb = row_of(tb);
+    // Rows of a page block are consecutive (16 | page size).
+    const uint16_t* K0 = K + ra * D;
+    const uint16_t* K1 = K + rb * D;
+    const uint16_t* V0 = V + ra * D;
+    const uint16_t* V1 = V + rb * D;
+    u32x4 kr[2][KC], vr[8];
+    const unsigned r0 = (unsigned)(min(n, lasta) * D + 8 * j);
+    const unsigned r1 = (unsigned)(min(n, lastb) * D + 8 * j);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      kr[0][c] = ld16<true>(K0 + r0 + 32 * c);
+      kr[1][c] = ld16<true>(K1 + r1 + 32 * c);
+    }
+    const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vr[e] = ld16<true>(V0 + (unsigned)(min(4 * j + e, lasta) * D + vcol));
+      vr[4 + e] = ld16<true>(V1 + (unsigned)(min(4 * j + e, lastb) * D + vcol));
+    }
+    f32x4 sacc[2];
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      sacc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(kr[tg][c]), qf[c], sacc[tg], 0, 0, 0);
+    }
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * j + i;
+        const bool ok = tg == 0 ? r <= lasta : (jb >= 0 && r <= lastb);
+        const float x = ok ? sacc[tg][i] * a.scale_log2 : -INFINITY;
+        sv[4 * tg + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = max_x32(max_x16(mx));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = fexp2(m_run - mn);     // m_run = -inf: 0
+    m_run = mn;
+    bf16x8 ph, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = fexp2(sv[e] - mn);
+      psum += p;
+      const __bf16 hb = (__bf16)p;
+      ph[e] = hb;
+      pl[e] = (__bf16)(p - (float)hb);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int cc = 0; cc < NV; ++cc) {
+      o[cc] *= alpha;
+      const bf16x8 vk = v_kvec<D>(vr, cc, n);
+      o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, ph, o[cc], 0, 0, 0);
+      o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, pl, o[cc], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the waves (as in the dense kernel) ---------------------------
+  l_run = sum_x32(sum_x16(l_run));
+  if (n < nh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* rowp = &mo[w][n][out_dim<D>(0, i, j)];
+      *reinterpret_cast<f32x4*>(rowp) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+      if (D == 128)
+        *reinterpret_cast<f32x4*>(rowp + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
+    }
+    if (j == 0) {
+      mm[w][n] = m_run;
+      ml[w][n] = l_run;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
+    const int g = idx / (D / 4);
+    const int d = 4 * (idx - g * (D / 4));
+    float Mx = mm[0][g];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) Mx = fmaxf(Mx, mm[ww][g]);
+    const float Ms = Mx == -INFINITY ? 0.f : Mx;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float wt = fexp2(mm[ww][g] - Ms);
+      acc += wt * *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
+      lsum += wt * ml[ww][g];
+    }
+    const bool none = Mx == -INFINITY;
+    *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) =
+        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / lsum);
+    if (d == 0) {
+      float* l = lse_dst(a, b, h0 + g, s);
+      if (l) *l = none ? -INFINITY : (Mx + flog2(lsum)) * kLn2;
+    }
+  }
+}
+
+template <int D, int GM, bool PAGED>
+void launch_sparse_gm(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
+                      hipStream_t st) {
+  hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED>),
+                     dim3((unsigned)s.Hkv, (unsigned)s.B, (unsigned)a.S),
+                     dim3(8 * 64), 0, st, a, sp);
+}
+
+template <int D, bool PAGED>
+void launch_sparse_d(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
+                     hipStream_t st) {
+  if (s.G <= 8)
+    launch_sparse_gm<D, 8, PAGED>(s, a, sp, st);
+  else
+    launch_sparse_gm<D, 16, PAGED>(s, a, sp, st);
+}
+
+}  // namespace
+
+int launch_summary(const Shape& s, const SummaryArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((s.L + kSumBlock - 1) / kSumBlock), (unsigned)s.Hkv,
+                  (unsigned)s.B);
+  if (grid.x == 0) return 0;
+  if (s.D == 128)
+    hipLaunchKernelGGL((summary_kernel<128>), grid, dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((summary_kernel<64>), grid, dim3(64), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+int launch_sparse(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
+                  void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool paged = s.bs > 0;
+  if (s.D == 128) {
+    if (paged) launch_sparse_d<128, true>(s, a, sp, st);
+    else launch_sparse_d<128, false>(s, a, sp, st);
+  } else {
+    if (paged) launch_sparse_d<64, true>(s, a, sp, st);
+    else launch_sparse_d<64, false>(s, a, sp, st);
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace fd

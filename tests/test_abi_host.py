@@ -232,3 +232,49 @@ def test_fp8_shape_needs_the_fp8_entry_points():
     # planning and workspace sizing accept it
     assert fb.fd_plan_splits(s, 256, -1) >= 1
     assert fb.fd_workspace_size(s, 8) == fb.fd_workspace_size(shp(), 8)
+
+
+def test_sparse_and_summary_reject_bad_args():
+    lib = fb.load()
+    s = shp(max_seq_len=8192)
+    F = ctypes.c_float
+
+    def sparse(**kw):
+        args = dict(shape=s, q=FAKE, k=FAKE, v=FAKE, codes=FAKE, scales=FAKE,
+                    bt=None, lens=FAKE, delta=4.0, S=4, ws=FAKE,
+                    ws_bytes=1 << 30, out=FAKE, lse=None, kept=None)
+        args.update(kw)
+        return lib.fd_decode_attn_sparse(
+            ctypes.byref(args["shape"]), args["q"], args["k"], args["v"],
+            args["codes"], args["scales"], args["bt"], args["lens"],
+            F(args["delta"]), args["S"], args["ws"], args["ws_bytes"],
+            args["out"], args["lse"], args["kept"], None)
+
+    assert sparse(codes=None) == fb.FD_ERR_INVALID_ARG
+    assert sparse(codes=FAKE + 8) == fb.FD_ERR_INVALID_ARG
+    assert sparse(scales=None) == fb.FD_ERR_INVALID_ARG
+    assert sparse(delta=-1.0) == fb.FD_ERR_INVALID_ARG
+    assert sparse(delta=float("nan")) == fb.FD_ERR_INVALID_ARG
+    assert sparse(ws_bytes=10) == fb.FD_ERR_WORKSPACE
+    # more than 8192 tokens per split, more than 16 query heads per kv head,
+    # fp32 or E4M3 caches: not supported on this path
+    assert sparse(shape=shp(max_seq_len=16384), S=1) == fb.FD_ERR_UNSUPPORTED
+    assert sparse(shape=shp(max_seq_len=8192, num_q_heads=64, num_kv_heads=2)
+                  ) == fb.FD_ERR_UNSUPPORTED
+    assert sparse(shape=shp(max_seq_len=8192, dtype="f32")) == fb.FD_ERR_UNSUPPORTED
+    assert sparse(shape=shp(max_seq_len=8192, dtype="fp8_e4m3")
+                  ) == fb.FD_ERR_UNSUPPORTED
+
+    def summary(**kw):
+        args = dict(shape=s, k=FAKE, bt=None, lens=FAKE, codes=FAKE,
+                    scales=FAKE)
+        args.update(kw)
+        return lib.fd_build_key_summary(
+            ctypes.byref(args["shape"]), args["k"], args["bt"], args["lens"],
+            args["codes"], args["scales"], None)
+
+    assert summary(codes=None) == fb.FD_ERR_INVALID_ARG
+    assert summary(scales=FAKE + 2) == fb.FD_ERR_INVALID_ARG
+    assert summary(k=FAKE + 4) == fb.FD_ERR_INVALID_ARG
+    assert summary(shape=shp(dtype="f32")) == fb.FD_ERR_UNSUPPORTED
+    assert summary(bt=FAKE) == fb.FD_ERR_INVALID_ARG

@@ -1,0 +1,238 @@
+"""Parity of the block-sparse path (key summary + top-delta + exact attention
+over kept blocks) against the float64 oracle (needs a gfx950 GPU).
+
+* The key summary is integer work decided in fp32 on both sides: codes and
+  scales must match the oracle bit for bit.
+* The kept-block set must match the oracle's on every block whose estimate
+  is not within EST_TOL of the threshold (there fp32 vs float64 rounding of
+  the estimate may decide either way); the output must match exact
+  attention over the blocks the kernel kept, to the bf16 bar (2e-3).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import sparse as osp
+import workloads
+from split_kv_long_amd import binding as fb
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+TOL = 2e-3
+LSE_TOL = 1e-4
+EST_TOL = 2e-3
+
+
+def shape_of(w):
+    return fb.make_shape(**w.shape_dict())
+
+
+def gpu_summary(w, t):
+    d = torch.device("cuda")
+    D = w.head_dim
+    codes = torch.full(tuple(w.k.shape[:-1]) + (D // 2,), 0xAA,
+                       dtype=torch.uint8, device=d)
+    if w.paged:
+        scales = torch.full((w.k.shape[0], w.num_kv_heads, w.block_size // 16),
+                            -1.0, device=d)
+    else:
+        scales = torch.full((w.batch, w.num_kv_heads,
+                             -(-w.max_seq_len // 16)), -1.0, device=d)
+    print(f"[gpu] summary {w.name} paged={w.paged} D={D}", flush=True)
+    fb.fd_build_key_summary(shape_of(w), t["k"], t["bt"], t["lens"], codes,
+                            scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+def device_inputs(w):
+    d = torch.device("cuda")
+    return dict(q=w.q.to(d), k=w.k.to(d), v=w.v.to(d), lens=w.seq_lens.to(d),
+                bt=None if w.block_table is None else w.block_table.to(d))
+
+
+def written_rows(w):
+    """(b-or-block, kvh, row) index arrays of every row the summary writes."""
+    a = w.numpy_view()
+    out = []
+    for b in range(w.batch):
+        n = int(a["seq_lens"][b])
+        for kvh in range(w.num_kv_heads):
+            for j in range(-(-n // 16)):
+                for r in range(16 * j, 16 * j + 16):
+                    if w.paged:
+                        blk = a["block_table"][b, r // w.block_size]
+                        out.append((blk, kvh, r % w.block_size))
+                    elif r < w.max_seq_len:
+                        out.append((b, kvh, r))
+    return tuple(np.array(x) for x in zip(*out))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("d", [128, 64])
+def test_summary_matches_oracle_bitwise(paged, d):
+    lens = [1, 15, 16, 17, 100, 0, 333]
+    w = workloads.make("sum", seed=71, batch=len(lens), num_q_heads=8,
+                       num_kv_heads=2, head_dim=d, max_seq_len=333,
+                       paged=paged, seq_lens=lens, poison_tail=True)
+    t = device_inputs(w)
+    codes, scales = gpu_summary(w, t)
+    a = w.numpy_view()
+    ref_c, ref_s = osp.key_summary(a["k"], a["seq_lens"], a["block_table"],
+                                   w.block_size)
+    got = codes.cpu().numpy()
+    rows = written_rows(w)
+    assert np.array_equal(osp.unpack_int4(got[rows]), ref_c[rows])
+    # nothing else was written
+    mask = np.ones(got.shape[:-1], dtype=bool)
+    mask[rows] = False
+    assert np.all(got[mask] == 0xAA)
+    gs = scales.cpu().numpy()
+    for b in range(w.batch):
+        n = lens[b]
+        for kvh in range(2):
+            for j in range(-(-n // 16)):
+                s_ref = osp.block_scale(ref_s, b, kvh, j, a["block_table"],
+                                        w.block_size)
+                s_got = osp.block_scale(gs, b, kvh, j, a["block_table"],
+                                        w.block_size)
+                assert np.float32(s_got) == np.float32(s_ref), (b, kvh, j)
+
+
+def sparse_case(seed, paged, d=128, hq=16, hkv=2, L=8192, lens=None):
+    lens = lens or [L]
+    return workloads.make("sparse", seed=seed, batch=len(lens),
+                          num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                          max_seq_len=L, paged=paged, seq_lens=lens,
+                          needles=[5, L // 3, L // 2 + 7, lens[-1] - 1],
+                          needle_logit=14.0, poison_tail=True)
+
+
+def run_sparse(w, t, codes, scales, delta, S):
+    d = torch.device("cuda")
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    out = torch.full((B, Hq, D), float("nan"), device=d)
+    lse = torch.full((B, Hq), float("nan"), device=d)
+    kept = torch.full((B, w.num_kv_heads, -(-w.max_seq_len // 16)), 7,
+                      dtype=torch.uint8, device=d)
+    shape = shape_of(w)
+    nbytes = fb.fd_workspace_size(shape, S)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=d)
+    print(f"[gpu] sparse {w.name} paged={w.paged} D={D} delta={delta} S={S}",
+          flush=True)
+    fb.fd_decode_attn_sparse(shape, t["q"], t["k"], t["v"], codes, scales,
+                             t["bt"], t["lens"], delta, S, ws, out, lse, kept)
+    torch.cuda.synchronize()
+    return (out.cpu().double().numpy(), lse.cpu().double().numpy(),
+            kept.cpu().numpy())
+
+
+def exact_over_kept(w, kept):
+    """Float64 attention of every head over the tokens of kept blocks."""
+    a = w.numpy_view()
+    q = oracle.decode_values(a["q"], "bf16")
+    B, Hq, D = q.shape
+    G = Hq // w.num_kv_heads
+    sc = w.effective_scale
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(a["seq_lens"][b])
+        for kvh in range(w.num_kv_heads):
+            toks = np.array([t for t in range(n) if kept[b, kvh, t // 16]],
+                            dtype=np.int64)
+            if toks.size == 0:
+                continue
+            kr = np.concatenate([oracle.decode_values(oracle.history_rows(
+                a["k"], b, kvh, t, t + 1, a["block_table"], a["block_size"]),
+                "bf16") for t in toks])
+            vr = np.concatenate([oracle.decode_values(oracle.history_rows(
+                a["v"], b, kvh, t, t + 1, a["block_table"], a["block_size"]),
+                "bf16") for t in toks])
+            hs = slice(kvh * G, (kvh + 1) * G)
+            o, l = oracle.softmax_attention(sc * (q[b, hs] @ kr.T), vr)
+            out[b, hs], lse[b, hs] = o, l
+    return out, lse
+
+
+def check_sparse(w, delta, S, expect_dropped=True):
+    t = device_inputs(w)
+    codes, scales = gpu_summary(w, t)
+    a = w.numpy_view()
+    ref_c, ref_s = osp.key_summary(a["k"], a["seq_lens"], a["block_table"],
+                                   w.block_size)
+    out, lse, kept = run_sparse(w, t, codes, scales, delta, S)
+    ro, rl, est, rkept = osp.sparse_decode_attention(
+        a["q"], a["k"], a["v"], a["seq_lens"], ref_c, ref_s, delta=delta,
+        num_splits=S, max_seq_len=w.max_seq_len, scale=w.scale,
+        block_table=a["block_table"], block_size=a["block_size"])
+    P = oracle.split_length(w.max_seq_len, S)
+    G = w.num_q_heads // w.num_kv_heads
+    n_amb = 0
+    for b in range(w.batch):
+        n = int(a["seq_lens"][b])
+        nb = -(-n // 16)
+        for kvh in range(w.num_kv_heads):
+            assert np.all(kept[b, kvh, nb:] == 7)       # untouched
+            got = kept[b, kvh, :nb].astype(bool)
+            want = rkept[b, kvh, :nb]
+            for j in np.nonzero(got != want)[0]:
+                s = j * 16 // P
+                j0, j1 = s * P // 16, min(-(-min((s + 1) * P, n) // 16), nb)
+                hs = slice(kvh * G, (kvh + 1) * G)
+                thr = np.nanmax(est[b, hs, j0:j1], axis=1) - delta
+                gap = np.abs(est[b, hs, j] - thr)
+                assert gap.min() <= EST_TOL * (1 + np.abs(thr).max()), \
+                    (b, kvh, j, gap.min())
+                n_amb += 1
+    if expect_dropped:
+        assert 0 < kept[kept != 7].sum() < (kept != 7).sum()
+    ref_out, ref_lse = exact_over_kept(w, kept.astype(bool) & (kept != 7))
+    assert np.all(np.isfinite(out))
+    err = float(np.abs(out - ref_out).max())
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isneginf(lse), ~fin)
+    lerr = float(np.abs(lse[fin] - ref_lse[fin]).max())
+    print(f"[gpu] sparse max|out-ref|={err:.3g} lse={lerr:.3g} "
+          f"kept={int(kept[kept != 7].sum())}/{int((kept != 7).sum())} "
+          f"ambiguous={n_amb}", flush=True)
+    assert err <= TOL and lerr <= LSE_TOL
+    return out, lse, kept
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("S", [1, 4, 16])
+def test_sparse_top_delta_matches_oracle(paged, S):
+    w = sparse_case(81, paged)
+    check_sparse(w, 1.0, S)
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 8), (64, 32, 4), (128, 12, 3)])
+def test_sparse_head_layouts_and_ragged(d, hq, hkv):
+    w = sparse_case(82, True, d=d, hq=hq, hkv=hkv, L=4000,
+                    lens=[4000, 1, 17, 2500])
+    check_sparse(w, 2.0, 3, expect_dropped=False)
+
+
+def test_sparse_delta_inf_is_dense():
+    w = sparse_case(83, False, L=6000, lens=[6000, 4321])
+    out, lse, kept = check_sparse(w, math.inf, 2, expect_dropped=False)
+    assert np.all(kept[kept != 7] == 1)
+    a = w.numpy_view()
+    ref = oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                  dtype="bf16")
+    assert np.abs(out - ref[0]).max() <= TOL
+
+
+def test_sparse_delta_zero_keeps_the_needles():
+    w = sparse_case(84, False, L=8192)
+    out, lse, kept = check_sparse(w, 0.0, 4)
+    for p in (5, 8192 // 3, 8192 // 2 + 7, 8191):
+        assert kept[0, 0, p // 16] == 1 and kept[0, 1, p // 16] == 1
