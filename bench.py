@@ -60,6 +60,10 @@ def parse_args():
     p.add_argument("--all", action="store_true",
                    help="also time every workload (extra JSON lines, "
                         "stderr)")
+    p.add_argument("--sparse-delta", type=float, default=None,
+                   help="time the block-sparse path (fd_decode_attn_sparse, "
+                        "top-delta with this delta) on the chosen workload "
+                        "instead of the dense one")
     p.add_argument("--frontier", action="store_true",
                    help="instead of the metric: sweep batch x history x "
                         "splits (uniform lengths, 16q/2kv d128 bf16) and "
@@ -385,6 +389,75 @@ def frontier(args):
             torch.cuda.empty_cache()
 
 
+def sparse_run(args):
+    """Block-sparse decode on one workload: the key summary is built once
+    per K copy outside the timed region (a serving loop would update it
+    incrementally), then K timed fd_decode_attn_sparse calls."""
+    import torch
+    import numpy as np
+    from split_kv_long_amd import binding as fb
+    b = Bench(args.workload, args.splits, args.steps,
+              parse_overrides(args.set))
+    w, dev = b.w, torch.device("cuda")
+    D, Hkv = w.head_dim, w.num_kv_heads
+    nblk = -(-w.max_seq_len // 16)
+    codes, scales = [], []
+    for r in range(b.R):
+        c = torch.empty(tuple(w.k.shape[:-1]) + (D // 2,), dtype=torch.uint8,
+                        device=dev)
+        sc = torch.empty((w.k.shape[0], Hkv, w.block_size // 16) if w.paged
+                         else (w.batch, Hkv, nblk), device=dev)
+        fb.fd_build_key_summary(b.shape, b.ks[r], b.bt, b.lens, c, sc)
+        codes.append(c)
+        scales.append(sc)
+
+    def build(i):
+        r = i % b.R
+        fb.fd_build_key_summary(b.shape, b.ks[r], b.bt, b.lens, codes[r],
+                                scales[r])
+    kept = torch.zeros(w.batch, Hkv, nblk, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        r = i % b.R
+        fb.fd_decode_attn_sparse(b.shape, b.q, b.ks[r], b.vs[r], codes[r],
+                                 scales[r], b.bt, b.lens, args.sparse_delta,
+                                 b.S, b.ws, b.out, b.lse, kept)
+    ms, _ = time_graph(torch, step, args.steps, args.warmup)
+    us = ms * 1e3 / args.steps
+    ms_b, _ = time_graph(torch, build, max(1, args.steps // 4), 2)
+    lens = w.seq_lens.numpy().astype(np.int64)
+    k = kept.cpu().numpy()
+    attended = kept_tok = 0
+    for bb in range(w.batch):
+        n = int(lens[bb])
+        nb = -(-n // 16)
+        for h in range(Hkv):
+            m = k[bb, h, :nb].astype(bool)
+            attended += n
+            kept_tok += int(m[:-1].sum()) * 16 + (
+                (n - 16 * (nb - 1)) if nb and m[-1] else 0)
+    row = D * 2                                       # bf16 bytes per row
+    scan = attended * D // 2 + attended // 16 * 4     # codes + scales
+    bytes_read = scan + 2 * kept_tok * row + w.batch * w.num_q_heads * D * 2
+    dense = 2 * attended * row
+    return {
+        "metric": "block-sparse decode us/call (top-delta over a 4-bit key "
+                  "summary)",
+        "value": round(us, 3), "unit": "us/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded, see workloads/)",
+        "config": {"workload": args.workload, "delta": args.sparse_delta,
+                   "num_splits": b.S, "tokens_per_split": b.P,
+                   "overrides": parse_overrides(args.set)},
+        "kept_token_fraction": round(kept_tok / max(attended, 1), 4),
+        "bytes_read_per_call": bytes_read,
+        "dense_kv_bytes": dense,
+        "achieved_GBps": round(bytes_read / (us * 1e3), 1),
+        "summary_build_us": round(ms_b * 1e3 / max(1, args.steps // 4), 3),
+    }
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -400,6 +473,9 @@ def main():
     binding.load()     # fails loudly if the HIP library is missing
     if args.frontier:
         frontier(args)
+        return
+    if args.sparse_delta is not None:
+        print(json.dumps(sparse_run(args)), flush=True)
         return
     rec = run_one(args, args.workload, args.steps, args.warmup,
                   not args.no_cpu_baseline)

@@ -23,6 +23,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fd_device.h"
 #include "fd_internal.h"
 
@@ -216,34 +218,41 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
     }
     qsum = sum_x32(sum_x16(qsum));             // head n's sum over all dims
     float wmax = -INFINITY;
-    for (int jl = w; jl < nb; jl += NW) {
-      const int t0 = lo + jl * kSumBlock;
-      const int last = min(kSumBlock, hi - t0) - 1;
-      const size_t rw = row_of(t0 + min(n, last));
-      const float bscale = sp.scales[scale_index(t0)];
-      const uint8_t* cp = sp.codes + rw * (D / 2) + CB * j;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (D == 128) {
-        const u32x4 cw = *reinterpret_cast<const u32x4*>(cp);
+    // A wave's blocks go CHUNK at a time: every code and scale request of a
+    // chunk is issued before the first product, one memory round trip each.
+    constexpr int CHUNK = 4;
+    using CT = typename std::conditional<D == 128, u32x4, u32x2>::type;
+    for (int jl0 = w; jl0 < nb; jl0 += NW * CHUNK) {
+      CT cw[CHUNK];
+      float bscale[CHUNK];
+      int lastr[CHUNK];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(nib8_to_bf16(cw[c])), qs[c], acc, 0, 0, 0);
-      } else {
-        const u32x2 cw = *reinterpret_cast<const u32x2*>(cp);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(nib8_to_bf16(cw[c])), qs[c], acc, 0, 0, 0);
+      for (int u = 0; u < CHUNK; ++u) {
+        const int jl = min(jl0 + NW * u, nb - 1);   // clamped: inside the split
+        const int t0 = lo + jl * kSumBlock;
+        lastr[u] = min(kSumBlock, hi - t0) - 1;
+        const size_t rw = row_of(t0 + min(n, lastr[u]));
+        bscale[u] = sp.scales[scale_index(t0)];
+        cw[u] = *reinterpret_cast<const CT*>(sp.codes + rw * (D / 2) + CB * j);
       }
-      float bm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * j + i <= last) bm = fmaxf(bm, acc[i] - 136.f * qsum);
-      bm = max_x32(max_x16(bm));
-      const float e = bm * bscale * a.scale_log2;   // base-2 logit units
-      if (j == 0 && n < GM) est_s[jl][n] = e;
-      wmax = fmaxf(wmax, e);
+      for (int u = 0; u < CHUNK; ++u) {
+        const int jl = jl0 + NW * u;
+        if (jl >= nb) break;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(nib8_to_bf16(cw[u][c])), qs[c], acc, 0, 0, 0);
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * j + i <= lastr[u]) bm = fmaxf(bm, acc[i] - 136.f * qsum);
+        bm = max_x32(max_x16(bm));
+        const float e = bm * bscale[u] * a.scale_log2;   // base-2 logit units
+        if (j == 0 && n < GM) est_s[jl][n] = e;
+        wmax = fmaxf(wmax, e);
+      }
     }
     if (j == 0 && n < GM) wmax_s[w][n] = wmax;
   }

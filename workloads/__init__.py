@@ -50,6 +50,14 @@ SPECS = {
         wid=2, batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
         max_seq_len=65536, dtype=BF16, kv_dtype=FP8, scale=None,
         paged=False),
+    # Needle-in-a-haystack structure (the retrieval-style long-context
+    # evaluations the "Faster Than Flash" page cites): haystack keys scaled
+    # so logits have std ~0.3, and in every 512-token chunk one 16-token
+    # block of keys every head of a kv group scores at logit ~6.
+    "needle_haystack_64k": dict(
+        wid=7, batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
+        max_seq_len=65536, dtype=BF16, scale=None, paged=False,
+        haystack_gain=0.3, needle_block_every=512, needle_block_logit=6.0),
     "short_batch": dict(
         wid=5, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
         max_seq_len=1024, dtype=BF16, scale=None, paged=False),
@@ -169,7 +177,10 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
          poison_tail: bool = False,
          needles: Optional[Sequence[int]] = None,
          needle_logit: float = 40.0,
-         kv_dtype: Optional[str] = None) -> Workload:
+         kv_dtype: Optional[str] = None,
+         haystack_gain: Optional[float] = None,
+         needle_block_every: Optional[int] = None,
+         needle_block_logit: Optional[float] = None) -> Workload:
     """Build a workload from a named recipe, with optional overrides.
 
     Draw order on one CPU generator: seq_lens (ragged recipes only), q, k, v,
@@ -182,6 +193,12 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
     needles: token positions p; for every (b, kv head) the key at p is set to
       c * q[b, first head of the group] with c chosen so that head's logit is
       ``needle_logit``, far above the N(0, 1)-scale logits of the other keys.
+    haystack_gain / needle_block_every / needle_block_logit: multiply every
+      key by haystack_gain, then in each chunk of needle_block_every
+      positions set one 16-aligned block (offset drawn after the block
+      table) of each (b, kv head) to the minimum-norm key on which every
+      query head of the group scores exactly needle_block_logit (before
+      bf16 rounding).
     kv_dtype: "fp8_e4m3" stores K and V as 8-bit E4M3 codes: per kv head,
       scale = amax / 448 over that head's whole pool (fp32), codes =
       E4M3(x / scale) rounded by torch; q stays bf16.
@@ -251,6 +268,28 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
             off += nblk[b]
 
     q = _cast(q32, dt)
+    hg = haystack_gain if haystack_gain is not None else spec.get(
+        "haystack_gain")
+    nbe = needle_block_every or spec.get("needle_block_every")
+    nbl = needle_block_logit if needle_block_logit is not None else spec.get(
+        "needle_block_logit", 6.0)
+    if hg is not None:
+        k32 *= hg
+    if nbe:
+        assert not pg and nbe % 16 == 0
+        scl = sc if sc else 1.0 / math.sqrt(D)
+        G = Hq // Hkv
+        qd = q.to(torch.float32)
+        offs = torch.randint(0, nbe // 16, (-(-L // nbe),), generator=g)
+        for b in range(B):
+            for h in range(Hkv):
+                qs = qd[b, h * G:(h + 1) * G].to(torch.float64)
+                # minimum-norm key with scl * <q_h, key> = nbl for every h
+                tgt = torch.full((G,), nbl / scl, dtype=torch.float64)
+                key = (qs.T @ torch.linalg.solve(qs @ qs.T, tgt)).float()
+                for c in range(-(-L // nbe)):
+                    p0 = c * nbe + 16 * int(offs[c])
+                    k32[b, h, p0:min(p0 + 16, L)] = key
     if needles:
         scl = sc if sc else 1.0 / math.sqrt(D)
         G = Hq // Hkv
