@@ -53,6 +53,9 @@ int check_shape(const fd_shape* s, Shape* out) {
   r.dtype = s->dtype;
   r.scale = s->scale > 0.f ? s->scale : (float)(1.0 / sqrt((double)s->head_dim));
   if ((int64_t)r.Hkv * head_groups(r) > INT32_MAX) return FD_ERR_UNSUPPORTED;  // grid x
+  // (sequence, kv head) row indices are formed in 32-bit arithmetic
+  if ((int64_t)r.B * r.Hkv > INT32_MAX || (int64_t)r.B * r.Hq > INT32_MAX)
+    return FD_ERR_UNSUPPORTED;
   if (out) *out = r;
   return FD_OK;
 }
@@ -61,11 +64,15 @@ int head_groups(const Shape& s) {
   return (s.G + kHeadsPerGroup - 1) / kHeadsPerGroup;
 }
 
-int tokens_per_split(const Shape& s, int num_splits) {
+static int64_t tokens_per_split64(const Shape& s, int num_splits) {
   const int64_t g = s.bs > 16 ? s.bs : 16;
   const int64_t L = s.L > 0 ? s.L : 1;
   const int64_t per = (L + num_splits - 1) / num_splits;
-  return (int)((per + g - 1) / g * g);
+  return (per + g - 1) / g * g;
+}
+
+int tokens_per_split(const Shape& s, int num_splits) {
+  return (int)tokens_per_split64(s, num_splits);   // checked by check_splits
 }
 
 size_t partial_o_bytes(const Shape& s, int num_splits) {
@@ -83,6 +90,9 @@ static int check_splits(const Shape& s, int num_splits) {
   // B*Hq*S*D must stay addressable with 64-bit offsets and 32-bit rows.
   if ((int64_t)s.B * s.Hq * num_splits > INT32_MAX) return FD_ERR_UNSUPPORTED;
   if ((int64_t)s.B * s.Hq * 16 > INT32_MAX) return FD_ERR_UNSUPPORTED;   // combine grid
+  // split starts s * P stay 32-bit
+  if ((int64_t)num_splits * tokens_per_split64(s, num_splits) > INT32_MAX)
+    return FD_ERR_UNSUPPORTED;
   return FD_OK;
 }
 

@@ -278,3 +278,21 @@ def test_sparse_and_summary_reject_bad_args():
     assert summary(k=FAKE + 4) == fb.FD_ERR_INVALID_ARG
     assert summary(shape=shp(dtype="f32")) == fb.FD_ERR_UNSUPPORTED
     assert summary(bt=FAKE) == fb.FD_ERR_INVALID_ARG
+
+
+def test_32bit_index_limits_are_enforced():
+    lib = fb.load()
+    # batch * kv heads beyond 32-bit row indices
+    s = shp(batch=65535, num_q_heads=65536, num_kv_heads=65536, max_seq_len=16)
+    out = ctypes.c_int(-99)
+    assert lib.fd_plan_splits(ctypes.byref(s), 256, -1,
+                              ctypes.byref(out)) == fb.FD_ERR_UNSUPPORTED
+    # S * P beyond 32 bits: the history bound near INT32_MAX, P rounded up
+    s = shp(max_seq_len=2 ** 31 - 1)
+    size = ctypes.c_size_t(0)
+    assert lib.fd_workspace_size(ctypes.byref(s), 1,
+                                 ctypes.byref(size)) == fb.FD_ERR_UNSUPPORTED
+    assert call(shape=s, S=1) == fb.FD_ERR_UNSUPPORTED
+    # a bound whose splits fit is fine for sizing
+    assert fb.fd_workspace_size(shp(max_seq_len=2 ** 31 - 16), 1) == 0
+    assert fb.fd_workspace_size(shp(max_seq_len=2 ** 30), 3) > 0

@@ -381,3 +381,39 @@ def test_fp8_paged_matches_contiguous_bitwise():
         o1, l1 = gpu_attention(w, S)
         o2, l2 = gpu_attention(c, S)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------ large sizes
+
+def test_million_token_history_and_max_splits():
+    """A 2^20-token history (512 MB of bf16 K/V for one kv head) at the
+    planned split count and at the largest split count the ABI allows
+    (65535: 16-token splits, half of them past the history's end)."""
+    L = 1 << 20
+    w = workloads.make("million", seed=91, batch=1, num_q_heads=8,
+                       num_kv_heads=1, head_dim=128, max_seq_len=L,
+                       seq_lens=[L - 3], needles=[L // 2 + 1], needle_logit=9.0)
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    planned = fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len())
+    for S in (planned, 65535):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"million/S={S}", "bf16", out, lse, ref_out, ref_lse)
+
+
+def test_large_ragged_batch():
+    """4096 short ragged sequences (lengths 0..48): batch x kv heads covers
+    the GPU many times over, so the planner does not split; forced splits
+    must agree too."""
+    g = torch.Generator().manual_seed(92)
+    lens = torch.randint(0, 49, (4096,), generator=g).tolist()
+    w = workloads.make("bigbatch", seed=92, batch=4096, num_q_heads=8,
+                       num_kv_heads=2, head_dim=64, max_seq_len=48,
+                       seq_lens=lens, paged=True, poison_tail=True)
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    planned = fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len())
+    assert planned == 1
+    for S in (1, 3):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"bigbatch/S={S}", "bf16", out, lse, ref_out, ref_lse)
