@@ -271,9 +271,17 @@ def run_one(args, name, steps, warmup, with_cpu):
     if b.S > 1:
         ms_c, _ = b.time_graph(b.combine_only, steps, 2)
         us_comb = ms_c * 1e3 / steps
+    w = b.w
+    # Batched calls (2..64 sequences) cut sequences into length-aware pieces
+    # inside fd_decode_attn; the split-only entry point keeps uniform splits,
+    # so the kernel the call runs is timed as the call minus the combine.
+    split_timing = "split-only launches (fd_decode_partials)"
+    if 1 < w.batch <= 64 and b.S > 1 and w.dtype != "f32":
+        us_split = us_call - us_comb
+        split_timing = ("call minus combine (length-aware pieces; "
+                        f"uniform-split launches: {round(ms_split * 1e3 / steps, 3)} us)")
     gbps = b.bytes_alg / (us_call * 1e3)
     split_gbps = b.bytes_split / (us_split * 1e3)
-    w = b.w
     # The counters were taken on the default 64K launch (planned splits).
     custom = name == args.workload and (args.splits or args.set)
     traffic = (read_traffic() if name == "long_gqa_64k" and not custom
@@ -319,6 +327,7 @@ def run_one(args, name, steps, warmup, with_cpu):
             "traffic": traffic,
             "bytes_per_launch": b.bytes_split,
             "launch_us": round(us_split, 3),
+            "timing": split_timing,
         },
     }
     if args.copy_probe and name == args.workload:

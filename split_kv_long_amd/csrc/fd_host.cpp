@@ -4,6 +4,7 @@
 // Nothing here touches the device; every check runs before anything is
 // enqueued, so a rejected call has no effect.
 
+#include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -122,6 +123,17 @@ static int check_scales(const Shape& s, const float* ks, const float* vs,
       (reinterpret_cast<uintptr_t>(vs) & 3u) != 0)
     return FD_ERR_INVALID_ARG;
   return FD_OK;
+}
+
+// Compute units of the current device (0 if the query fails: the uniform
+// split layout is used then).
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+      hipSuccess)
+    return 0;
+  return cus;
 }
 
 static SplitArgs make_split_args(const Shape& s, const void* q, const void* k,
@@ -243,6 +255,10 @@ static int decode_attn(const fd_shape* shape, const void* q,
                                 num_splits);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  // Batched calls cut each sequence into pieces by its length (the partial
+  // slots stay internal to this call, so their layout may differ from
+  // fd_decode_partials' uniform splits).
+  if (s.B > 1 && num_splits > 1) a.balance_cus = device_cus();
   if (num_splits == 1) {
     a.o_dst = out;
     a.lse_dst = lse_out;

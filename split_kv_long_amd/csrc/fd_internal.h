@@ -55,6 +55,8 @@ struct SplitArgs {
   int bs, max_blocks, num_blocks;
   int S, P, nhg;      // splits, tokens per split, head groups per kv head
   int final_out;      // 1: write normalised output + lse to out/lse_out
+  int balance_cus;    // > 0 (CU count): length-aware pieces for batches
+  int bal_target;     // set by the launcher: pieces per kv head unit
   float scale_log2;   // scale * log2(e)
 };
 

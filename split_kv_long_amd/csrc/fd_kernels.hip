@@ -243,6 +243,110 @@ __global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
 constexpr int kMaxPages = 1024;   // page ids a workgroup stages in LDS
 constexpr float kRefSlack = 8.f;  // exponent-reference slack, base 2
 
+// ----------------------------------------------------------------------------
+// Length-aware split pieces for batched calls.
+//
+// With one split length P for the whole batch, a ragged batch leaves short
+// last splits, and the number of busy workgroups rarely fits the CUs: some
+// CUs get one more split than others and set the kernel's time. Batched
+// fd_decode_attn calls (at most 64 sequences) therefore cut sequence b into
+// n_b = ceil(len_b / T) pieces of equal length (rounded to 16), with T >= P
+// the smallest multiple of 16 for which sum_b n_b <= target (about two
+// workgroups per CU over all kv head units); n_b <= S holds because T >= P.
+// Piece p of b goes to split slot p. Workgroups take pieces in dispatch
+// order (kv head unit fastest), so the busy ones are the first dispatched
+// and spread evenly over the CUs; the B * S - sum n_b idle ones each write
+// one unused slot (p >= n_b) as empty, so the combine still reads S valid
+// slots per (sequence, head). Every wave computes the same plan from the
+// lengths (lane = sequence) with wave-wide reductions and scans: no LDS, no
+// barrier, one length load.
+struct Piece { int b, slot, lo, hi, unit; };
+
+// Wave-wide integer sum on the VALU: DPP within each 16-lane row (swap
+// neighbours, swap pairs, rotate by 4 and by 8), then the row exchanges.
+__device__ __forceinline__ int wave_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);
+  const auto r16 = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v,
+                                                    false, false);
+  v = (int)(r16[0] + r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v,
+                                                    false, false);
+  return (int)(r32[0] + r32[1]);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int x = __shfl_up(v, off);
+    if (lane >= off) v += x;
+  }
+  return v;
+}
+
+__device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.B, S = a.S;
+  int len = 0;
+  if (lane < B) {
+    len = a.seq_lens[lane];
+    len = len < 0 ? 0 : (len > L ? L : len);
+  }
+  // Smallest T (multiple of 16, >= P) with sum ceil(len / T) <= target.
+  // sum ceil(len / T) lies in [W / T, W / T + B'] (W tokens, B' non-empty
+  // sequences), which brackets T; beyond L every sequence is one piece.
+  const int W = wave_sum(len);
+  const int Bn = wave_sum(len > 0 ? 1 : 0);
+  const int tgt = a.bal_target;
+  const int lmax = max(P, (L + 15) & ~15);
+  int tlo = max(P, min(lmax, ((int)(((long long)W + tgt - 1) / tgt) + 15) & ~15));
+  int thi = tgt > Bn ? min(lmax, ((int)(((long long)W + (tgt - Bn) - 1) /
+                                       (tgt - Bn)) + 15) & ~15)
+                     : lmax;
+  thi = max(thi, tlo);
+  while (tlo < thi) {
+    const int T = max(tlo, ((tlo + thi) >> 1) & ~15);
+    const int cnt = wave_sum(len > 0 ? (len + T - 1) / T : 0);
+    if (cnt <= a.bal_target) thi = T;
+    else tlo = T + 16;
+  }
+  const int T = tlo;
+  const int nb = len > 0 ? (len + T - 1) / T : 0;
+  const int unused = lane < B ? S - nb : 0;
+  const int incl = wave_incl_scan(nb);
+  const int eincl = wave_incl_scan(unused);
+  const int total = __shfl(incl, 63);
+  // Dispatch-order index: kv head unit fastest, then piece.
+  const unsigned gid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  Piece pc;
+  pc.unit = (int)(gid % (unsigned)units);
+  const int i = (int)(gid / (unsigned)units);
+  if (i < total) {
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(
+        lane < B && i >= incl - nb && i < incl);
+    const int bb = __builtin_ctzll(m);
+    pc.b = bb;
+    const int lb = __shfl(len, bb);
+    const int npc = __shfl(nb, bb);
+    const int p = i - (__shfl(incl, bb) - npc);
+    const int len_p = ((lb + npc - 1) / npc + 15) & ~15;   // equal pieces
+    pc.slot = p;
+    pc.lo = p * len_p;
+    pc.hi = min(lb, pc.lo + len_p);
+  } else {
+    const int k = i - total;
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(
+        lane < B && k >= eincl - unused && k < eincl);
+    const int bb = __builtin_ctzll(m);
+    pc.b = bb;
+    pc.slot = __shfl(nb, bb) + (k - (__shfl(eincl, bb) - __shfl(unused, bb)));
+    pc.lo = pc.hi = 0;
+  }
+  return pc;
+}
+
 // F8: the cache holds 8-bit E4M3 codes with one scale per kv head for K and
 // one for V. A lane then reads 16 bytes = 16 dims of a key row per request
 // (dims 16(j + 4c)..+15) and 8 bytes = 8 dims of a value row, converts them
@@ -251,7 +355,7 @@ constexpr float kRefSlack = 8.f;  // exponent-reference slack, base 2
 // normalisation. The QK contraction order is free, so Q's fragments simply
 // follow the same dim order.
 template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8,
-          bool NT = true>
+          bool BAL = false, bool NT = true>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
@@ -272,13 +376,24 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, j = lane >> 4;
-  const int s = blockIdx.z, b = blockIdx.y;
-  const int kvh = blockIdx.x / nhg;
-  const int hg = blockIdx.x - kvh * nhg;
+  int unit = blockIdx.x;                    // kv head x head group
+  int s = blockIdx.z, b = blockIdx.y;       // output slot, sequence
+  int lo = s * P;
+  int hi_max = min(lo + P, L);              // split end for a full history
+  if constexpr (BAL) {
+    // Length-aware pieces (batched calls): every wave derives the same plan
+    // from the lengths; the workgroup takes the piece of its dispatch rank.
+    const Piece pc = balanced_piece(a, L, P, Hkv * nhg);
+    unit = pc.unit;
+    b = pc.b;
+    s = pc.slot;
+    lo = pc.lo;
+    hi_max = pc.hi;
+  }
+  const int kvh = unit / nhg;
+  const int hg = unit - kvh * nhg;
   const int h0 = kvh * G + hg * GM;
   const int nh = min(GM, G - hg * GM);
-  const int lo = s * P;
-  const int hi_max = min(lo + P, L);        // split end for a full history
   if (__builtin_expect(lo >= hi_max, 0)) {  // no sequence reaches this split
     write_empty<D>(a, b, h0, nh, s);
     return;
@@ -365,7 +480,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   // lengths vary, where many splits are empty or short) the length comes
   // first and nothing past it is read.
   int hi = hi_max;
-  if (!SPEC) {
+  if (!SPEC && !BAL) {
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > L ? L : len);
     hi = min(lo + P, len);
@@ -689,23 +804,24 @@ MfmaShape mfma_shape(int P, bool f8) {
 // request; they fit the 14 kernel-argument dwords gfx950 preloads into SGPRs
 // at dispatch, so no wave waits on an argument load before its first
 // request (such loads queue behind other waves' K/V traffic).
-template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8>
+template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8,
+          bool BAL = false>
 void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_mfma<D, NW, U, GM, PAGED, SPEC, F8>), grid,
+  hipLaunchKernelGGL((split_mfma<D, NW, U, GM, PAGED, SPEC, F8, BAL>), grid,
                      dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
                      a.nhg, a.G, a.block_table, a.bs, a);
 }
 
-template <int D, bool PAGED, int GM, bool SPEC, bool F8>
+template <int D, bool PAGED, int GM, bool SPEC, bool F8, bool BAL = false>
 void launch_mfma_spec(dim3 grid, MfmaShape m, const SplitArgs& a,
                       hipStream_t st) {
   if (m.nw == 8)
-    launch_one<D, 8, 1, GM, PAGED, SPEC, F8>(grid, a, st);
+    launch_one<D, 8, 1, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
   else if (!F8 && m.u == 2)
-    launch_one<D, 4, F8 ? 1 : 2, GM, PAGED, SPEC, F8>(grid, a, st);
+    launch_one<D, 4, F8 ? 1 : 2, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
   else
-    launch_one<D, 4, 1, GM, PAGED, SPEC, F8>(grid, a, st);
+    launch_one<D, 4, 1, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
 }
 
 // Speculative first loads pay off for a single sequence (its splits are all
@@ -715,6 +831,8 @@ template <int D, bool PAGED, int GM, bool F8>
 void launch_mfma_gm(dim3 grid, MfmaShape m, const SplitArgs& a, hipStream_t st) {
   if (a.B == 1)
     launch_mfma_spec<D, PAGED, GM, true, F8>(grid, m, a, st);
+  else if (a.bal_target > 0 && a.B <= 64)       // lane = sequence
+    launch_mfma_spec<D, PAGED, GM, false, F8, true>(grid, m, a, st);
   else
     launch_mfma_spec<D, PAGED, GM, false, F8>(grid, m, a, st);
 }
@@ -723,6 +841,9 @@ template <int D, bool PAGED, bool F8>
 void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const int gm = s.G <= 8 ? 8 : 16;
   a.nhg = (s.G + gm - 1) / gm;
+  // About two workgroups per CU in total, spread over the kv head units.
+  a.bal_target = a.balance_cus > 0 && a.S > 1
+                     ? max(1, 2 * a.balance_cus / (s.Hkv * a.nhg)) : 0;
   const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
   const MfmaShape m = mfma_shape(a.P, F8);
   if (gm == 8)

@@ -417,3 +417,21 @@ def test_large_ragged_batch():
     for S in (1, 3):
         out, lse = gpu_attention(w, S, t)
         assert_parity(f"bigbatch/S={S}", "bf16", out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("batch", [63, 64, 65])
+def test_length_aware_pieces_at_the_batch_limit(batch):
+    """Batched calls cut sequences by their lengths when the batch fits one
+    lane of a wave (<= 64 sequences) and fall back to
+    uniform splits above; empty sequences and single-token ones included."""
+    g = torch.Generator().manual_seed(93)
+    lens = torch.randint(0, 700, (batch,), generator=g)
+    lens[:3] = torch.tensor([0, 1, 699])
+    w = workloads.make("bal", seed=93, batch=batch, num_q_heads=4,
+                       num_kv_heads=1, head_dim=128, max_seq_len=700,
+                       seq_lens=lens.tolist(), paged=True, poison_tail=True)
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    for S in (2, 5, 44):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"bal{batch}/S={S}", "bf16", out, lse, ref_out, ref_lse)
