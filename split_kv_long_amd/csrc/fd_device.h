@@ -57,6 +57,28 @@ __device__ __forceinline__ float sum_x32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Whole-wave max / sum on the VALU: DPP inside each 16-lane row (swap
+// neighbours, swap pairs, rotate by 4, rotate by 8), then the row exchanges.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL,
+                                                    0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  return max_x32(max_x16(v));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x128>(v);
+  return sum_x32(sum_x16(v));
+}
+
 __device__ __forceinline__ int clamp_len(const SplitArgs& a, int b) {
   int n = a.seq_lens[b];
   n = n < 0 ? 0 : n;

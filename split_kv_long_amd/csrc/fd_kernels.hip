@@ -140,15 +140,11 @@ __global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
     __syncthreads();
     for (int g = wave; g < nh; g += kGenThreads / 64) {
       const float x = lane < nt ? p_s[g][lane] : -INFINITY;
-      float mx = x;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mx = wave_max_f(x);
       const float mn = fmaxf(m_s[g], mx);
       const float e = lane < nt ? fexp2(x - mn) : 0.f;
       if (lane < TILE) p_s[g][lane] = e;
-      float sum = e;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      const float sum = wave_sum_f(e);
       if (lane == 0) {
         const float al = fexp2(m_s[g] - mn);
         l_s[g] = l_s[g] * al + sum;
