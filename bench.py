@@ -37,7 +37,8 @@ MALL_BYTES = 256 * 2 ** 20
 COUNTERS_FILE = os.path.join(ROOT, "profiles",
                              "split_mfma_long_gqa_64k_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "split_kv_long_amd", "csrc", f)
-                  for f in ("fd_kernels.hip", "fd_host.cpp")]
+                  for f in ("fd_kernels.hip", "fd_device.h", "fd_internal.h",
+                            "fd_host.cpp")]
 
 
 def parse_args():
