@@ -10,15 +10,21 @@
 // list), so one pass over K and V suffices.
 //
 // Kernels:
-//   split_mfma<D, NW>    bf16 K/V, head_dim 64/128. One workgroup per
-//                        (split, kv head, 16-head group, sequence); NW waves
-//                        share the split, each wave streaming 32-token
-//                        subtiles straight from HBM into registers, and the
-//                        GQA group's QK^T and PV tile products run on the
-//                        16x16x32 bf16 matrix cores.
+//   split_mfma<D, NW, U, GM, PAGED, SPEC, F8, BAL>
+//                        bf16 or 8-bit E4M3 K/V, head_dim 64/128. One
+//                        workgroup per (split, kv head x group of <= GM
+//                        query heads, sequence); NW waves share the split,
+//                        each streaming 32-token subtiles (U at a time)
+//                        straight from HBM into registers, and the GQA
+//                        group's QK^T and PV tile products run on the
+//                        16x16x32 bf16 matrix cores. SPEC: batch one, first
+//                        requests before the length is known. BAL: batched
+//                        calls, length-aware pieces instead of uniform
+//                        splits.
 //   split_f32<D>         fp32 caches: LDS-tiled, plain fp32 FMA, exact fp32
 //                        products.
 //   combine_kernel<D>    log-sum-exp reduction of the split partials.
+// The block-sparse kernels live in fd_sparse.hip.
 
 #include <hip/hip_runtime.h>
 #include <math.h>

@@ -435,3 +435,85 @@ def test_length_aware_pieces_at_the_batch_limit(batch):
     for S in (2, 5, 44):
         out, lse = gpu_attention(w, S, t)
         assert_parity(f"bal{batch}/S={S}", "bf16", out, lse, ref_out, ref_lse)
+
+
+# ------------------------------------------------- graphs and streams
+
+@pytest.mark.parametrize("name,over", [
+    ("long_gqa_64k", dict(max_seq_len=8192)),
+    ("ragged_paged", dict(batch=6, max_seq_len=5000, min_seq_len=1)),
+    ("long_gqa_64k_fp8", dict(max_seq_len=8192)),
+])
+def test_graph_replays_match_eager(name, over):
+    """The calls enqueue kernels only (no allocation, no memset), so they
+    can be captured in a graph: every replay, with eager work and
+    synchronisations in between, must reproduce the eager result bitwise."""
+    w = workloads.make(name, **over)
+    t = device_inputs(w)
+    S = max(2, fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len()))
+    eager_out, eager_lse = gpu_attention(w, S, t)
+    shape = shape_of(w)
+    out = torch.zeros(w.batch, w.num_q_heads, w.head_dim, device="cuda")
+    lse = torch.zeros(w.batch, w.num_q_heads, device="cuda")
+    ws = torch.empty(max(fb.fd_workspace_size(shape, S), 16),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        if w.cache_dtype == "fp8_e4m3":
+            fb.fd_decode_attn_fp8(shape, t["q"], t["k"], t["v"], t["ks"],
+                                  t["vs"], t["bt"], t["seq_lens"], S, ws, out,
+                                  lse)
+        else:
+            fb.fd_decode_attn(shape, t["q"], t["k"], t["v"], t["bt"],
+                              t["seq_lens"], S, ws, out, lse)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    print(f"[gpu] graph capture {name} S={S}", flush=True)
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            call()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(0xFF)                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().double().numpy(), eager_out), rep
+        assert np.array_equal(lse.cpu().double().numpy(), eager_lse), rep
+
+
+def test_concurrent_streams():
+    """Two calls with their own workspaces on two streams (default
+    priority) overlap and both match the oracle."""
+    ws_ = [workloads.make("long_gqa_64k", max_seq_len=4096),
+           workloads.make("ragged_paged", seed=94, batch=5, max_seq_len=3000,
+                          min_seq_len=1)]
+    refs = [oracle_attention(w) for w in ws_]
+    ts = [device_inputs(w) for w in ws_]
+    outs = []
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for w, t, st in zip(ws_, ts, streams):
+        shape = shape_of(w)
+        S = fb.fd_plan_splits(shape, num_cus(), w.sum_seq_len())
+        out = torch.empty(w.batch, w.num_q_heads, w.head_dim, device="cuda")
+        lse = torch.empty(w.batch, w.num_q_heads, device="cuda")
+        ws = torch.empty(max(fb.fd_workspace_size(shape, S), 16),
+                         dtype=torch.uint8, device="cuda")
+        st.wait_stream(torch.cuda.current_stream())
+        print(f"[gpu] stream call {w.name} S={S}", flush=True)
+        with torch.cuda.stream(st):
+            for _ in range(5):
+                fb.fd_decode_attn(shape, t["q"], t["k"], t["v"], t["bt"],
+                                  t["seq_lens"], S, ws, out, lse)
+        outs.append((out, lse))
+    torch.cuda.synchronize()
+    for w, (out, lse), (ro, rl) in zip(ws_, outs, refs):
+        assert_parity(f"stream-{w.name}", w.cache_dtype,
+                      out.cpu().double().numpy(), lse.cpu().double().numpy(),
+                      ro, rl)
