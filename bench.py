@@ -471,7 +471,7 @@ def sparse_run(args):
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+        print("bench.py runs on one GPU only; --gpus must be 1 "
               "(sequence- or head-sharded multi-GPU decode is not built)",
               file=sys.stderr)
         sys.exit(2)

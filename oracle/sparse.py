@@ -3,7 +3,7 @@
 invariants and brute force, not by values the pages print).
 
 The "Faster Than Flash" page (abstract) describes decoding that first scans
-a low-bit quantized copy of the keys to judge which blocks of the history
+a low-bit quantized copy of the keys to estimate which blocks of the history
 matter, keeps the blocks a "top-delta" rule admits (without global
 synchronization), and computes exact attention over the kept blocks only.
 The page defines neither the quantizer nor the rule; the readings taken here

@@ -2,7 +2,7 @@
 //
 // After the abstract of "Faster Than Flash: Exploiting Attention Sparsity
 // for Efficient Long-Context Decoding": a low-bit quantized copy of the keys
-// is scanned to judge which blocks of the history matter, a top-delta rule
+// is scanned to estimate which blocks of the history matter, a top-delta rule
 // keeps the blocks whose estimated best logit comes within delta of the
 // best one (decided inside each split, so no workgroup waits on another),
 // and exact attention runs over the kept blocks only. The partials then go
