@@ -28,17 +28,30 @@ def shape_for(q, k_cache, seq_lens, block_table=None, max_seq_len=None,
         L = max_seq_len if max_seq_len is not None else maxb * bs
     if max_seq_len is not None:
         L = max_seq_len
-    dt = {torch.bfloat16: "bf16", torch.float32: "f32"}[q.dtype]
+    if k_cache.dtype == torch.float8_e4m3fn:
+        if q.dtype != torch.bfloat16:
+            raise ValueError("an E4M3 cache takes a bf16 query")
+        dt = "fp8_e4m3"
+    else:
+        if k_cache.dtype != q.dtype or q.dtype not in (torch.bfloat16,
+                                                       torch.float32):
+            raise ValueError("q and the cache must both be bf16 or fp32 "
+                             f"(got {q.dtype} and {k_cache.dtype})")
+        dt = {torch.bfloat16: "bf16", torch.float32: "f32"}[q.dtype]
     return binding.make_shape(B, Hq, Hkv, D, L, dt, bs, maxb, nb, scale or 0.0)
 
 
 def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
                      num_splits: Optional[int] = None, scale=None,
-                     max_seq_len=None, return_lse: bool = False):
+                     max_seq_len=None, return_lse: bool = False,
+                     k_scale=None, v_scale=None):
     """out[b, h] = softmax attention of q[b, h] over the first seq_lens[b]
-    cached positions (fp32). Tensors must be on the current GPU."""
+    cached positions (fp32). Tensors must be on the current GPU. An E4M3
+    cache (torch.float8_e4m3fn) needs k_scale / v_scale (fp32 [Hkv])."""
     import torch
     from . import binding
+    if v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must match in dtype and shape")
     shape = shape_for(q, k_cache, seq_lens, block_table, max_seq_len, scale)
     if num_splits is None:
         cus = torch.cuda.get_device_properties(q.device).multi_processor_count
@@ -48,6 +61,13 @@ def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
     nbytes = binding.fd_workspace_size(shape, num_splits)
     ws = (torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
           if nbytes else None)
-    binding.fd_decode_attn(shape, q, k_cache, v_cache, block_table, seq_lens,
-                           num_splits, ws, out, lse)
+    if k_cache.dtype == torch.float8_e4m3fn:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an E4M3 cache needs k_scale and v_scale")
+        binding.fd_decode_attn_fp8(shape, q, k_cache, v_cache, k_scale,
+                                   v_scale, block_table, seq_lens,
+                                   num_splits, ws, out, lse)
+    else:
+        binding.fd_decode_attn(shape, q, k_cache, v_cache, block_table,
+                               seq_lens, num_splits, ws, out, lse)
     return (out, lse) if return_lse else out

@@ -296,3 +296,17 @@ def test_32bit_index_limits_are_enforced():
     # a bound whose splits fit is fine for sizing
     assert fb.fd_workspace_size(shp(max_seq_len=2 ** 31 - 16), 1) == 0
     assert fb.fd_workspace_size(shp(max_seq_len=2 ** 30), 3) > 0
+
+
+def test_wrapper_rejects_mismatched_dtypes():
+    import torch
+    import split_kv_long_amd as fd
+    q = torch.zeros(1, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 8, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fd.shape_for(q, k, torch.zeros(1, dtype=torch.int32))
+    k8 = torch.zeros(1, 1, 8, 64).to(torch.float8_e4m3fn)
+    s = fd.shape_for(q, k8, torch.zeros(1, dtype=torch.int32))
+    assert s.dtype == fb.FD_DTYPE_FP8_E4M3
+    with pytest.raises(ValueError):
+        fd.shape_for(q.float(), k8, torch.zeros(1, dtype=torch.int32))

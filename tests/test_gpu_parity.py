@@ -517,3 +517,16 @@ def test_concurrent_streams():
         assert_parity(f"stream-{w.name}", w.cache_dtype,
                       out.cpu().double().numpy(), lse.cpu().double().numpy(),
                       ro, rl)
+
+
+def test_convenience_wrapper_e4m3_cache():
+    import split_kv_long_amd as fd
+    w = workloads.make("long_gqa_64k_fp8", max_seq_len=5000)
+    t = device_inputs(w)
+    out, lse = fd.decode_attention(t["q"], t["k"], t["v"], t["seq_lens"],
+                                   return_lse=True, k_scale=t["ks"],
+                                   v_scale=t["vs"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_attention(w)
+    assert_parity("wrapper-fp8", "fp8_e4m3", out.cpu().double().numpy(),
+                  lse.cpu().double().numpy(), ref_out, ref_lse)
