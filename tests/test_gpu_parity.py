@@ -530,3 +530,18 @@ def test_convenience_wrapper_e4m3_cache():
     ref_out, ref_lse = oracle_attention(w)
     assert_parity("wrapper-fp8", "fp8_e4m3", out.cpu().double().numpy(),
                   lse.cpu().double().numpy(), ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("bs", [32, 256])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_larger_page_sizes(bs, kv):
+    """Pages of 32 and 256 tokens: splits are rounded to whole pages, and
+    16-token subtiles start inside a page."""
+    lens = [1, 31, 33, 255, 257, 1000, 0, 2047]
+    w = workloads.make("pages", seed=95, batch=len(lens), num_q_heads=16,
+                       num_kv_heads=2, head_dim=128, max_seq_len=2048,
+                       paged=True, block_size=bs, seq_lens=lens,
+                       poison_tail=True,
+                       kv_dtype=None if kv == "bf16" else kv)
+    for S in (1, 3, 8):
+        check(w, S)

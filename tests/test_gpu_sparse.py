@@ -236,3 +236,14 @@ def test_sparse_delta_zero_keeps_the_needles():
     out, lse, kept = check_sparse(w, 0.0, 4)
     for p in (5, 8192 // 3, 8192 // 2 + 7, 8191):
         assert kept[0, 0, p // 16] == 1 and kept[0, 1, p // 16] == 1
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_sparse_and_summary_with_larger_pages(bs):
+    lens = [4000, 1, 17, 2500]
+    w = workloads.make("sparse", seed=85, batch=len(lens), num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, max_seq_len=4000,
+                       paged=True, block_size=bs, seq_lens=lens,
+                       needles=[5, 1333, 3999], needle_logit=14.0,
+                       poison_tail=True)
+    check_sparse(w, 2.0, 3, expect_dropped=False)
