@@ -413,10 +413,10 @@ def sparse_run(args):
     nblk = -(-w.max_seq_len // 16)
     codes, scales = [], []
     for r in range(b.R):
-        c = torch.empty(tuple(w.k.shape[:-1]) + (D // 2,), dtype=torch.uint8,
-                        device=dev)
-        sc = torch.empty((w.k.shape[0], Hkv, w.block_size // 16) if w.paged
-                         else (w.batch, Hkv, nblk), device=dev)
+        nrec = ((w.k.shape[0], Hkv, w.block_size // 16) if w.paged
+                else (w.batch, Hkv, nblk))
+        c = torch.empty(nrec + (8 * D,), dtype=torch.uint8, device=dev)
+        sc = torch.empty(nrec, device=dev)
         fb.fd_build_key_summary(b.shape, b.ks[r], b.bt, b.lens, c, sc)
         codes.append(c)
         scales.append(sc)

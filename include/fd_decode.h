@@ -218,11 +218,16 @@ int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
  * scale = amax / 7, each one correctly rounded fp32 operation (0 when
  * amax = 0); code = rint(k * inv) (fp32 product, ties to even), in [-7, 7],
  * stored as 4-bit two's complement, dim 2m in the low nibble of byte m of
- * the row. Rows past a sequence's length get code 0.
+ * the row's head_dim / 2 bytes. Rows past a sequence's length get code 0.
+ * Each block's 16 rows form one record of 8 * head_dim bytes in which row n's
+ * piece p (its bytes p * head_dim/8 .. (p+1) * head_dim/8 - 1, p = 0..3)
+ * sits at byte offset head_dim/8 * (n + 16 p): the order in which the scan
+ * reads them, one contiguous request per wave.
  *
- *   codes   device uint8, the layout of k_cache with head_dim / 2 bytes per
- *           row: contiguous [batch, Hkv, max_seq_len, head_dim/2], paged
- *           [num_blocks, Hkv, block_size, head_dim/2]; 16-byte aligned
+ *   codes   device uint8 records, one per (16-token block, kv head):
+ *           contiguous [batch, Hkv, ceil(max_seq_len/16), 8 * head_dim],
+ *           paged [num_blocks, Hkv, block_size/16, 8 * head_dim] (the same
+ *           bytes as a [.., block_size, head_dim/2] pool); 16-byte aligned
  *   scales  device fp32: contiguous [batch, Hkv, ceil(max_seq_len/16)];
  *           paged [num_blocks, Hkv, block_size/16]; 4-byte aligned
  * Only blocks holding at least one attended token are written. bf16 keys

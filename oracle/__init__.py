@@ -46,8 +46,11 @@ from .attention import (  # noqa: F401
 )
 from .sparse import (  # noqa: F401
     quantize_block,
+    quantize_query,
+    log2_units,
     key_summary,
     pack_int4,
     unpack_int4,
+    records_to_rows,
     sparse_decode_attention,
 )

@@ -16,12 +16,20 @@ The page defines neither the quantizer nor the rule; the readings taken here
   float32; amax = 0 gives inv = scale = 0); every attended element gets the
   4-bit code rint(float32(k * inv)) (round half to even), which lies in
   [-7, 7]. Rows past the length get code 0.
-* estimate: for block j and query head h, est[j, h] = attention scale *
-  scale_j * max over the block's attended tokens i of sum_d q[h, d] *
-  code[i, d] -- the block's largest logit as the summary sees it.
+* query for the scan: per (sequence, query head), amax_q = max |q| (float32),
+  inv_q = float32(127 / amax_q), s_q = float32(amax_q / 127), and the 8-bit
+  query q8 = rint(float32(q * inv_q)) in [-127, 127] (amax_q = 0: all 0).
+* estimate: dot[i, h] = sum_d q8[h, d] * code[i, d], an exact integer; for
+  block j, dmax = the largest dot over the block's attended tokens, and, in
+  float32 with the multiplications in this order,
+  est[j, h] = ((float(dmax) * s_q) * scale_j) * scale_log2, with
+  scale_log2 = float32(scale * log2 e) -- the block's largest logit, in
+  base-2 units, as the summary sees it.
 * top-delta, per split (no cross-split synchronization): with M[h] the
-  largest est over the split's blocks, block j is kept when
-  est[j, h] >= M[h] - delta for at least one query head h of its kv head.
+  largest est over the split's blocks and delta2 = float32(delta * log2 e),
+  block j is kept when est[j, h] >= float32(M[h] - delta2) for at least one
+  query head h of its kv head (float32 comparison, so both implementations
+  take every decision identically).
 * result: exact softmax attention (as ``decode_attention``) over the tokens
   of every kept block; delta = +inf keeps every block and gives the dense
   result.
@@ -51,6 +59,24 @@ def quantize_block(rows_bf16_bits) -> Tuple[np.ndarray, np.float32]:
     scale = np.float32(amax / np.float32(7))
     codes = np.rint((x * inv).astype(np.float32)).astype(np.int64)
     return codes, scale
+
+
+def quantize_query(q_bf16_bits) -> Tuple[np.ndarray, np.float32]:
+    """One query head's bf16 bits [D] -> (int8-range codes [D], float32
+    scale), per the reading above."""
+    x = decode_values(q_bf16_bits, "bf16").astype(np.float32)
+    amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x.shape, dtype=np.int64), np.float32(0)
+    inv = np.float32(np.float32(127) / amax)
+    s = np.float32(amax / np.float32(127))
+    return np.rint((x * inv).astype(np.float32)).astype(np.int64), s
+
+
+def log2_units(x: float) -> np.float32:
+    """float32(x * log2 e) with the product taken in double precision (how
+    the library converts the logit scale and delta)."""
+    return np.float32(float(np.float32(x)) * 1.4426950408889634)
 
 
 def key_summary(k, seq_lens, block_table=None, block_size: int = 0):
@@ -95,6 +121,15 @@ def pack_int4(codes) -> np.ndarray:
     return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
+def records_to_rows(records, head_dim: int) -> np.ndarray:
+    """Summary records (uint8 [..., 8 * D]) -> packed rows [..., 16, D / 2]:
+    row n's piece p (D / 8 bytes) is stored at byte D / 8 * (n + 16 p)."""
+    r = np.asarray(records, dtype=np.uint8)
+    cb = head_dim // 8
+    x = r.reshape(r.shape[:-1] + (4, 16, cb))          # [.., piece, row, byte]
+    return np.swapaxes(x, -3, -2).reshape(r.shape[:-1] + (16, 4 * cb))
+
+
 def unpack_int4(packed) -> np.ndarray:
     p = np.asarray(packed, dtype=np.int64)
     lo, hi = p & 0xF, (p >> 4) & 0xF
@@ -119,14 +154,17 @@ def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
 
     q [B, Hq, D] bf16 bits; k, v bf16 bits (contiguous or paged);
     codes int (layout of k), scales as ``key_summary`` returns.
-    Returns out [B, Hq, D], lse [B, Hq], est [B, Hq, nblk] (NaN where no
-    block), kept [B, Hkv, nblk] (bool), with nblk = ceil(L / 16).
+    Returns out [B, Hq, D], lse [B, Hq], est [B, Hq, nblk] (float32 values
+    in base-2 units; NaN where no block), kept [B, Hkv, nblk] (bool), with
+    nblk = ceil(L / 16).
     """
     qf = decode_values(q, "bf16")
     B, Hq, D = qf.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     sc = scale if scale else 1.0 / math.sqrt(D)
+    sl2 = log2_units(sc)
+    d2 = log2_units(delta) if math.isfinite(delta) else np.float32(np.inf)
     P = split_length(max_seq_len, num_splits)
     nblk = -(-max(max_seq_len, 1) // BLOCK)
     out = np.zeros((B, Hq, D))
@@ -138,21 +176,30 @@ def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
         for kvh in range(Hkv):
             heads = slice(kvh * G, (kvh + 1) * G)
             # 1. estimates from the summary
+            qq = [quantize_query(q[b, h]) for h in range(kvh * G, (kvh + 1) * G)]
+            q8 = np.stack([x[0] for x in qq])              # [G, D] ints
+            sq = [x[1] for x in qq]
             for j in range(-(-n // BLOCK)):
                 lo, hi = j * BLOCK, min((j + 1) * BLOCK, n)
                 c = history_rows(codes, b, kvh, lo, hi, block_table,
-                                 block_size).astype(np.float64)
-                s = block_scale(scales, b, kvh, j, block_table, block_size)
-                est[b, heads, j] = sc * s * (qf[b, heads] @ c.T).max(axis=1)
+                                 block_size).astype(np.int64)
+                s = np.float32(block_scale(scales, b, kvh, j, block_table,
+                                           block_size))
+                dmax = (q8 @ c.T).max(axis=1)              # exact integers
+                for g in range(G):
+                    e = np.float32(np.float32(dmax[g]) * sq[g])
+                    e = np.float32(e * s)
+                    est[b, kvh * G + g, j] = np.float32(e * sl2)
             # 2./3. top-delta inside each split
             for s_ in range(num_splits):
                 j0, j1 = s_ * P // BLOCK, min((s_ + 1) * P, n)
                 j1 = -(-j1 // BLOCK)
                 if j1 <= j0:
                     continue
-                e = est[b, heads, j0:j1]
+                e = est[b, heads, j0:j1].astype(np.float32)
                 M = e.max(axis=1, keepdims=True)
-                kept[b, kvh, j0:j1] = (e >= M - delta).any(axis=0)
+                thr = (M - d2).astype(np.float32)
+                kept[b, kvh, j0:j1] = (e >= thr).any(axis=0)
             # 4. exact attention over the kept tokens
             toks = [t for t in range(n) if kept[b, kvh, t // BLOCK]]
             if not toks:

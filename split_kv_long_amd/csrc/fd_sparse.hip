@@ -12,7 +12,12 @@
 //   summary_kernel<D>   bf16 keys -> 4-bit codes (two per byte, even dim in
 //                       the low nibble) + one fp32 scale per 16-token block
 //                       and kv head: scale = amax / 7, code =
-//                       rint(k * (7 / amax)).
+//                       rint(k * (7 / amax)). A block's codes form one
+//                       16 * D/2-byte record, stored in the order the scan's
+//                       MFMA operands need: bytes D/8 * (n + 16 p) ..
+//                       + D/8 - 1 hold piece p (dims D/4 * p ..) of row n, so
+//                       every lane's request is contiguous with its
+//                       neighbours'.
 //   split_sparse<D, NW, GM, PAGED>
 //                       one workgroup per (split, kv head, sequence):
 //                       phase 1 scans the split's summary blocks (MFMA on the
@@ -21,6 +26,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -38,7 +44,8 @@ constexpr int kSumBlock = 16;   // tokens per summary block
 
 // One wave per (16-token block, kv head, sequence). Lane l takes row l / 4
 // of the block and the quarter l % 4 of its dims. Blocks with no attended
-// token are skipped; rows past the length get code 0.
+// token are skipped; rows past the length (all 16 rows of a record exist)
+// get code 0.
 template <int D>
 __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
   constexpr int QD = D / 4;                  // dims per lane
@@ -51,15 +58,22 @@ __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
   const int r = lane >> 2, part = lane & 3;
   const int t = t0 + r;
   const bool valid = t < len;
-  const bool exists = a.bs > 0 || t < a.L;   // contiguous rows stop at L
-  size_t row;                                // element offset of row t
+  // Block index: the record and scale slot of this (block, kv head).
+  size_t bi;
+  int page = 0, pb = 0;
   if (a.bs == 0) {
-    row = ((size_t)(b * a.Hkv + kvh) * a.L + t);
+    bi = (size_t)(b * a.Hkv + kvh) * a.nblk_row + blk;
   } else {
-    const int page = t / a.bs;
-    int pb = a.block_table[(size_t)b * a.max_blocks + page];
+    page = t0 / a.bs;
+    pb = a.block_table[(size_t)b * a.max_blocks + page];
     pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
-    row = ((size_t)pb * a.Hkv + kvh) * a.bs + (t - page * a.bs);
+    bi = ((size_t)pb * a.Hkv + kvh) * (a.bs / kSumBlock) +
+         (t0 - page * a.bs) / kSumBlock;
+  }
+  size_t row = 0;                            // element offset of row t in K
+  if (valid) {
+    row = a.bs == 0 ? ((size_t)(b * a.Hkv + kvh) * a.L + t)
+                    : ((size_t)pb * a.Hkv + kvh) * a.bs + (t - page * a.bs);
   }
   float x[QD];
   float amax = 0.f;
@@ -85,7 +99,7 @@ __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
   // Correctly rounded fp32 quotients (HIP's default division).
   const float inv = amax > 0.f ? 7.0f / amax : 0.f;
   const float scale = amax > 0.f ? amax / 7.0f : 0.f;
-  if (exists) {
+  {
     unsigned packed[QD / 8];
 #pragma unroll
     for (int wd = 0; wd < QD / 8; ++wd) {
@@ -97,47 +111,17 @@ __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
       }
       packed[wd] = v;
     }
-    uint8_t* cp = a.codes + row * (D / 2) + part * (QD / 2);
+    uint8_t* cp = a.codes + bi * (kSumBlock * D / 2) + (QD / 2) * (r + 16 * part);
     if (QD == 32)
       *reinterpret_cast<u32x4*>(cp) = u32x4{packed[0], packed[1], packed[2], packed[3]};
     else
       *reinterpret_cast<u32x2*>(cp) = u32x2{packed[0], packed[1]};
   }
-  if (lane == 0) {
-    size_t si;
-    if (a.bs == 0) {
-      si = (size_t)(b * a.Hkv + kvh) * a.nblk_row + blk;
-    } else {
-      const int page = t0 / a.bs;
-      int pb = a.block_table[(size_t)b * a.max_blocks + page];
-      pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
-      si = ((size_t)pb * a.Hkv + kvh) * (a.bs / kSumBlock) +
-           (t0 - page * a.bs) / kSumBlock;
-    }
-    a.scales[si] = scale;
-  }
+  if (lane == 0) a.scales[bi] = scale;
 }
 
 // ----------------------------------------------------------------------------
 // Sparse split kernel.
-
-// 4-bit codes -> bf16 operands holding 136 + code (exact). A dword of 8
-// nibbles (dims 2m in low nibbles) becomes 4 dwords of bf16 pairs: flipping
-// bit 3 of each nibble turns code s into s + 8 in [0, 15], and 0x4300 | m
-// is the bf16 value 128 + m. The offset 136 times the query's dim sum is
-// subtracted after the product.
-__device__ __forceinline__ u32x4 nib8_to_bf16(unsigned w) {
-  const unsigned y = w ^ 0x88888888u;
-  const unsigned lo = y & 0x0F0F0F0Fu;          // even dims, one per byte
-  const unsigned hi = (y >> 4) & 0x0F0F0F0Fu;   // odd dims
-  // byte k of lo / hi -> bf16 mantissas of dims 2k / 2k+1
-  const unsigned d0 = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u);
-  const unsigned d1 = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u);
-  const unsigned d2 = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u);
-  const unsigned d3 = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u);
-  return u32x4{d0 | 0x43004300u, d1 | 0x43004300u, d2 | 0x43004300u,
-               d3 | 0x43004300u};
-}
 
 constexpr int kMaxSparseBlocks = kMaxSparseSplit / kSumBlock;
 
@@ -204,19 +188,65 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   const uint16_t* qrow = Q + ((size_t)b * a.Hq + qh) * D;
 
   // ---- phase 1: scan the summary -----------------------------------------
+  // The query is rounded to 8 bits per head (q8 = rint(q * 127 / amax_q));
+  // the int8 matrix cores then give every token's sum_d q8 * code exactly,
+  // and the block estimate is ((float(max dot) * s_q) * scale_blk) *
+  // scale_log2, the same float32 operations in the same order as the
+  // reference, so every keep decision is reproduced exactly.
   {
     constexpr int SD = D / 4;                  // scan dims per lane group
-    bf16x8 qs[KC];
-    float qsum = 0.f;
+    constexpr int NG = SD / 8;                 // 8-dim groups per lane
+    constexpr int KM = D / 64;                 // int8 MFMA calls per tile
+    // Lane (n, j): head n's dims [SD j, SD j + SD). Codes arrive as nibbles
+    // (dim 8m + e in nibble e of dword m); after unpacking, a dword's 8
+    // values sit as dims (0, 2, 4, 6) then (1, 3, 5, 7), and the query
+    // bytes are laid out in that same order.
+    float qv[SD];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
+    for (int c = 0; c < SD / 8; ++c) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + SD * j + 8 * c);
-      qs[c] = as_bf16x8(v);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qsum += __uint_as_float(v[e] << 16) + __uint_as_float(v[e] & 0xffff0000u);
+      for (int e = 0; e < 4; ++e) {
+        qv[8 * c + 2 * e] = __uint_as_float(v[e] << 16);
+        qv[8 * c + 2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+      }
     }
-    qsum = sum_x32(sum_x16(qsum));             // head n's sum over all dims
+    float qmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < SD; ++i) qmax = fmaxf(qmax, fabsf(qv[i]));
+    qmax = max_x32(max_x16(qmax));             // head n's max |q|
+    // Correctly rounded fp32 quotients (HIP's default division).
+    const float inv_q = qmax > 0.f ? 127.0f / qmax : 0.f;
+    const float s_q = qmax > 0.f ? qmax / 127.0f : 0.f;
+    unsigned q8w[2 * NG];
+    int qsum8 = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      int qi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qi[e] = (int)__builtin_rintf(qv[8 * g + e] * inv_q);
+        qsum8 += qi[e];
+      }
+      q8w[2 * g] = (qi[0] & 0xFF) | ((qi[2] & 0xFF) << 8) |
+                   ((qi[4] & 0xFF) << 16) | ((unsigned)(qi[6] & 0xFF) << 24);
+      q8w[2 * g + 1] = (qi[1] & 0xFF) | ((qi[3] & 0xFF) << 8) |
+                       ((qi[5] & 0xFF) << 16) | ((unsigned)(qi[7] & 0xFF) << 24);
+    }
+    {
+      const auto r16 = __builtin_amdgcn_permlane16_swap(
+          (unsigned)qsum8, (unsigned)qsum8, false, false);
+      qsum8 = (int)(r16[0] + r16[1]);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(
+          (unsigned)qsum8, (unsigned)qsum8, false, false);
+      qsum8 = (int)(r32[0] + r32[1]);          // head n's sum of q8
+    }
+    i32x4 qb[KM];
+#pragma unroll
+    for (int c = 0; c < KM; ++c)
+      qb[c] = i32x4{(int)q8w[4 * c], (int)q8w[4 * c + 1], (int)q8w[4 * c + 2],
+                    (int)q8w[4 * c + 3]};
+    const int off = 8 * qsum8;                 // codes arrive as code + 8
     float wmax = -INFINITY;
     // A wave's blocks go CHUNK at a time: every code and scale request of a
     // chunk is issued before the first product, one memory round trip each.
@@ -231,25 +261,42 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         const int jl = min(jl0 + NW * u, nb - 1);   // clamped: inside the split
         const int t0 = lo + jl * kSumBlock;
         lastr[u] = min(kSumBlock, hi - t0) - 1;
-        const size_t rw = row_of(t0 + min(n, lastr[u]));
-        bscale[u] = sp.scales[scale_index(t0)];
-        cw[u] = *reinterpret_cast<const CT*>(sp.codes + rw * (D / 2) + CB * j);
+        const size_t bi = scale_index(t0);    // record = scale slot
+        bscale[u] = sp.scales[bi];
+        cw[u] = *reinterpret_cast<const CT*>(sp.codes + bi * (kSumBlock * D / 2) +
+                                             CB * lane);
       }
 #pragma unroll
       for (int u = 0; u < CHUNK; ++u) {
         const int jl = jl0 + NW * u;
         if (jl >= nb) break;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        i32x4 acc = i32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(nib8_to_bf16(cw[u][c])), qs[c], acc, 0, 0, 0);
-        float bm = -INFINITY;
+        for (int c = 0; c < KM; ++c) {
+          // nibble -> byte (code + 8): flip bit 3, split even/odd dims
+          const unsigned y0 = cw[u][2 * c] ^ 0x88888888u;
+          const unsigned y1 = cw[u][2 * c + 1] ^ 0x88888888u;
+          const i32x4 ca = i32x4{(int)(y0 & 0x0F0F0F0Fu),
+                                 (int)((y0 >> 4) & 0x0F0F0F0Fu),
+                                 (int)(y1 & 0x0F0F0F0Fu),
+                                 (int)((y1 >> 4) & 0x0F0F0F0Fu)};
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ca, qb[c], acc, 0, 0, 0);
+        }
+        int dm = INT_MIN;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * j + i <= lastr[u]) bm = fmaxf(bm, acc[i] - 136.f * qsum);
-        bm = max_x32(max_x16(bm));
-        const float e = bm * bscale[u] * a.scale_log2;   // base-2 logit units
+          if (4 * j + i <= lastr[u]) dm = max(dm, acc[i]);
+        {
+          const auto r16 = __builtin_amdgcn_permlane16_swap(
+              (unsigned)dm, (unsigned)dm, false, false);
+          dm = max((int)r16[0], (int)r16[1]);
+          const auto r32 = __builtin_amdgcn_permlane32_swap(
+              (unsigned)dm, (unsigned)dm, false, false);
+          dm = max((int)r32[0], (int)r32[1]);
+        }
+        float e = (float)(dm - off) * s_q;     // block max, reference order
+        e = e * bscale[u];
+        e = e * a.scale_log2;                  // base-2 logit units
         if (j == 0 && n < GM) est_s[jl][n] = e;
         wmax = fmaxf(wmax, e);
       }

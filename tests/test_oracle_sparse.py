@@ -59,6 +59,18 @@ def test_int4_packing_by_hand():
     assert np.array_equal(osp.unpack_int4(osp.pack_int4(pairs)), pairs)
 
 
+def test_summary_records_by_hand():
+    """Record bytes D/8 * (n + 16 p) .. hold piece p of row n."""
+    D = 64                                        # 8-byte pieces, 512 B
+    rec = np.arange(8 * D, dtype=np.int64) % 251
+    rows = osp.records_to_rows(rec.astype(np.uint8), D)
+    assert rows.shape == (16, D // 2)
+    for n in (0, 5, 15):
+        for p in range(4):
+            assert rows[n, 8 * p:8 * p + 8].tolist() == \
+                [(8 * (n + 16 * p) + i) % 251 for i in range(8)]
+
+
 def test_key_summary_paged_equals_contiguous():
     w = workloads.make("ragged_paged", seed=51, batch=3, num_q_heads=4,
                        num_kv_heads=2, head_dim=32, max_seq_len=100,
@@ -113,11 +125,13 @@ def check_one_block_per_split_is_dense(fn):
 
 
 def check_brute_force_keep(fn):
-    """Estimates by explicit loops and the keep rule written out per block."""
+    """Estimates by explicit loops (int8 query, integer dots, float32
+    products in the stated order) and the keep rule written out per block."""
     a, codes, scales = _case(62, B=1, Hq=4, Hkv=2, D=16, L=80, lens=(75,))
     q = oracle.decode_values(a["q"], "bf16")
-    sc = 1.0 / math.sqrt(16)
+    sl2 = np.float32(float(np.float32(1.0 / math.sqrt(16))) * 1.4426950408889634)
     for delta in (0.0, 0.3, 1.0):
+        d2 = np.float32(float(np.float32(delta)) * 1.4426950408889634)
         out, lse, est, kept = fn(a["q"], a["k"], a["v"], a["seq_lens"],
                                  codes, scales, delta=delta, num_splits=2,
                                  max_seq_len=80)
@@ -125,20 +139,45 @@ def check_brute_force_keep(fn):
         for kvh in range(2):
             e = {}
             for h in (2 * kvh, 2 * kvh + 1):
+                amax = max(abs(float(x)) for x in q[0, h])
+                inv = np.float32(np.float32(127) / np.float32(amax))
+                sq = np.float32(np.float32(amax) / np.float32(127))
+                q8 = [int(np.rint(np.float32(np.float32(x) * inv)))
+                      for x in q[0, h]]
+                assert max(abs(x) for x in q8) == 127
                 for j in range(5):
-                    best = -math.inf
+                    best = None
                     for t in range(16 * j, min(16 * j + 16, 75)):
-                        acc = 0.0
+                        acc = 0
                         for d in range(16):
-                            acc += q[0, h, d] * codes[0, kvh, t, d]
-                        best = max(best, acc)
-                    e[h, j] = sc * float(scales[0, kvh, j]) * best
-                    assert abs(est[0, h, j] - e[h, j]) < 1e-12
+                            acc += q8[d] * int(codes[0, kvh, t, d])
+                        best = acc if best is None else max(best, acc)
+                    v = np.float32(np.float32(best) * sq)
+                    v = np.float32(v * np.float32(scales[0, kvh, j]))
+                    e[h, j] = np.float32(v * sl2)
+                    assert est[0, h, j] == e[h, j]
             for blocks in ((0, 1, 2), (3, 4)):
                 for j in blocks:
-                    want = any(e[h, j] >= max(e[h, i] for i in blocks) - delta
-                               for h in (2 * kvh, 2 * kvh + 1))
+                    want = any(e[h, j] >= np.float32(
+                        max(e[h, i] for i in blocks) - d2)
+                        for h in (2 * kvh, 2 * kvh + 1))
                     assert kept[0, kvh, j] == want, (delta, kvh, j)
+
+
+def test_query_quantizer_nearest_integer_and_range():
+    rng = np.random.default_rng(3)
+    for trial in range(50):
+        x = rng.standard_normal(64) * 10 ** rng.uniform(-3, 3)
+        bits = _bf16(x)
+        xv = oracle.decode_values(bits, "bf16")
+        q8, s = osp.quantize_query(bits)
+        amax = np.abs(xv).max()
+        assert q8.min() >= -127 and q8.max() <= 127
+        assert np.all(np.abs(127.0 * xv / amax - q8) <= 0.5 + 1e-5)
+        assert abs(q8[np.abs(xv).argmax()]) == 127
+        assert abs(float(s) * 127 - amax) <= 1e-6 * amax
+    q8, s = osp.quantize_query(_bf16(np.zeros(8)))
+    assert not q8.any() and s == 0
 
 
 def check_masked_sdpa(fn):
@@ -213,14 +252,21 @@ def _mutant(kind):
             n = int(seq_lens[b])
             for kvh in range(Hkv):
                 heads = slice(kvh * G, (kvh + 1) * G)
+                qq = [osp.quantize_query(q[b, h])
+                      for h in range(kvh * G, (kvh + 1) * G)]
+                q8 = np.stack([x[0] for x in qq])
+                sl2 = osp.log2_units(sc)
                 for j in range(-(-n // 16)):
-                    c = codes[b, kvh, 16 * j:min(16 * j + 16, n)].astype(float)
-                    sj = 1.0 if kind == "no_block_scale" else float(
-                        scales[b, kvh, j])
-                    sc_all = qf[b, heads] @ c.T
-                    red = sc_all.mean(axis=1) if kind == "mean_not_max" \
-                        else sc_all.max(axis=1)
-                    est[b, heads, j] = sc * sj * red
+                    c = codes[b, kvh, 16 * j:min(16 * j + 16, n)].astype(np.int64)
+                    sj = np.float32(1.0) if kind == "no_block_scale" else \
+                        np.float32(scales[b, kvh, j])
+                    dots = q8 @ c.T
+                    red = dots.mean(axis=1) if kind == "mean_not_max" \
+                        else dots.max(axis=1)
+                    for g in range(G):
+                        e = np.float32(np.float32(red[g]) * qq[g][1])
+                        e = np.float32(e * sj)
+                        est[b, kvh * G + g, j] = np.float32(e * sl2)
                 for s_ in range(num_splits):
                     j0 = s_ * P // 16
                     j1 = -(-min((s_ + 1) * P, n) // 16)
@@ -228,11 +274,14 @@ def _mutant(kind):
                         j1 = max(j0, j1 - 1)
                     if j1 <= j0:
                         continue
-                    e = est[b, heads, j0:j1]
+                    e = est[b, heads, j0:j1].astype(np.float32)
                     M = e.max(axis=1, keepdims=True)
                     if kind == "global_threshold":
-                        M = np.nanmax(est[b, heads], axis=1, keepdims=True)
-                    ok = e >= M - delta
+                        M = np.nanmax(est[b, heads], axis=1,
+                                      keepdims=True).astype(np.float32)
+                    d2 = osp.log2_units(delta) if math.isfinite(delta) \
+                        else np.float32(np.inf)
+                    ok = e >= (M - d2).astype(np.float32)
                     kept[b, kvh, j0:j1] = (ok.all(axis=0) if kind == "all_heads"
                                            else ok.any(axis=0))
                 toks = [t for t in range(n) if kept[b, kvh, t // 16]]
