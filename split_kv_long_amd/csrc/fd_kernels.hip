@@ -299,23 +299,30 @@ __device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
   // Smallest T (multiple of 16, >= P) with sum ceil(len / T) <= target.
   // sum ceil(len / T) lies in [W / T, W / T + B'] (W tokens, B' non-empty
   // sequences), which brackets T; beyond L every sequence is one piece.
-  const int W = wave_sum(len);
+  // 64-bit token total (two 16-bit halves keep each wave sum in range);
+  // it only brackets the search, which checks every candidate exactly.
+  const long long W = ((long long)wave_sum(len >> 16) << 16) +
+                      wave_sum(len & 0xFFFF);
   const int Bn = wave_sum(len > 0 ? 1 : 0);
   const int tgt = a.bal_target;
-  const int lmax = max(P, (L + 15) & ~15);
-  int tlo = max(P, min(lmax, ((int)(((long long)W + tgt - 1) / tgt) + 15) & ~15));
-  int thi = tgt > Bn ? min(lmax, ((int)(((long long)W + (tgt - Bn) - 1) /
-                                       (tgt - Bn)) + 15) & ~15)
-                     : lmax;
+  const long long lmax = max((long long)P, ((long long)L + 15) & ~15LL);
+  auto round16 = [&](long long x) {
+    return min(lmax, (x + 15) & ~15LL);
+  };
+  long long tlo = max((long long)P, round16((W + tgt - 1) / tgt));
+  long long thi = tgt > Bn ? round16((W + (tgt - Bn) - 1) / (tgt - Bn)) : lmax;
   thi = max(thi, tlo);
+  auto pieces = [&](long long T) {          // ceil(len / T), no overflow
+    return len > 0 ? (int)(((long long)len + T - 1) / T) : 0;
+  };
   while (tlo < thi) {
-    const int T = max(tlo, ((tlo + thi) >> 1) & ~15);
-    const int cnt = wave_sum(len > 0 ? (len + T - 1) / T : 0);
+    const long long T = max(tlo, ((tlo + thi) >> 1) & ~15LL);
+    const int cnt = wave_sum(pieces(T));
     if (cnt <= a.bal_target) thi = T;
     else tlo = T + 16;
   }
-  const int T = tlo;
-  const int nb = len > 0 ? (len + T - 1) / T : 0;
+  const long long T = tlo;
+  const int nb = pieces(T);
   const int unused = lane < B ? S - nb : 0;
   const int incl = wave_incl_scan(nb);
   const int eincl = wave_incl_scan(unused);
@@ -333,10 +340,11 @@ __device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
     const int lb = __shfl(len, bb);
     const int npc = __shfl(nb, bb);
     const int p = i - (__shfl(incl, bb) - npc);
-    const int len_p = ((lb + npc - 1) / npc + 15) & ~15;   // equal pieces
+    const long long len_p =                     // equal pieces
+        (((long long)lb + npc - 1) / npc + 15) & ~15LL;
     pc.slot = p;
-    pc.lo = p * len_p;
-    pc.hi = min(lb, pc.lo + len_p);
+    pc.lo = (int)min((long long)lb, p * len_p);
+    pc.hi = (int)min((long long)lb, p * len_p + len_p);
   } else {
     const int k = i - total;
     const unsigned long long m = __builtin_amdgcn_ballot_w64(
