@@ -260,6 +260,11 @@ def cpu_baseline(w, target_s):
                 host_cpu_count=os.cpu_count())
 
 
+def workloads_compare_splits(name):
+    import workloads
+    return workloads.SPECS.get(name, {}).get("compare_splits")
+
+
 def run_one(args, name, steps, warmup, with_cpu):
     import torch
     b = Bench(name, args.splits if name == args.workload else 0, steps,
@@ -331,6 +336,18 @@ def run_one(args, name, steps, warmup, with_cpu):
             "timing": split_timing,
         },
     }
+    # The workload recipes that name split counts to compare (the tiny MHA
+    # case, the short-history batch) get the call time at each of them.
+    cmp = workloads_compare_splits(name)
+    if cmp:
+        res = {}
+        for S in sorted(set(cmp) | {b.S}):
+            b2 = Bench(name, S, steps, None)
+            ms2, _ = b2.time_graph(b2.step, steps, warmup)
+            res[str(S)] = round(ms2 * 1e3 / steps, 3)
+            del b2
+        rec["split_comparison_us_per_call"] = res
+        rec["split_comparison_planned"] = b.S
     if args.copy_probe and name == args.workload:
         rec["copy_probe"] = copy_probe(torch)
     if with_cpu:

@@ -32,7 +32,8 @@ FP8_MAX = 448.0   # largest finite E4M3 magnitude
 SPECS = {
     "tiny_mha": dict(
         wid=1, batch=1, num_q_heads=8, num_kv_heads=8, head_dim=64,
-        max_seq_len=512, dtype=F32, scale=1.0 / 8.0, paged=False),
+        max_seq_len=512, dtype=F32, scale=1.0 / 8.0, paged=False,
+        compare_splits=[1, 4]),
     "long_gqa_64k": dict(
         wid=2, batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
         max_seq_len=65536, dtype=BF16, scale=None, paged=False),
@@ -60,7 +61,8 @@ SPECS = {
         haystack_gain=0.3, needle_block_every=512, needle_block_logit=6.0),
     "short_batch": dict(
         wid=5, batch=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
-        max_seq_len=1024, dtype=BF16, scale=None, paged=False),
+        max_seq_len=1024, dtype=BF16, scale=None, paged=False,
+        compare_splits=[1, 2, 8]),
     # The ragged batch's lengths in a contiguous [B, Hkv, L, D] cache, to
     # separate paging cost from ragged-length imbalance when measuring.
     "ragged_contig": dict(
