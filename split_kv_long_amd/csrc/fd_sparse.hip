@@ -20,8 +20,9 @@
 //                       neighbours'.
 //   split_sparse<D, NW, GM, PAGED>
 //                       one workgroup per (split, kv head, sequence):
-//                       phase 1 scans the split's summary blocks (MFMA on the
-//                       codes), phase 2 keeps blocks per top-delta, phase 3
+//                       phase 1 scans the split's summary blocks (8-bit
+//                       query x 4-bit codes, exact, on the int8 matrix
+//                       cores), phase 2 keeps blocks per top-delta, phase 3
 //                       runs exact bf16 attention over the kept blocks.
 
 #include <hip/hip_runtime.h>
@@ -127,9 +128,11 @@ constexpr int kMaxSparseBlocks = kMaxSparseSplit / kSumBlock;
 
 // Lane layout as in the dense MFMA kernel (lane l: n = l % 16, j = l / 16;
 // S^T = K * Q^T so a lane holds one head n and tokens 4j..4j+3 of a 16-token
-// tile). Scan operand order: lane group j covers the code dims
-// [32j, 32j + 32) at D = 128 ([16j, 16j + 16) at D = 64), 8 per MFMA call;
-// the query fragments follow the same order.
+// tile). Scan: lane group j covers the code dims [32j, 32j + 32) at
+// D = 128 ([16j, 16j + 16) at D = 64), 64 dims per int8 MFMA call; the
+// query bytes of each lane follow the order its code bytes arrive in, and
+// since every (lane group, byte) pair names one k-slot of the product for
+// both operands alike, the sum runs over every dim exactly once.
 template <int D, int NW, int GM, bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void split_sparse(SplitArgs a, SparseArgs sp) {
