@@ -364,10 +364,18 @@ __device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
 // scale is folded into the logit scale and the value scale into the final
 // normalisation. The QK contraction order is free, so Q's fragments simply
 // follow the same dim order.
+// Waves per SIMD the register allocation targets: two where a wave holds
+// two subtiles of registers (U = 2, or the reissue schedule below), else
+// three.
+constexpr int split_waves_per_simd(int NW, int U, bool f8) {
+  return (U >= 2 || (U == 1 && NW == 8 && !f8)) ? 2 : 3;
+}
+
 template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8,
           bool BAL = false, bool NT = true>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(NW, U, F8))))
+void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
     const int32_t* __restrict__ bt, int bs, SplitArgs a) {
@@ -441,8 +449,9 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   };
 
   // Requests the subtile starting at t0 with every row clamped below `end`.
+  // `part` selects the key requests (1), the value requests (2) or both.
   auto load_subtile = [&](int t0, int end, u32x4 (&kr)[2][KL],
-                          VT (&vr)[8]) {
+                          VT (&vr)[8], int part) {
     const int last0 = min(15, end - 1 - t0);
     const int last1 = end - 1 - (t0 + 16);
     const KT* K0 = K + group_base(t0);
@@ -465,22 +474,26 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     constexpr int KJ = F8 ? 16 : 8, KS = F8 ? 64 : 32;
     const unsigned r0 = (unsigned)(min(n, last0) * D + KJ * j);
     const unsigned r1 = (unsigned)(min(n, cap1) * D + KJ * j);
+    if (part & 1) {
 #pragma unroll
-    for (int c = 0; c < KL; ++c) {
-      kr[0][c] = ld16<NT>(K0 + r0 + KS * c);
-      kr[1][c] = ld16<NT>(K1 + r1 + KS * c);
+      for (int c = 0; c < KL; ++c) {
+        kr[0][c] = ld16<NT>(K0 + r0 + KS * c);
+        kr[1][c] = ld16<NT>(K1 + r1 + KS * c);
+      }
     }
     const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
+    if (part & 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const unsigned v0 = (unsigned)(min(4 * j + e, last0) * D + vcol);
-      const unsigned v1 = (unsigned)(min(4 * j + e, cap1) * D + vcol);
-      if constexpr (F8) {
-        vr[e] = ld8<NT>(V0 + v0);
-        vr[4 + e] = ld8<NT>(V1 + v1);
-      } else {
-        vr[e] = ld16<NT>(V0 + v0);
-        vr[4 + e] = ld16<NT>(V1 + v1);
+      for (int e = 0; e < 4; ++e) {
+        const unsigned v0 = (unsigned)(min(4 * j + e, last0) * D + vcol);
+        const unsigned v1 = (unsigned)(min(4 * j + e, cap1) * D + vcol);
+        if constexpr (F8) {
+          vr[e] = ld8<NT>(V0 + v0);
+          vr[4 + e] = ld8<NT>(V1 + v1);
+        } else {
+          vr[e] = ld16<NT>(V0 + v0);
+          vr[4 + e] = ld16<NT>(V1 + v1);
+        }
       }
     }
   };
@@ -504,7 +517,8 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   VT vp[U][8];
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    load_subtile(min(t_first + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u]);
+    load_subtile(min(t_first + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u],
+                 3);
 
   // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
   // scores are computed and never used.
@@ -542,6 +556,15 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
   // holds both subtiles' operands across them (lower occupancy): straight
   // line code instead.
   constexpr bool kSkip = U == 1;
+  // Eight waves with one bf16 subtile each: a wave reissues as soon as a
+  // subtile lands. The next subtile's keys are requested once the current
+  // keys are in registers, its values once the current values are, each
+  // before the current data is used, so a wave's compute never delays its
+  // next request (two subtiles of registers; two waves per SIMD). Issuing
+  // the next subtile earlier, before the current one lands, measured
+  // slower, and so did this schedule for E4M3 subtiles (half the bytes per
+  // request round, plus the conversions).
+  constexpr bool kPipe = U == 1 && NW == 8 && !F8;
 
   // The k-vector of QK call c for token group tg (bf16 operands).
   auto k_operand = [&](const u32x4 (&kr)[2][KL], int tg, int c) -> bf16x8 {
@@ -555,8 +578,9 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
     }
   };
 
+  // `after_scores` runs between the softmax step and the PV products.
   auto compute_subtile = [&](int t0, const u32x4 (&kr)[2][KL],
-                             const VT (&vraw)[8]) {
+                             const VT (&vraw)[8], auto&& after_scores) {
     f32x4 sacc[2];
 #pragma unroll
     for (int tg = 0; tg < 2; ++tg) {
@@ -618,6 +642,7 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
 #pragma unroll
       for (int cc = 0; cc < NV; ++cc) o[cc] *= alpha;
     }
+    after_scores();
     u32x4 vr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -651,17 +676,54 @@ __attribute__((amdgpu_waves_per_eu(U >= 2 ? 2 : 3))) void split_mfma(
         if (t >= hi) vp[u][e] = VT{};
       }
     }
-    compute_subtile(t0, kp[u], vp[u]);
   }
-  for (int t0 = t_first + 32 * NW * U; t0 < hi; t0 += 32 * NW * U) {
+  if constexpr (kPipe) {
+    // Two register sets, used in turn. An empty asm statement that takes a
+    // subtile's registers as inputs makes the compiler wait for exactly
+    // those loads there; the scheduling barriers keep the next requests
+    // between that wait and the first use of the current data.
+    u32x4 kq[2][KL];
+    VT vq[8];
+    auto step = [&](int tc, const u32x4 (&kc)[2][KL], const VT (&vc)[8],
+                    u32x4 (&kn)[2][KL], VT (&vn)[8]) -> bool {
+      const int tn = tc + 32 * NW;
+      const bool more = tn < hi;
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+        for (int c = 0; c < KL; ++c) asm volatile("" ::"v"(kc[tg][c]));
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_subtile(tn, hi, kn, vn, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_subtile(tc, kc, vc, [&] {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(vc[e]));
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_subtile(tn, hi, kn, vn, 2);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      return more;
+    };
+    for (int t0 = t_first;; t0 += 64 * NW) {
+      if (!step(t0, kp[0], vp[0], kq, vq)) break;
+      if (!step(t0 + 32 * NW, kq, vq, kp[0], vp[0])) break;
+    }
+  } else {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      load_subtile(min(t0 + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u]);
-    // All of the block's requests go out before its first use.
-    __builtin_amdgcn_sched_barrier(0);
+      compute_subtile(t_first + 32 * NW * u, kp[u], vp[u], [] {});
+    for (int t0 = t_first + 32 * NW * U; t0 < hi; t0 += 32 * NW * U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t0 + 32 * NW * u < hi) compute_subtile(t0 + 32 * NW * u, kp[u], vp[u]);
+      for (int u = 0; u < U; ++u)
+        load_subtile(min(t0 + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u],
+                     3);
+      // All of the block's requests go out before its first use.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t0 + 32 * NW * u < hi)
+          compute_subtile(t0 + 32 * NW * u, kp[u], vp[u], [] {});
+    }
   }
 
   // Per-head sum over the 4 lane groups; then park (O, m, l) in LDS.
