@@ -638,6 +638,13 @@ void split_mfma(
       pl[e] = (__bf16)(p - (float)hb);
     }
     l_run = l_run * alpha + psum;
+    if constexpr (kPipe) {
+      // Pin the exponentials here, ahead of the value wait: left alone the
+      // compiler sinks them next to their only use, the PV products, which
+      // puts them behind the arrival of the wave's last subtile.
+      asm volatile("" ::"v"(__builtin_bit_cast(u32x4, ph)),
+                   "v"(__builtin_bit_cast(u32x4, pl)));
+    }
     if (!kSkip || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
       for (int cc = 0; cc < NV; ++cc) o[cc] *= alpha;
