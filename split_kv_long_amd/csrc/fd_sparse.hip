@@ -142,7 +142,10 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   constexpr int CB = D / 8;                    // code bytes per lane per row
   __shared__ float est_s[kMaxSparseBlocks][GM];
   __shared__ float wmax_s[NW][GM];
-  __shared__ uint8_t keep_s[kMaxSparseBlocks];
+  __shared__ float thr_s[GM];                  // per-head keep threshold
+  __shared__ int cnt_s[NW];                    // kept blocks per wave slice
+  __shared__ int16_t list_s[kMaxSparseBlocks]; // kept blocks, ascending
+  static_assert(NW * 64 >= kMaxSparseBlocks, "one block per thread");
   __shared__ float mo[NW][GM][DP];
   __shared__ float mm[NW][GM], ml[NW][GM];
 
@@ -222,34 +225,23 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
     const float inv_q = qmax > 0.f ? 127.0f / qmax : 0.f;
     const float s_q = qmax > 0.f ? qmax / 127.0f : 0.f;
     unsigned q8w[2 * NG];
-    int qsum8 = 0;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       int qi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         qi[e] = (int)__builtin_rintf(qv[8 * g + e] * inv_q);
-        qsum8 += qi[e];
       }
       q8w[2 * g] = (qi[0] & 0xFF) | ((qi[2] & 0xFF) << 8) |
                    ((qi[4] & 0xFF) << 16) | ((unsigned)(qi[6] & 0xFF) << 24);
       q8w[2 * g + 1] = (qi[1] & 0xFF) | ((qi[3] & 0xFF) << 8) |
                        ((qi[5] & 0xFF) << 16) | ((unsigned)(qi[7] & 0xFF) << 24);
     }
-    {
-      const auto r16 = __builtin_amdgcn_permlane16_swap(
-          (unsigned)qsum8, (unsigned)qsum8, false, false);
-      qsum8 = (int)(r16[0] + r16[1]);
-      const auto r32 = __builtin_amdgcn_permlane32_swap(
-          (unsigned)qsum8, (unsigned)qsum8, false, false);
-      qsum8 = (int)(r32[0] + r32[1]);          // head n's sum of q8
-    }
     i32x4 qb[KM];
 #pragma unroll
     for (int c = 0; c < KM; ++c)
       qb[c] = i32x4{(int)q8w[4 * c], (int)q8w[4 * c + 1], (int)q8w[4 * c + 2],
                     (int)q8w[4 * c + 3]};
-    const int off = 8 * qsum8;                 // codes arrive as code + 8
     float wmax = -INFINITY;
     // A wave's blocks go CHUNK at a time: every code and scale request of a
     // chunk is issued before the first product, one memory round trip each.
@@ -273,22 +265,29 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
       for (int u = 0; u < CHUNK; ++u) {
         const int jl = jl0 + NW * u;
         if (jl >= nb) break;
+        // A 4-bit two's complement code moved into the high nibble of a
+        // byte (low nibble zero) is the signed byte 16 * code, so the
+        // products are 16 * sum_d q8 * code with no offset to remove:
+        // even dims from the low nibbles shifted up, odd dims masked.
         i32x4 acc = i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < KM; ++c) {
-          // nibble -> byte (code + 8): flip bit 3, split even/odd dims
-          const unsigned y0 = cw[u][2 * c] ^ 0x88888888u;
-          const unsigned y1 = cw[u][2 * c + 1] ^ 0x88888888u;
-          const i32x4 ca = i32x4{(int)(y0 & 0x0F0F0F0Fu),
-                                 (int)((y0 >> 4) & 0x0F0F0F0Fu),
-                                 (int)(y1 & 0x0F0F0F0Fu),
-                                 (int)((y1 >> 4) & 0x0F0F0F0Fu)};
+          const unsigned x0 = cw[u][2 * c], x1 = cw[u][2 * c + 1];
+          const i32x4 ca = i32x4{(int)((x0 << 4) & 0xF0F0F0F0u),
+                                 (int)(x0 & 0xF0F0F0F0u),
+                                 (int)((x1 << 4) & 0xF0F0F0F0u),
+                                 (int)(x1 & 0xF0F0F0F0u)};
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ca, qb[c], acc, 0, 0, 0);
         }
-        int dm = INT_MIN;
+        int dm;
+        if (lastr[u] == kSumBlock - 1) {      // full block (wave-uniform)
+          dm = max(max(acc[0], acc[1]), max(acc[2], acc[3]));
+        } else {
+          dm = INT_MIN;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * j + i <= lastr[u]) dm = max(dm, acc[i]);
+          for (int i = 0; i < 4; ++i)
+            if (4 * j + i <= lastr[u]) dm = max(dm, acc[i]);
+        }
         {
           const auto r16 = __builtin_amdgcn_permlane16_swap(
               (unsigned)dm, (unsigned)dm, false, false);
@@ -297,7 +296,7 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
               (unsigned)dm, (unsigned)dm, false, false);
           dm = max((int)r32[0], (int)r32[1]);
         }
-        float e = (float)(dm - off) * s_q;     // block max, reference order
+        float e = (float)(dm >> 4) * s_q;      // block max, reference order
         e = e * bscale[u];
         e = e * a.scale_log2;                  // base-2 logit units
         if (j == 0 && n < GM) est_s[jl][n] = e;
@@ -309,20 +308,42 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   __syncthreads();
 
   // ---- phase 2: top-delta inside the split --------------------------------
-  {
-    float M = wmax_s[0][n < GM ? n : 0];
+  // Thread t decides block t (a split has at most NW * 64 blocks) and the
+  // kept blocks are compacted, in ascending order, into list_s.
+  if (threadIdx.x < GM) {
+    const int h = threadIdx.x;
+    float M = wmax_s[0][h];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, wmax_s[ww][n < GM ? n : 0]);
-    for (int jl = w; jl < nb; jl += NW) {
-      const bool mine = j == 0 && n < nh && est_s[jl][n] >= M - sp.delta_log2;
-      const bool keep = __builtin_amdgcn_ballot_w64(mine) != 0;
-      if (lane == 0) {
-        keep_s[jl] = keep ? 1 : 0;
-        if (sp.kept_out)
-          sp.kept_out[(size_t)(b * Hkv + kvh) * sp.nblk_row + jg0 + jl] =
-              keep ? 1 : 0;
-      }
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, wmax_s[ww][h]);
+    thr_s[h] = M - sp.delta_log2;
+  }
+  __syncthreads();
+  int nkept;
+  {
+    const int jl = threadIdx.x;
+    bool keep = false;
+    if (jl < nb) {
+      for (int h = 0; h < nh; ++h) keep |= est_s[jl][h] >= thr_s[h];
+      if (sp.kept_out)
+        sp.kept_out[(size_t)(b * Hkv + kvh) * sp.nblk_row + jg0 + jl] =
+            keep ? 1 : 0;
     }
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(keep);
+    if (lane == 0) cnt_s[w] = __builtin_popcountll(mask);
+    __syncthreads();
+    int base = 0;
+    nkept = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const int c = cnt_s[ww];
+      base += ww < w ? c : 0;
+      nkept += c;
+    }
+    if (keep) {
+      const uint64_t below = mask & ((1ull << lane) - 1ull);
+      list_s[base + __builtin_popcountll(below)] = (int16_t)jl;
+    }
+    nkept = __builtin_amdgcn_readfirstlane(nkept);
   }
   __syncthreads();
 
@@ -336,17 +357,12 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  int jl = w;
-  auto next_kept = [&]() -> int {
-    while (jl < nb && !keep_s[jl]) jl += NW;
-    const int r = jl < nb ? jl : -1;
-    jl += NW;
-    return r;
-  };
-  for (;;) {
-    const int ja = next_kept();
-    if (ja < 0) break;
-    const int jb = next_kept();                // -1: second half masked
+  // Wave w takes kept blocks 2w, 2w + 1, then 2(w + NW), ... in pairs.
+  for (int k = 2 * w; k < nkept; k += 2 * NW) {
+    const int ja = __builtin_amdgcn_readfirstlane((int)list_s[k]);
+    const int jb = k + 1 < nkept                // -1: second half masked
+                       ? __builtin_amdgcn_readfirstlane((int)list_s[k + 1])
+                       : -1;
     const int ta = lo + ja * kSumBlock;
     const int tb = jb >= 0 ? lo + jb * kSumBlock : ta;
     const int lasta = min(kSumBlock, hi - ta) - 1;
