@@ -10,11 +10,11 @@
 // list), so one pass over K and V suffices.
 //
 // Kernels:
-//   split_mfma<D, NW, U, GM, PAGED, SPEC, F8, BAL>
+//   split_mfma<D, NW, GM, PAGED, SPEC, F8, BAL>
 //                        bf16 or 8-bit E4M3 K/V, head_dim 64/128. One
 //                        workgroup per (split, kv head x group of <= GM
 //                        query heads, sequence); NW waves share the split,
-//                        each streaming 32-token subtiles (U at a time)
+//                        each streaming 32-token subtiles one at a time
 //                        straight from HBM into registers, and the GQA
 //                        group's QK^T and PV tile products run on the
 //                        16x16x32 bf16 matrix cores. SPEC: batch one, first
@@ -357,6 +357,11 @@ __device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
   return pc;
 }
 
+// Waves per SIMD the register allocation targets: two for bf16, whose
+// waves hold two subtiles of registers (the reissue schedule below), three
+// for E4M3.
+constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
+
 // F8: the cache holds 8-bit E4M3 codes with one scale per kv head for K and
 // one for V. A lane then reads 16 bytes = 16 dims of a key row per request
 // (dims 16(j + 4c)..+15) and 8 bytes = 8 dims of a value row, converts them
@@ -364,17 +369,10 @@ __device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
 // scale is folded into the logit scale and the value scale into the final
 // normalisation. The QK contraction order is free, so Q's fragments simply
 // follow the same dim order.
-// Waves per SIMD the register allocation targets: two where a wave holds
-// two subtiles of registers (U = 2, or the reissue schedule below), else
-// three.
-constexpr int split_waves_per_simd(int NW, int U, bool f8) {
-  return (U >= 2 || (U == 1 && NW == 8 && !f8)) ? 2 : 3;
-}
-
-template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8,
-          bool BAL = false, bool NT = true>
+template <int D, int NW, int GM, bool PAGED, bool SPEC, bool F8,
+          bool BAL = false>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(NW, U, F8))))
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(F8))))
 void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
@@ -477,8 +475,8 @@ void split_mfma(
     if (part & 1) {
 #pragma unroll
       for (int c = 0; c < KL; ++c) {
-        kr[0][c] = ld16<NT>(K0 + r0 + KS * c);
-        kr[1][c] = ld16<NT>(K1 + r1 + KS * c);
+        kr[0][c] = ld16<true>(K0 + r0 + KS * c);
+        kr[1][c] = ld16<true>(K1 + r1 + KS * c);
       }
     }
     const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
@@ -488,17 +486,17 @@ void split_mfma(
         const unsigned v0 = (unsigned)(min(4 * j + e, last0) * D + vcol);
         const unsigned v1 = (unsigned)(min(4 * j + e, cap1) * D + vcol);
         if constexpr (F8) {
-          vr[e] = ld8<NT>(V0 + v0);
-          vr[4 + e] = ld8<NT>(V1 + v1);
+          vr[e] = ld8<true>(V0 + v0);
+          vr[4 + e] = ld8<true>(V1 + v1);
         } else {
-          vr[e] = ld16<NT>(V0 + v0);
-          vr[4 + e] = ld16<NT>(V1 + v1);
+          vr[e] = ld16<true>(V0 + v0);
+          vr[4 + e] = ld16<true>(V1 + v1);
         }
       }
     }
   };
 
-  // With SPEC the wave's first U subtiles go out before anything else,
+  // With SPEC the wave's first subtile goes out before anything else,
   // clamped to the split's full-history end; without it (batches whose
   // lengths vary, where many splits are empty or short) the length comes
   // first and nothing past it is read.
@@ -513,12 +511,9 @@ void split_mfma(
     }
   }
   const int t_first = lo + 32 * w;
-  u32x4 kp[U][2][KL];
-  VT vp[U][8];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-    load_subtile(min(t_first + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u],
-                 3);
+  u32x4 kp[2][KL];
+  VT vp[8];
+  load_subtile(min(t_first, (hi - 1) & ~15), hi, kp, vp, 3);
 
   // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
   // scores are computed and never used.
@@ -549,22 +544,18 @@ void split_mfma(
   for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // With one subtile in flight per wave the compute tail is on the critical
-  // path, and it branches (uniformly) around the masking of full subtiles
-  // and around unneeded rescales. With two in flight the branches would
-  // split the block the scheduler overlaps, and the register allocator then
-  // holds both subtiles' operands across them (lower occupancy): straight
-  // line code instead.
-  constexpr bool kSkip = U == 1;
-  // Eight waves with one bf16 subtile each: a wave reissues as soon as a
-  // subtile lands. The next subtile's keys are requested once the current
-  // keys are in registers, its values once the current values are, each
-  // before the current data is used, so a wave's compute never delays its
-  // next request (two subtiles of registers; two waves per SIMD). Issuing
-  // the next subtile earlier, before the current one lands, measured
-  // slower, and so did this schedule for E4M3 subtiles (half the bytes per
-  // request round, plus the conversions).
-  constexpr bool kPipe = U == 1 && NW == 8 && !F8;
+  // A wave has one subtile in flight, so the compute tail is on the
+  // critical path: it branches (uniformly) around the masking of full
+  // subtiles and around unneeded rescales.
+  //
+  // bf16 (reissue on arrival): the next subtile's keys are requested once
+  // the current keys are in registers, its values once the current values
+  // are, each before the current data is used, so a wave's compute never
+  // delays its next request (two subtiles of registers; two waves per
+  // SIMD). Issuing the next subtile earlier, before the current one lands,
+  // measured slower; so did this schedule for E4M3 subtiles (half the
+  // bytes per request, plus the conversions), which keep the plain loop.
+  constexpr bool kPipe = !F8;
 
   // The k-vector of QK call c for token group tg (bf16 operands).
   auto k_operand = [&](const u32x4 (&kr)[2][KL], int tg, int c) -> bf16x8 {
@@ -592,7 +583,7 @@ void split_mfma(
     }
     float sv[8];
     float mx = -INFINITY;
-    if (kSkip && t0 + 32 <= hi) {           // every token valid (uniform)
+    if (t0 + 32 <= hi) {                    // every token valid (uniform)
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg)
 #pragma unroll
@@ -622,7 +613,7 @@ void split_mfma(
     const float mcand = fmaxf(m_run, mx);
     const bool upd = mcand > m_run + kRefSlack;
     float alpha = 1.f;
-    if (!kSkip || __builtin_amdgcn_ballot_w64(upd) != 0) {
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
       alpha = upd ? fexp2(m_run - mcand) : 1.f;
       m_run = upd ? mcand : m_run;
     }
@@ -645,7 +636,7 @@ void split_mfma(
       asm volatile("" ::"v"(__builtin_bit_cast(u32x4, ph)),
                    "v"(__builtin_bit_cast(u32x4, pl)));
     }
-    if (!kSkip || __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
       for (int cc = 0; cc < NV; ++cc) o[cc] *= alpha;
     }
@@ -669,19 +660,15 @@ void split_mfma(
     }
   };
 
-  // The first U subtiles are consumed without a branch on the length (a
-  // branch would let the compiler sink their loads behind the length load).
-  // A subtile past hi is fully masked and changes nothing.
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int t0 = t_first + 32 * NW * u;
+  // The first subtile is consumed without a branch on the length (a branch
+  // would let the compiler sink its loads behind the length load). A
+  // subtile past hi is fully masked and changes nothing.
+  if (SPEC && t_first + 32 > hi) {
     // Rows at or past hi were read speculatively: zero their V.
-    if (SPEC && (!kSkip || t0 + 32 > hi)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = t0 + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
-        if (t >= hi) vp[u][e] = VT{};
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int t = t_first + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
+      if (t >= hi) vp[e] = VT{};
     }
   }
   if constexpr (kPipe) {
@@ -712,24 +699,16 @@ void split_mfma(
       return more;
     };
     for (int t0 = t_first;; t0 += 64 * NW) {
-      if (!step(t0, kp[0], vp[0], kq, vq)) break;
-      if (!step(t0 + 32 * NW, kq, vq, kp[0], vp[0])) break;
+      if (!step(t0, kp, vp, kq, vq)) break;
+      if (!step(t0 + 32 * NW, kq, vq, kp, vp)) break;
     }
   } else {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      compute_subtile(t_first + 32 * NW * u, kp[u], vp[u], [] {});
-    for (int t0 = t_first + 32 * NW * U; t0 < hi; t0 += 32 * NW * U) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        load_subtile(min(t0 + 32 * NW * u, (hi - 1) & ~15), hi, kp[u], vp[u],
-                     3);
-      // All of the block's requests go out before its first use.
+    compute_subtile(t_first, kp, vp, [] {});
+    for (int t0 = t_first + 32 * NW; t0 < hi; t0 += 32 * NW) {
+      load_subtile(t0, hi, kp, vp, 3);
+      // All of the subtile's requests go out before its first use.
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (t0 + 32 * NW * u < hi)
-          compute_subtile(t0 + 32 * NW * u, kp[u], vp[u], [] {});
+      compute_subtile(t0, kp, vp, [] {});
     }
   }
 
@@ -862,58 +841,50 @@ dim3 split_grid(int units, int B, int S) {
   return dim3((unsigned)units, (unsigned)B, (unsigned)S);
 }
 
-// Launch shape of the MFMA kernel for a split of P tokens: waves per
-// workgroup and subtiles each wave requests at once. Measured on MI355X
-// (64K, 256K and batch-64 histories, non-temporal K/V loads): short splits
-// want about two subtiles per wave (4 or 8 waves); long splits run best with
-// 4 waves each holding two subtiles in flight (2 waves per SIMD). E4M3
-// caches (64K and 256K histories, S = 64..256): one subtile in flight per
-// wave wins at every split length (the in-register conversion lengthens
-// the compute tail more than extra requests help), 8 waves from 9 subtiles.
-struct MfmaShape { int nw, u; };
-MfmaShape mfma_shape(int P, bool f8) {
+// Waves per workgroup of the MFMA kernel for a split of P tokens. Measured
+// on MI355X: bf16 runs best with 4 waves and the reissue schedule at every
+// split length (64K, 256K, the ragged batch and the batch of 64 short
+// histories; 8 waves, or 4 waves with two subtiles requested at once, were
+// 1-4 % slower). E4M3 (64K and 256K, S = 64..256) keeps the plain loop with
+// 8 waves from 9 subtiles per split (the in-register conversion lengthens
+// the compute tail more than extra requests help).
+int split_waves(int P, bool f8) {
   const int nsub = (P + 31) / 32;
-  if (f8) return nsub > 8 ? MfmaShape{8, 1} : MfmaShape{4, 1};
-  if (nsub > 16) return {4, 2};
-  if (nsub > 8) return {8, 1};
-  return {4, 1};
+  return f8 && nsub > 8 ? 8 : 4;
 }
 
 // The leading scalar arguments are what a wave needs before its first K/V
 // request; they fit the 14 kernel-argument dwords gfx950 preloads into SGPRs
 // at dispatch, so no wave waits on an argument load before its first
 // request (such loads queue behind other waves' K/V traffic).
-template <int D, int NW, int U, int GM, bool PAGED, bool SPEC, bool F8,
+template <int D, int NW, int GM, bool PAGED, bool SPEC, bool F8,
           bool BAL = false>
 void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_mfma<D, NW, U, GM, PAGED, SPEC, F8, BAL>), grid,
+  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, F8, BAL>), grid,
                      dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
                      a.nhg, a.G, a.block_table, a.bs, a);
 }
 
 template <int D, bool PAGED, int GM, bool SPEC, bool F8, bool BAL = false>
-void launch_mfma_spec(dim3 grid, MfmaShape m, const SplitArgs& a,
-                      hipStream_t st) {
-  if (m.nw == 8)
-    launch_one<D, 8, 1, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
-  else if (!F8 && m.u == 2)
-    launch_one<D, 4, F8 ? 1 : 2, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
+void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
+  if (F8 && nw == 8)
+    launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
   else
-    launch_one<D, 4, 1, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
+    launch_one<D, 4, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
 }
 
 // Speculative first loads pay off for a single sequence (its splits are all
 // full when the caller's bound is its length); for a batch, whose lengths
 // may differ, they could read splits that turn out empty.
 template <int D, bool PAGED, int GM, bool F8>
-void launch_mfma_gm(dim3 grid, MfmaShape m, const SplitArgs& a, hipStream_t st) {
+void launch_mfma_gm(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
   if (a.B == 1)
-    launch_mfma_spec<D, PAGED, GM, true, F8>(grid, m, a, st);
+    launch_mfma_spec<D, PAGED, GM, true, F8>(grid, nw, a, st);
   else if (a.bal_target > 0 && a.B <= 64)       // lane = sequence
-    launch_mfma_spec<D, PAGED, GM, false, F8, true>(grid, m, a, st);
+    launch_mfma_spec<D, PAGED, GM, false, F8, true>(grid, nw, a, st);
   else
-    launch_mfma_spec<D, PAGED, GM, false, F8>(grid, m, a, st);
+    launch_mfma_spec<D, PAGED, GM, false, F8>(grid, nw, a, st);
 }
 
 template <int D, bool PAGED, bool F8>
@@ -924,11 +895,11 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   a.bal_target = a.balance_cus > 0 && a.S > 1
                      ? max(1, 2 * a.balance_cus / (s.Hkv * a.nhg)) : 0;
   const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
-  const MfmaShape m = mfma_shape(a.P, F8);
+  const int nw = split_waves(a.P, F8);
   if (gm == 8)
-    launch_mfma_gm<D, PAGED, 8, F8>(grid, m, a, st);
+    launch_mfma_gm<D, PAGED, 8, F8>(grid, nw, a, st);
   else
-    launch_mfma_gm<D, PAGED, 16, F8>(grid, m, a, st);
+    launch_mfma_gm<D, PAGED, 16, F8>(grid, nw, a, st);
 }
 
 template <bool F8>
