@@ -233,15 +233,15 @@ __global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
 //
 // One workgroup = NW waves on one split of one (sequence, kv head, group of
 // at most GM query heads). Wave w owns the 32-token subtiles w, w+NW, ... of
-// the split, each loaded and then consumed; the other resident waves cover
-// the latency. With SPEC (batch 1) a wave's first subtiles are requested
-// before the sequence length is known: their rows are clamped to the
-// split's range for a full-length history, which is always inside the
-// cache, and V rows past the true length are zeroed once the length arrives
-// (they may hold anything, NaN included, and are multiplied by p = 0).
-// Without SPEC the length comes first and nothing past it is read. At the
-// end every wave parks its (O, m, l) in LDS and the whole workgroup merges
-// them in one pass.
+// the split, one in flight at a time (bf16: the next one is requested as the
+// current one lands); the other resident waves cover the latency. With SPEC
+// (batch 1) a wave's first subtile is requested before the sequence length
+// is known: its rows are clamped to the split's range for a full-length
+// history, which is always inside the cache, and V rows past the true length
+// are zeroed once the length arrives (they may hold anything, NaN included,
+// and are multiplied by p = 0). Without SPEC the length comes first and
+// nothing past it is read. At the end every wave parks its (O, m, l) in LDS
+// and the whole workgroup merges them in one pass.
 constexpr int kMaxPages = 1024;   // page ids a workgroup stages in LDS
 constexpr float kRefSlack = 8.f;  // exponent-reference slack, base 2
 
