@@ -73,7 +73,7 @@ struct SummaryArgs {
   const uint16_t* k;            // bf16 keys, contiguous or paged
   const int32_t* block_table;
   const int32_t* seq_lens;
-  uint8_t* codes;               // layout of k with D/2 bytes per row
+  uint8_t* codes;               // one 8*D-byte record per 16-token block
   float* scales;                // [B,Hkv,nblk_row] or [NB,Hkv,bs/16]
   int Hkv, L, bs, max_blocks, num_blocks, nblk_row;
 };
