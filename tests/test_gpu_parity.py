@@ -142,6 +142,21 @@ def test_ragged_tails_with_poisoned_cache(dtype, paged):
         check(w, S)
 
 
+@pytest.mark.parametrize("batch", [1, 3])
+def test_subtile_rounds_per_wave(batch):
+    # A bf16 wave streams the subtiles w, w + NW, ... of its split and
+    # requests the next one as the current one lands, alternating two
+    # register sets; these lengths end that loop after 1 to 7 rounds, on
+    # either set, with full, partial and fully masked last subtiles.
+    for L in (96, 128, 200, 256, 401, 640, 777, 896):
+        lens = [L] if batch == 1 else [L, max(L - 37, 1), L // 2]
+        w = workloads.make(f"rounds{L}", seed=40 + L, batch=batch,
+                           num_q_heads=16, num_kv_heads=2, head_dim=128,
+                           max_seq_len=L, seq_lens=lens, poison_tail=True)
+        for S in (1, 2, 3):
+            check(w, S)
+
+
 def test_more_splits_than_tiles():
     lens = [3, 64, 40, 17]
     w = workloads.make("few_tiles", seed=22, batch=4, num_q_heads=8,
