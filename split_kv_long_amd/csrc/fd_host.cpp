@@ -191,7 +191,11 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
   const int64_t units = (int64_t)s.B * s.Hkv * head_groups(s);
   const int64_t cmin =
       s.dtype == FD_DTYPE_F32 ? kMinSplitTokensF32 : kMinSplitTokens;
-  if (units >= num_cus || s.L < 2 * cmin) {
+  // No split when the sequences alone fill the CUs, when the history is
+  // shorter than two minimum splits, or when they fill half the CUs and
+  // the history is short (the combine then costs more than it saves).
+  if (units >= num_cus || s.L < 2 * cmin ||
+      (2 * units >= num_cus && s.L < kShortHistoryTokens)) {
     *num_splits = 1;
     return FD_OK;
   }
@@ -199,9 +203,11 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
   const int64_t work = tokens * s.Hkv * head_groups(s);
   const int64_t target = (int64_t)kOccupancy * num_cus;
   int64_t per = (work + target - 1) / target;
-  // Long splits: two workgroups per CU balance better and the extra
-  // partials cost nothing measurable.
-  if (per > kLongSplitTokens) per = (per + 1) / 2;
+  // A ragged batch (a known total below batch x bound): long splits are
+  // halved, so the length-aware pieces can even out about two workgroups
+  // per CU. Uniform histories keep one workgroup per CU.
+  const bool ragged = sum_seq_len >= 0 && sum_seq_len < (int64_t)s.B * s.L;
+  if (ragged && per > kLongSplitTokens) per = (per + 1) / 2;
   if (per < cmin) per = cmin;
   const int64_t g = s.bs > 16 ? s.bs : 16;
   per = (per + g - 1) / g * g;

@@ -10,17 +10,18 @@
 namespace fd {
 
 // Planner constants. A split is never shorter than kMinSplitTokens
-// (kMinSplitTokensF32 for fp32 caches); the
-// attended tokens are spread over about kOccupancy * num_cus workgroups,
-// twice that when the resulting splits exceed kLongSplitTokens. Set from a
-// sweep of batch {1..256} x history {512..256K} x splits {1..256} (16 query
-// / 2 kv heads, d 128, bf16) on MI355X: with these values the planned
-// split count is within a few percent of the best measured one except at
-// a few short-history points.
+// (kMinSplitTokensF32 for fp32 caches); the attended tokens are spread over
+// about kOccupancy * num_cus workgroups, twice that for a ragged batch whose
+// splits would exceed kLongSplitTokens; a batch that fills half the CUs is
+// not split below kShortHistoryTokens. Set from a sweep of batch {1..256} x
+// history {512..256K} x splits {1..256} (16 query / 2 kv heads, d 128,
+// bf16) and the ragged 16-sequence batch on MI355X: with these values the
+// planned split count is within a few percent of the best measured one.
 constexpr int kMinSplitTokens = 128;
 constexpr int kMinSplitTokensF32 = 64;   // fp32 path: latency-bound, split finer
 constexpr int kOccupancy = 1;
 constexpr int kLongSplitTokens = 1024;
+constexpr int kShortHistoryTokens = 1024;
 constexpr int kMaxSplits = 65535;
 constexpr int kMaxBlockSize = 4096;
 constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves

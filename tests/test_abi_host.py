@@ -60,16 +60,27 @@ def plan(cus=256, sum_len=-1, **kw):
 def test_planner_regimes():
     # batch-one long history: spread over the CUs, 512-token splits
     assert plan() == 128
-    assert plan(num_q_heads=64, num_kv_heads=8, max_seq_len=262144) == 64
+    # uniform long history: one workgroup per CU, 8192-token splits
+    assert plan(num_q_heads=64, num_kv_heads=8, max_seq_len=262144) == 32
+    assert plan(max_seq_len=262144) == 128
+    assert plan(max_seq_len=131072) == 128
     # a batch that already fills the GPU: no split
     assert plan(batch=64, num_q_heads=32, num_kv_heads=8, max_seq_len=1024) == 1
+    # half the CUs busy and a short history: no split either ...
+    assert plan(batch=64, max_seq_len=512) == 1
+    # ... but a longer one still gains from splitting
+    assert plan(batch=64, max_seq_len=2048) == 2
     # a short history: no split below two minimum-length (128-token) splits
     assert plan(max_seq_len=200) == 1
     # ... but a batch-one 512-token history already gains from 4 splits
     assert plan(max_seq_len=512) == 4
-    # splits longer than 1024 tokens are halved (two workgroups per CU)
-    assert plan(max_seq_len=262144) == 256
-    assert plan(max_seq_len=131072) == 128
+    # a ragged batch (known total below batch x bound): splits longer than
+    # 1024 tokens are halved, about two workgroups per CU for the
+    # length-aware pieces; the same batch taken as uniform is not
+    ragged = dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=32768)
+    assert plan(sum_len=245263, **ragged) == 9
+    assert plan(sum_len=16 * 32768, **ragged) == 2
+    assert plan(**ragged) == 2
     # tiny fp32 MHA history of 512 tokens: the fp32 path is latency-bound,
     # so it takes the shorter fp32 minimum split (64 tokens) -> 8 splits
     assert plan(num_q_heads=8, num_kv_heads=8, head_dim=64, max_seq_len=512,
