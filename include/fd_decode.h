@@ -110,15 +110,18 @@ typedef struct fd_shape {
  * history or a batch that already fills the GPU the extra partials and the
  * reduction may cost more than they save (slavadubrov.com, "Why decode needs
  * a different schedule"; aiexpertsdirectory.org, operational constraints).
- * The rule here: with units = batch * num_kv_heads, return 1 if units already
- * cover num_cus or L is short; otherwise size splits so that the attended
- * tokens spread over about num_cus workgroups, no split shorter than a
- * minimum length.
+ * The rule here: with units = batch * num_kv_heads (times the groups of up
+ * to 16 query heads), return 1 if units already cover num_cus, if L is
+ * short, or if units cover half of num_cus and L is under 1024; otherwise
+ * size splits so that the attended tokens spread over about num_cus
+ * workgroups (twice that, for splits over 1024 tokens, when sum_seq_len
+ * shows a ragged batch), no split shorter than a minimum length.
  *
  *   shape        host pointer, validated as for fd_decode_attn
  *   num_cus      compute units of the device (hipDeviceProp_t
  *                multiProcessorCount), >= 1
- *   sum_seq_len  sum of seq_lens[] if the caller knows it, else -1
+ *   sum_seq_len  sum of seq_lens[] if the caller knows it, else -1 (then
+ *                every sequence is taken to be max_seq_len long)
  *   num_splits   host out: the chosen S >= 1
  */
 int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
