@@ -47,9 +47,10 @@ constexpr int kGenThreads = 256;
 // A tile is 16 KB of K and 16 KB of V (64 tokens at D = 64, 32 at D = 128):
 // each thread requests its four 16-byte pieces of each at once, the next
 // tile's requests go out while the current one is computed, and rows past
-// the split's end are never read (zero in LDS). Scores are per-(head, token)
-// fp32 dot products, the online-softmax update is wave-parallel (one wave
-// per head, lanes = tokens) and the PV update is per-(head, dim).
+// the split's end hold zeros in LDS. Scores are fp32 dot products, four
+// lanes per (head, token); the online-softmax update is wave-parallel (one
+// wave per head, lanes = tokens); the PV update takes sixteen lanes per
+// (head, 4 dims), each over a sixteenth of the tile, summed with DPP.
 template <int D>
 __global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
   constexpr int GH = kHeadsPerGroup;
@@ -83,19 +84,19 @@ __global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
   const float* V = static_cast<const float*>(a.v);
   const float* Q = static_cast<const float*>(a.q) + ((size_t)b * a.Hq + h0) * D;
 
+  // Rows past the tile's end re-read its last row (attended, so always
+  // readable) and are zeroed when stored to LDS: the loads stay
+  // unconditional and the pieces stay in registers.
   f32x4 kr[NL], vr[NL];
   auto load_tile = [&](int t0, int nt) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int idx = tid + i * kGenThreads;
       const int r = idx / C4, c = idx - r * C4;
-      if (r < nt) {
-        const size_t off = row_offset<D>(a, b, kvh, t0 + r) + 4 * c;
-        kr[i] = *reinterpret_cast<const f32x4*>(K + off);
-        vr[i] = *reinterpret_cast<const f32x4*>(V + off);
-      } else {
-        kr[i] = vr[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      const size_t off =
+          row_offset<D>(a, b, kvh, t0 + (r < nt ? r : nt - 1)) + 4 * c;
+      kr[i] = *reinterpret_cast<const f32x4*>(K + off);
+      vr[i] = *reinterpret_cast<const f32x4*>(V + off);
     }
   };
   int t0 = lo;
@@ -118,30 +119,33 @@ __global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
     for (int i = 0; i < NL; ++i) {
       const int idx = tid + i * kGenThreads;
       const int r = idx / C4, c = idx - r * C4;
-      *reinterpret_cast<f32x4*>(&k_s[r][4 * c]) = kr[i];
-      *reinterpret_cast<f32x4*>(&v_s[r][4 * c]) = vr[i];
+      const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&k_s[r][4 * c]) = r < nt ? kr[i] : z;
+      *reinterpret_cast<f32x4*>(&v_s[r][4 * c]) = r < nt ? vr[i] : z;
     }
     __syncthreads();
     const int t1 = t0 + TILE;
     if (t1 < hi) load_tile(t1, min(TILE, hi - t1));   // prefetch
 
-    for (int i = tid; i < nh * TILE; i += kGenThreads) {
-      const int g = i / TILE, jj = i - g * TILE;
-      float sc = -INFINITY;
-      if (jj < nt) {
-        float acc = 0.f;
+    // Scores: four lanes per (head, token), a quarter of the dims each,
+    // summed across the quad.
+    for (int i = tid; i < nh * TILE * 4; i += kGenThreads) {
+      const int qq = i & 3, gt = i >> 2;
+      const int g = gt / TILE, jj = gt - g * TILE;
+      float acc = 0.f;
 #pragma unroll
-        for (int c = 0; c < C4; ++c) {
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(&q_s[g][4 * c]);
-          const f32x4 kv = *reinterpret_cast<const f32x4*>(&k_s[jj][4 * c]);
-          acc = fmaf(qv[0], kv[0], acc);
-          acc = fmaf(qv[1], kv[1], acc);
-          acc = fmaf(qv[2], kv[2], acc);
-          acc = fmaf(qv[3], kv[3], acc);
-        }
-        sc = acc * a.scale_log2;
+      for (int c0 = 0; c0 < C4 / 4; ++c0) {
+        const int c = qq * (C4 / 4) + c0;
+        const f32x4 qv = *reinterpret_cast<const f32x4*>(&q_s[g][4 * c]);
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(&k_s[jj][4 * c]);
+        acc = fmaf(qv[0], kv[0], acc);
+        acc = fmaf(qv[1], kv[1], acc);
+        acc = fmaf(qv[2], kv[2], acc);
+        acc = fmaf(qv[3], kv[3], acc);
       }
-      p_s[g][jj] = sc;
+      acc += dpp_f<0xB1>(acc);
+      acc += dpp_f<0x4E>(acc);
+      if (qq == 0) p_s[g][jj] = jj < nt ? acc * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
     for (int g = wave; g < nh; g += kGenThreads / 64) {
@@ -159,26 +163,41 @@ __global__ __launch_bounds__(kGenThreads) void split_f32(SplitArgs a) {
       }
     }
     __syncthreads();
-    // Rows past nt hold zeros in v_s and p_s, so the loop runs the full
-    // tile with a constant trip count and its LDS reads batch up.
-    for (int i = tid; i < nh * C4; i += kGenThreads) {
-      const int g = i / C4, c = i - g * C4;
-      const float al = al_s[g];
-      f32x4 acc = *reinterpret_cast<const f32x4*>(&acc_s[g][4 * c]);
-      acc[0] *= al;
-      acc[1] *= al;
-      acc[2] *= al;
-      acc[3] *= al;
-#pragma unroll 16
-      for (int jj = 0; jj < TILE; ++jj) {
+    // PV: sixteen lanes (one DPP row) per (head, 4 dims), each over a
+    // sixteenth of the tile's tokens, summed across the row. Rows past nt
+    // hold zeros in v_s and p_s, so every lane runs the same trip count.
+    for (int i = tid; i < nh * C4 * 16; i += kGenThreads) {
+      const int t = i & 15, gc = i >> 4;
+      const int g = gc / C4, c = gc - g * C4;
+      f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < TILE / 16; ++u) {
+        const int jj = t * (TILE / 16) + u;
         const float pj = p_s[g][jj];
         const f32x4 vv = *reinterpret_cast<const f32x4*>(&v_s[jj][4 * c]);
-        acc[0] = fmaf(pj, vv[0], acc[0]);
-        acc[1] = fmaf(pj, vv[1], acc[1]);
-        acc[2] = fmaf(pj, vv[2], acc[2]);
-        acc[3] = fmaf(pj, vv[3], acc[3]);
+        part[0] = fmaf(pj, vv[0], part[0]);
+        part[1] = fmaf(pj, vv[1], part[1]);
+        part[2] = fmaf(pj, vv[2], part[2]);
+        part[3] = fmaf(pj, vv[3], part[3]);
       }
-      *reinterpret_cast<f32x4*>(&acc_s[g][4 * c]) = acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = part[e];
+        x += dpp_f<0xB1>(x);
+        x += dpp_f<0x4E>(x);
+        x += dpp_f<0x124>(x);
+        x += dpp_f<0x128>(x);
+        part[e] = x;
+      }
+      if (t == 0) {
+        const float al = al_s[g];
+        f32x4 acc = *reinterpret_cast<const f32x4*>(&acc_s[g][4 * c]);
+        acc[0] = fmaf(acc[0], al, part[0]);
+        acc[1] = fmaf(acc[1], al, part[1]);
+        acc[2] = fmaf(acc[2], al, part[2]);
+        acc[3] = fmaf(acc[3], al, part[3]);
+        *reinterpret_cast<f32x4*>(&acc_s[g][4 * c]) = acc;
+      }
     }
     __syncthreads();
     if (t1 >= hi) break;
