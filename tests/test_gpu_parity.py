@@ -157,6 +157,31 @@ def test_subtile_rounds_per_wave(batch):
             check(w, S)
 
 
+def test_random_shapes():
+    # A seeded sweep over the shape space: dtype, head_dim, kv heads, group
+    # size (both head-group widths), batch, ragged lengths with one full
+    # history, contiguous or paged (16- to 64-token pages), split count.
+    import random
+    rng = random.Random(2026)
+    for case in range(60):
+        kv = rng.choice(["bf16", "bf16", "fp8_e4m3", "f32"])
+        hkv, g = rng.choice([1, 2, 3, 4]), rng.choice([1, 2, 4, 5, 8, 12, 16, 24])
+        b = rng.choice([1, 1, 2, 3, 5, 9])
+        L = rng.choice([1, 15, 33, 100, 257, 511, 700, 1024, 1500, 3000])
+        lens = [rng.randint(0, L) for _ in range(b)]
+        lens[rng.randrange(b)] = L
+        paged = rng.random() < 0.5
+        w = workloads.make(f"random{case}", seed=3000 + case, batch=b,
+                           num_q_heads=g * hkv, num_kv_heads=hkv,
+                           head_dim=rng.choice([64, 128]), max_seq_len=L,
+                           dtype="f32" if kv == "f32" else "bf16",
+                           paged=paged,
+                           block_size=rng.choice([16, 32, 64]) if paged else 16,
+                           seq_lens=lens, poison_tail=True,
+                           kv_dtype="fp8_e4m3" if kv == "fp8_e4m3" else None)
+        check(w, rng.choice([1, 2, 3, 4, 7, 8, 16, 33, 64]))
+
+
 def test_more_splits_than_tiles():
     lens = [3, 64, 40, 17]
     w = workloads.make("few_tiles", seed=22, batch=4, num_q_heads=8,
