@@ -245,3 +245,26 @@ def test_sparse_and_summary_with_larger_pages(bs):
                        needles=[5, 1333, 3999], needle_logit=14.0,
                        poison_tail=True)
     check_sparse(w, 2.0, 3, expect_dropped=False)
+
+
+def test_sparse_random_shapes():
+    # Seeded sweep: batch, kv heads, group size (both head-group widths),
+    # head_dim, ragged lengths, contiguous or paged, delta and split count;
+    # kept sets must equal the oracle's and outputs match exact attention
+    # over the kept blocks.
+    import random
+    rng = random.Random(909)
+    for case in range(16):
+        hkv, g = rng.choice([1, 2, 3]), rng.choice([1, 3, 8, 12, 16])
+        L = rng.choice([17, 100, 511, 900, 1500])
+        b = rng.choice([1, 2, 3])
+        lens = [rng.randint(1, L) for _ in range(b)]
+        lens[rng.randrange(b)] = L
+        w = workloads.make(f"sparse_random{case}", seed=4000 + case,
+                           batch=b, num_q_heads=g * hkv, num_kv_heads=hkv,
+                           head_dim=rng.choice([64, 128]), max_seq_len=L,
+                           paged=rng.random() < 0.5, seq_lens=lens,
+                           needles=[0, L // 2, L - 1], needle_logit=10.0,
+                           poison_tail=True)
+        check_sparse(w, rng.choice([0.0, 0.5, 2.0, 5.0]),
+                     rng.choice([1, 2, 3, 5, 8]), expect_dropped=False)
