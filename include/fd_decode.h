@@ -137,7 +137,11 @@ int fd_workspace_size(const fd_shape* shape, int num_splits, size_t* bytes);
 
 /*
  * Full decode attention: the split kernel, then (if num_splits > 1) the
- * log-sum-exp combine kernel, on `stream`.
+ * log-sum-exp combine kernel, on `stream`. For 2 to 64 sequences and
+ * num_splits > 1 the split kernel cuts each sequence into up to num_splits
+ * equal pieces sized by its own length instead of the uniform splits above
+ * (an internal choice: the result is the same attention, and it stays
+ * deterministic for a given device).
  *
  *   q, k_cache, v_cache  device, dtype per shape, 16-byte aligned
  *   block_table          device int32, non-NULL iff shape->block_size > 0
