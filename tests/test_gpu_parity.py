@@ -327,6 +327,47 @@ def test_partials_and_combine_entry_points():
                   lse.cpu().double().numpy(), ref_out, ref_lse)
 
 
+@pytest.mark.parametrize("lens", [[16384], [16384, 9000, 4100, 1]])
+def test_sequence_sharded_partials_then_combine(lens):
+    # The sequence-sharded layout on one GPU: the history is cut into four
+    # contiguous shards (what four GPUs would each hold); every shard runs
+    # the split step on its own cache with its own split count, the
+    # partials are concatenated along the split axis (what an all-gather
+    # would deliver), and one combine gives attention over the whole
+    # history. Shards past a sequence's end contribute empty partials.
+    L, R = 16384, 4
+    w = workloads.make("sharded", seed=29, batch=len(lens), num_q_heads=16,
+                       num_kv_heads=2, head_dim=128, max_seq_len=L,
+                       seq_lens=lens, poison_tail=True)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    d = torch.device("cuda")
+    q = w.q.to(d)
+    Ls = L // R
+    ops, lps = [], []
+    for r in range(R):
+        k = w.k[:, :, r * Ls:(r + 1) * Ls].contiguous().to(d)
+        v = w.v[:, :, r * Ls:(r + 1) * Ls].contiguous().to(d)
+        sl = torch.clamp(w.seq_lens - r * Ls, 0, Ls).to(torch.int32).to(d)
+        shape = fb.make_shape(B, Hq, w.num_kv_heads, D, Ls, "bf16")
+        S_r = 8 + 8 * r                        # shards need not agree on S
+        op = torch.empty(B, Hq, S_r, D, device=d)
+        lp = torch.empty(B, Hq, S_r, device=d)
+        print(f"[gpu] shard {r} S={S_r}", flush=True)
+        fb.fd_decode_partials(shape, q, k, v, None, sl, S_r, op, lp)
+        ops.append(op)
+        lps.append(lp)
+    op = torch.cat(ops, dim=2).contiguous()
+    lp = torch.cat(lps, dim=2).contiguous()
+    S = op.shape[2]
+    out = torch.empty(B, Hq, D, device=d)
+    lse = torch.empty(B, Hq, device=d)
+    fb.fd_combine_partials(B, Hq, D, S, op, lp, out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_attention(w)
+    assert_parity("sharded", "bf16", out.cpu().double().numpy(),
+                  lse.cpu().double().numpy(), ref_out, ref_lse)
+
+
 def test_deterministic_bitwise():
     w = workloads.make("long_gqa_64k", max_seq_len=16384)
     t = device_inputs(w)
