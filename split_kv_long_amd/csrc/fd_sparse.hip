@@ -258,8 +258,9 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         lastr[u] = min(kSumBlock, hi - t0) - 1;
         const size_t bi = scale_index(t0);    // record = scale slot
         bscale[u] = sp.scales[bi];
-        cw[u] = *reinterpret_cast<const CT*>(sp.codes + bi * (kSumBlock * D / 2) +
-                                             CB * lane);
+        // Streamed once per call, like K and V: non-temporal.
+        cw[u] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(
+            sp.codes + bi * (kSumBlock * D / 2) + CB * lane));
       }
 #pragma unroll
       for (int u = 0; u < CHUNK; ++u) {
