@@ -244,12 +244,13 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
                     (int)q8w[4 * c + 3]};
     float wmax = -INFINITY;
     // A wave's blocks go CHUNK at a time: every code and scale request of a
-    // chunk is issued before the first product, one memory round trip each.
+    // chunk is issued before the first product, and the next chunk is
+    // requested as soon as the current one is in registers (two register
+    // sets, used in turn; the empty asm statements make the compiler wait
+    // for exactly those loads there).
     using CT = typename std::conditional<D == 128, u32x4, u32x2>::type;
-    for (int jl0 = w; jl0 < nb; jl0 += NW * CHUNK) {
-      CT cw[CHUNK];
-      float bscale[CHUNK];
-      int lastr[CHUNK];
+    auto load_chunk = [&](int jl0, CT (&cw)[CHUNK], float (&bscale)[CHUNK],
+                          int (&lastr)[CHUNK]) {
 #pragma unroll
       for (int u = 0; u < CHUNK; ++u) {
         const int jl = min(jl0 + NW * u, nb - 1);   // clamped: inside the split
@@ -261,6 +262,10 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         cw[u] = __builtin_nontemporal_load(reinterpret_cast<const CT*>(
             sp.codes + bi * (kSumBlock * D / 2) + CB * lane));
       }
+    };
+    auto scan_chunk = [&](int jl0, const CT (&cw)[CHUNK],
+                          const float (&bscale)[CHUNK],
+                          const int (&lastr)[CHUNK]) {
 #pragma unroll
       for (int u = 0; u < CHUNK; ++u) {
         const int jl = jl0 + NW * u;
@@ -302,6 +307,30 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         if (j == 0 && n < GM) est_s[jl][n] = e;
         wmax = fmaxf(wmax, e);
       }
+    };
+    CT cwA[CHUNK], cwB[CHUNK];
+    float bsA[CHUNK], bsB[CHUNK];
+    int lrA[CHUNK], lrB[CHUNK];
+    int jl0 = w;
+    if (jl0 < nb) load_chunk(jl0, cwA, bsA, lrA);
+    while (jl0 < nb) {
+#pragma unroll
+      for (int u = 0; u < CHUNK; ++u) asm volatile("" ::"v"(cwA[u]));
+      __builtin_amdgcn_sched_barrier(0);
+      int jn = jl0 + NW * CHUNK;
+      if (jn < nb) load_chunk(jn, cwB, bsB, lrB);
+      __builtin_amdgcn_sched_barrier(0);
+      scan_chunk(jl0, cwA, bsA, lrA);
+      jl0 = jn;
+      if (jl0 >= nb) break;
+#pragma unroll
+      for (int u = 0; u < CHUNK; ++u) asm volatile("" ::"v"(cwB[u]));
+      __builtin_amdgcn_sched_barrier(0);
+      jn = jl0 + NW * CHUNK;
+      if (jn < nb) load_chunk(jn, cwA, bsA, lrA);
+      __builtin_amdgcn_sched_barrier(0);
+      scan_chunk(jl0, cwB, bsB, lrB);
+      jl0 = jn;
     }
     if (j == 0 && n < GM) wmax_s[w][n] = wmax;
   }
