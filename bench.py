@@ -14,7 +14,11 @@ Prints one JSON line (rank 0). Besides the metric it carries
   roofline      the split kernel's algorithmic bytes per launch over its
                 average launch time, measured here with events around a
                 graph of split-only launches, against 8 TB/s HBM peak;
-  cpu_baseline  the float64 CPU oracle timed on the same call.
+  cpu_baseline  the float64 CPU oracle timed on the same call (all host
+                cores, and one core);
+  stream_loop_us_per_call  the same calls enqueued in a plain loop, no graph;
+  warm_one_copy_us_per_call  every call on the same K/V copy, which the
+                Infinity Cache may serve: context only, not an HBM figure.
 """
 
 from __future__ import annotations
@@ -185,6 +189,22 @@ class Bench:
         return time_graph(self.torch, fn, steps, warmup)
 
 
+def time_stream(torch, fn, steps, warmup):
+    """The same calls enqueued eagerly on the current stream, timed with
+    events around the loop (host enqueue cost included)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def time_graph(torch, fn, steps, warmup):
     """Eager warmup, capture `steps` calls in a graph, replay once untimed,
     then time one replay. Returns (ms total, wall ms)."""
@@ -236,34 +256,54 @@ def copy_probe(torch):
                 GBps_read_plus_write=2 * n / (ms * 1e6))
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, target_s):
-    import numpy as np
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()
                        if i.get("user_api") == "blas"] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     a = w.numpy_view()
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
-                                dtype=a["dtype"], scale=a["scale"],
-                                block_table=a["block_table"],
-                                block_size=a["block_size"],
-                                kv_dtype=a["kv_dtype"], k_scale=a["k_scale"],
-                                v_scale=a["v_scale"])
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start >= target_s or len(times) >= 50:
-            break
-    med = statistics.median(times)
-    return dict(value=med * 1e6, unit="us/call", cores=threads, kind="oracle",
-                sample=(f"{len(times)} full calls of the {w.name} workload "
-                        f"(float64 NumPy oracle, median)"),
-                host_cpu_count=os.cpu_count())
+
+    def timed(budget_s, max_calls):
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                    dtype=a["dtype"], scale=a["scale"],
+                                    block_table=a["block_table"],
+                                    block_size=a["block_size"],
+                                    kv_dtype=a["kv_dtype"],
+                                    k_scale=a["k_scale"], v_scale=a["v_scale"])
+            times.append(time.perf_counter() - t0)
+            if (time.perf_counter() - t_start >= budget_s
+                    or len(times) >= max_calls):
+                return times
+    times = timed(target_s, 50)
+    rec = dict(value=statistics.median(times) * 1e6, unit="us/call",
+               cores=threads, kind="oracle",
+               sample=(f"{len(times)} full calls of the {w.name} workload "
+                       f"(float64 NumPy oracle, median)"),
+               host_cpu_count=os.cpu_count(), cpu_model=cpu_model())
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1 = timed(target_s / 2, 20)
+        rec["value_one_core"] = statistics.median(t1) * 1e6
+        rec["sample_one_core"] = f"{len(t1)} calls, BLAS limited to 1 thread"
+    return rec
 
 
 def workloads_compare_splits(name):
@@ -277,6 +317,9 @@ def run_one(args, name, steps, warmup, with_cpu):
               parse_overrides(args.set) if name == args.workload else None)
     ms, wall = b.time_graph(b.step, steps, warmup)
     us_call = ms * 1e3 / steps
+    ms_loop = time_stream(torch, b.step, steps, warmup)
+    warm_steps = min(steps, 50)
+    ms_warm, _ = b.time_graph(lambda i: b.step(0), warm_steps, warmup)
     ms_split, _ = b.time_graph(b.split_only, steps, warmup)
     us_split = ms_split * 1e3 / steps
     us_comb = None
@@ -327,6 +370,8 @@ def run_one(args, name, steps, warmup, with_cpu):
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": b.bytes_alg,
         "wall_ms_timed_region": round(wall, 3),
+        "stream_loop_us_per_call": round(ms_loop * 1e3 / steps, 3),
+        "warm_one_copy_us_per_call": round(ms_warm * 1e3 / warm_steps, 3),
         "split_kernel_us": round(us_split, 3),
         "combine_kernel_us": None if us_comb is None else round(us_comb, 3),
         "roofline": {
