@@ -205,9 +205,10 @@ def time_stream(torch, fn, steps, warmup):
     return e0.elapsed_time(e1)
 
 
-def time_graph(torch, fn, steps, warmup):
+def time_graph(torch, fn, steps, warmup, replays=1, spread=None):
     """Eager warmup, capture `steps` calls in a graph, replay once untimed,
-    then time one replay. Returns (ms total, wall ms)."""
+    then time `replays` replays. Returns (median ms per replay, wall ms of
+    the timed region); `spread`, if a dict, receives min/median/max."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -221,16 +222,22 @@ def time_graph(torch, fn, steps, warmup):
     torch.cuda.current_stream().wait_stream(s)
     g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
     wall = (time.perf_counter() - t0) * 1e3
-    return e0.elapsed_time(e1), wall
+    if spread is not None:
+        spread.update(min=min(times), median=statistics.median(times),
+                      max=max(times))
+    return statistics.median(times), wall
 
 
 def copy_probe(torch):
@@ -315,7 +322,9 @@ def run_one(args, name, steps, warmup, with_cpu):
     import torch
     b = Bench(name, args.splits if name == args.workload else 0, steps,
               parse_overrides(args.set) if name == args.workload else None)
-    ms, wall = b.time_graph(b.step, steps, warmup)
+    spread = {}
+    ms, wall = time_graph(torch, b.step, steps, warmup, replays=5,
+                          spread=spread)
     us_call = ms * 1e3 / steps
     ms_loop = time_stream(torch, b.step, steps, warmup)
     warm_steps = min(steps, 50)
@@ -362,7 +371,7 @@ def run_one(args, name, steps, warmup, with_cpu):
             "paged": w.paged, "kv_dtype": w.cache_dtype,
             "num_splits": b.S, "tokens_per_split": b.P,
             "kv_copies_rotated": b.R, "timing": "hip graph replay of all "
-            "timed steps between two events",
+            "timed steps between two events, median of 5 replays",
             "overrides": parse_overrides(args.set) if name == args.workload
             else {},
         },
@@ -370,6 +379,9 @@ def run_one(args, name, steps, warmup, with_cpu):
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": b.bytes_alg,
         "wall_ms_timed_region": round(wall, 3),
+        "replays": {"count": 5, "us_per_call_min": round(spread["min"] * 1e3 / steps, 3),
+                    "us_per_call_max": round(spread["max"] * 1e3 / steps, 3),
+                    "value_is": "median"},
         "stream_loop_us_per_call": round(ms_loop * 1e3 / steps, 3),
         "warm_one_copy_us_per_call": round(ms_warm * 1e3 / warm_steps, 3),
         "split_kernel_us": round(us_split, 3),
