@@ -23,7 +23,9 @@ What it computes, and where each step comes from:
 
 ``fp8_e4m3_to_f64`` decodes 8-bit E4M3 cache codes from the format's
 definition; ``decode_attention`` with ``kv_dtype="fp8_e4m3"`` and per-kv-head
-scales is the definition over the dequantized cache.
+scales is the definition over the dequantized cache. ``int8_to_f64`` and
+``kv_dtype="int8"`` do the same for an 8-bit integer cache, whose scales
+``scale_rows`` reads per (position, kv head).
 
 ``oracle.sparse`` holds the block-sparse variant (a low-bit key summary,
 a top-delta block filter per split, exact attention over the kept blocks),
@@ -36,8 +38,10 @@ Every function is float64 NumPy, one (sequence, kv head) at a time.
 from .attention import (  # noqa: F401
     bf16_bits_to_f64,
     fp8_e4m3_to_f64,
+    int8_to_f64,
     decode_values,
     history_rows,
+    scale_rows,
     softmax_attention,
     decode_attention,
     split_length,

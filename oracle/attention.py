@@ -10,7 +10,11 @@ implements, written independently there):
 * exposed log-sum-exp values are natural logarithms;
 * splits are contiguous token ranges of ``split_length(L, S)`` tokens;
 * a quantized (8-bit float E4M3) cache is read as its decoded codes times a
-  per-kv-head scale, and attention runs over those dequantized values.
+  per-kv-head scale, and attention runs over those dequantized values;
+* an 8-bit integer cache is read as its two's-complement codes times one
+  scale per (position, kv head), stored in the cache's own row layout
+  without the head dimension, and attention again runs over the
+  dequantized values.
 """
 
 from __future__ import annotations
@@ -52,16 +56,45 @@ def fp8_e4m3_to_f64(codes) -> np.ndarray:
     return sign * mag
 
 
+def int8_to_f64(codes) -> np.ndarray:
+    """8-bit two's-complement codes -> float64: a byte b >= 128 stands for
+    b - 256 (so 0x80 is -128 and 0xFF is -1); others for themselves."""
+    c = np.asarray(codes)
+    if c.dtype == np.int8:
+        c = c.view(np.uint8)
+    c = c.astype(np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
+
+
 def decode_values(arr, dtype: str) -> np.ndarray:
     """Raw input array -> float64 ('bf16': uint16 bit patterns; 'f32';
-    'fp8_e4m3': uint8 codes)."""
+    'fp8_e4m3': uint8 codes; 'int8': int8 or uint8 bytes)."""
     if dtype == "bf16":
         return bf16_bits_to_f64(arr)
     if dtype == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
     if dtype == "fp8_e4m3":
         return fp8_e4m3_to_f64(arr)
+    if dtype == "int8":
+        return int8_to_f64(arr)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def scale_rows(scale, b: int, kvh: int, lo: int, hi: int, block_table=None,
+               block_size: int = 0) -> np.ndarray:
+    """Per-position scales for positions lo..hi-1 of sequence b, kv head
+    kvh, as a column [n, 1].
+
+    A scale array of one value per kv head ([Hkv]) applies to every
+    position. One value per (position, kv head) is laid out like the cache
+    without its last axis: [B, Hkv, L], or [NB, Hkv, bs] for a paged pool,
+    where position i sits in block block_table[b, i // bs] at slot i % bs.
+    """
+    sc = np.asarray(scale, dtype=np.float64)
+    if sc.ndim == 1:
+        return np.full((max(hi - lo, 0), 1), sc[kvh])
+    return history_rows(sc[..., None], b, kvh, lo, hi, block_table,
+                        block_size)
 
 
 def history_rows(cache, b: int, kvh: int, lo: int, hi: int,
@@ -118,10 +151,11 @@ def decode_attention(q, k, v, seq_lens, *, dtype: str,
     token_range=(lo, hi) restricts every sequence to positions
     lo .. min(hi, seq_lens[b]) - 1 (used for split partials).
     Quantized caches: kv_dtype names the cache's encoding (default: dtype),
-    and k_scale / v_scale [Hkv] multiply every decoded key / value of that
-    kv head, so attention runs over the dequantized cache (the cache
-    precision the "What is Flash-Decoding" page asks comparisons to hold
-    fixed, in the low-bit form the "Faster Than Flash" abstract scans).
+    and k_scale / v_scale multiply every decoded key / value: one value per
+    kv head ([Hkv]) or one per (position, kv head) (see scale_rows), so
+    attention runs over the dequantized cache (the cache precision the
+    "What is Flash-Decoding" page asks comparisons to hold fixed, in the
+    low-bit form the "Faster Than Flash" abstract scans).
     Returns out [B, Hq, D] and lse [B, Hq] (natural log), float64.
     """
     kvd = kv_dtype or dtype
@@ -146,9 +180,11 @@ def decode_attention(q, k, v, seq_lens, *, dtype: str,
             vr = decode_values(history_rows(v, b, kvh, lo, hi, block_table,
                                             block_size), kvd)
             if k_scale is not None:
-                kr = kr * float(k_scale[kvh])
+                kr = kr * scale_rows(k_scale, b, kvh, lo, hi, block_table,
+                                     block_size)
             if v_scale is not None:
-                vr = vr * float(v_scale[kvh])
+                vr = vr * scale_rows(v_scale, b, kvh, lo, hi, block_table,
+                                     block_size)
             heads = slice(kvh * G, (kvh + 1) * G)
             scores = sc * (qf[b, heads] @ kr.T)
             o, l = softmax_attention(scores, vr)

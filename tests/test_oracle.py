@@ -545,3 +545,210 @@ def test_fp8_planted_mistake_is_caught(kind, monkeypatch):
         except AssertionError:
             failed.append(chk.__name__)
     assert failed, f"mutant {kind} passed every fp8 pin"
+
+
+# --- 8-bit integer cache, one scale per (position, kv head) ---------------
+
+INT8_HAND = {
+    # byte: value, from two's complement by hand (b >= 128 means b - 256)
+    0x00: 0.0, 0x01: 1.0, 0x7F: 127.0, 0x80: -128.0, 0x81: -127.0,
+    0xFE: -2.0, 0xFF: -1.0, 0x40: 64.0, 0xC0: -64.0,
+}
+
+
+def test_int8_decode_hand_values():
+    got = oracle.int8_to_f64(np.array(list(INT8_HAND), dtype=np.uint8))
+    assert np.array_equal(got, np.array(list(INT8_HAND.values())))
+    signed = np.array([-128, -1, 0, 1, 127], dtype=np.int8)
+    assert np.array_equal(oracle.int8_to_f64(signed),
+                          np.array([-128.0, -1.0, 0.0, 1.0, 127.0]))
+
+
+def _int8_case(seed, B=2, Hq=8, Hkv=2, D=16, L=29):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    k8 = torch.randint(-128, 128, (B, Hkv, L, D), generator=g,
+                       dtype=torch.int8)
+    v8 = torch.randint(-128, 128, (B, Hkv, L, D), generator=g,
+                       dtype=torch.int8)
+    ks = torch.rand(B, Hkv, L, generator=g) * 0.04 + 0.002
+    vs = torch.rand(B, Hkv, L, generator=g) * 0.1 + 0.01
+    lens = np.array([L, L // 2 + 1][:B])
+    return q, k8, v8, ks, vs, lens
+
+
+def _attn_i8(q, k, v, lens, ks, vs, block_table=None, block_size=0):
+    return oracle.decode_attention(q, k, v, lens, dtype="bf16",
+                                   kv_dtype="int8", k_scale=ks, v_scale=vs,
+                                   block_table=block_table,
+                                   block_size=block_size)
+
+
+def _i8_args(q, k8, v8, lens):
+    return (q.view(torch.uint16).numpy(), k8.numpy(), v8.numpy(), lens)
+
+
+def check_int8_sdpa(attn_i8, seed=40):
+    """Attention over an int8 cache with per-position scales against torch's
+    float64 scaled_dot_product_attention on the cache torch dequantizes."""
+    q, k8, v8, ks, vs, lens = _int8_case(seed)
+    B, Hq, D = q.shape
+    G = Hq // k8.shape[1]
+    out, lse = attn_i8(*_i8_args(q, k8, v8, lens), ks.numpy(), vs.numpy())
+    kd = k8.to(torch.float64) * ks.double()[..., None]
+    vd = v8.to(torch.float64) * vs.double()[..., None]
+    for b in range(B):
+        n = int(lens[b])
+        qt = q[b].double()[None, :, None, :]
+        kt = kd[b, :, :n].repeat_interleave(G, dim=0)[None]
+        vt = vd[b, :, :n].repeat_interleave(G, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+        assert np.allclose(out[b], ref[0, :, 0].numpy(), rtol=0, atol=1e-12)
+        s = (qt[0, :, 0, None, :] * kt[0]).sum(-1) / math.sqrt(D)
+        assert np.allclose(lse[b], torch.logsumexp(s, -1).numpy(), atol=1e-12)
+
+
+def check_int8_equals_bf16_of_same_values(attn_i8, seed=41):
+    """Power-of-two scales per position: every dequantized value is exact in
+    bf16 (an int8 has at most 8 significant bits), so the int8 path must
+    equal the (separately pinned) bf16 path on those values, bit for bit."""
+    q, k8, v8, _, _, lens = _int8_case(seed)
+    g = torch.Generator().manual_seed(seed + 100)
+    ks = torch.exp2(torch.randint(-9, -3, k8.shape[:3], generator=g).float())
+    vs = torch.exp2(torch.randint(-8, 0, v8.shape[:3], generator=g).float())
+    out, lse = attn_i8(*_i8_args(q, k8, v8, lens), ks.numpy(), vs.numpy())
+    kb = (k8.float() * ks[..., None]).to(torch.bfloat16)
+    vb = (v8.float() * vs[..., None]).to(torch.bfloat16)
+    assert torch.equal(kb.float(), k8.float() * ks[..., None])
+    assert torch.equal(vb.float(), v8.float() * vs[..., None])
+    o2, l2 = oracle.decode_attention(q.view(torch.uint16).numpy(),
+                                     kb.view(torch.uint16).numpy(),
+                                     vb.view(torch.uint16).numpy(), lens,
+                                     dtype="bf16")
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+
+
+def check_int8_paged_equals_contiguous(attn_i8, seed=42, bs=16):
+    """The same codes and scales moved, with no arithmetic, into a pool of
+    bs-slot blocks in shuffled order: the result must not change."""
+    q, k8, v8, ks, vs, lens = _int8_case(seed, L=61)
+    B, Hkv, L, D = k8.shape
+    nblk = -(-L // bs)
+    perm = torch.randperm(B * nblk, generator=torch.Generator().manual_seed(7))
+    NB = B * nblk + 1
+    kp = torch.full((NB, Hkv, bs, D), 99, dtype=torch.int8)
+    vp = torch.full((NB, Hkv, bs, D), -99, dtype=torch.int8)
+    ksp = torch.full((NB, Hkv, bs), 1e30)
+    vsp = torch.full((NB, Hkv, bs), float("nan"))
+    bt = np.zeros((B, nblk), dtype=np.int64)
+    for b in range(B):
+        for j in range(nblk):
+            blk = int(perm[b * nblk + j])
+            bt[b, j] = blk
+            t0, t1 = j * bs, min((j + 1) * bs, L)
+            kp[blk, :, :t1 - t0] = k8[b, :, t0:t1]
+            vp[blk, :, :t1 - t0] = v8[b, :, t0:t1]
+            ksp[blk, :, :t1 - t0] = ks[b, :, t0:t1]
+            vsp[blk, :, :t1 - t0] = vs[b, :, t0:t1]
+    ref = attn_i8(*_i8_args(q, k8, v8, lens), ks.numpy(), vs.numpy())
+    got = attn_i8(*_i8_args(q, kp, vp, lens), ksp.numpy(), vsp.numpy(),
+                  block_table=bt, block_size=bs)
+    assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
+
+
+def test_int8_attention_matches_torch_sdpa():
+    check_int8_sdpa(_attn_i8)
+
+
+def test_int8_attention_equals_bf16_on_exact_values():
+    check_int8_equals_bf16_of_same_values(_attn_i8)
+
+
+def test_int8_paged_equals_contiguous():
+    check_int8_paged_equals_contiguous(_attn_i8)
+
+
+def test_int8_per_head_scales_broadcast():
+    """A per-position scale array that is constant along positions gives
+    the same result as the one-value-per-kv-head form."""
+    q, k8, v8, _, _, lens = _int8_case(43)
+    B, Hkv, L, _ = k8.shape
+    kh = np.array([0.01, 0.03])[:Hkv]
+    vh = np.array([0.2, 0.05])[:Hkv]
+    a = _attn_i8(*_i8_args(q, k8, v8, lens), kh, vh)
+    b = _attn_i8(*_i8_args(q, k8, v8, lens),
+                 np.broadcast_to(kh[None, :, None], (B, Hkv, L)).copy(),
+                 np.broadcast_to(vh[None, :, None], (B, Hkv, L)).copy())
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_int8_split_partials_recombine():
+    q, k8, v8, ks, vs, lens = _int8_case(44, L=100)
+    args = _i8_args(q, k8, v8, lens)
+    ref = _attn_i8(*args, ks.numpy(), vs.numpy())
+    op, lp = oracle.split_partials(*args, 7, dtype="bf16", max_seq_len=100,
+                                   kv_dtype="int8", k_scale=ks.numpy(),
+                                   v_scale=vs.numpy())
+    out, lse = oracle.combine_partials(op, lp)
+    assert np.allclose(out, ref[0], atol=1e-13)
+    assert np.allclose(lse, ref[1], atol=1e-13)
+
+
+INT8_MUTANTS = ["unsigned", "sign_magnitude", "scale_shift", "scale_swap",
+                "scale_first_position", "scale_ignores_table"]
+
+
+@pytest.mark.parametrize("kind", INT8_MUTANTS)
+def test_int8_planted_mistake_is_caught(kind, monkeypatch):
+    real_rows = oa.scale_rows
+    if kind == "unsigned":
+        monkeypatch.setattr(oa, "int8_to_f64", lambda c: np.asarray(
+            c).view(np.uint8).astype(np.float64))
+    elif kind == "sign_magnitude":
+        def sm(c):
+            u = np.asarray(c).view(np.uint8).astype(np.int64)
+            return np.where(u & 0x80, -(u & 0x7F), u).astype(np.float64)
+        monkeypatch.setattr(oa, "int8_to_f64", sm)
+    elif kind == "scale_shift":
+        def shifted(scale, b, kvh, lo, hi, block_table=None, block_size=0):
+            sc = np.asarray(scale, dtype=np.float64)
+            if sc.ndim == 1:
+                return real_rows(scale, b, kvh, lo, hi, block_table,
+                                 block_size)
+            rolled = np.roll(sc, 1, axis=-1)
+            return real_rows(rolled, b, kvh, lo, hi, block_table, block_size)
+        monkeypatch.setattr(oa, "scale_rows", shifted)
+    elif kind == "scale_first_position":
+        def first(scale, b, kvh, lo, hi, block_table=None, block_size=0):
+            r = real_rows(scale, b, kvh, lo, hi, block_table, block_size)
+            return np.full_like(r, r[0, 0])
+        monkeypatch.setattr(oa, "scale_rows", first)
+    elif kind == "scale_ignores_table":
+        def flat(scale, b, kvh, lo, hi, block_table=None, block_size=0):
+            sc = np.asarray(scale, dtype=np.float64)
+            if sc.ndim == 3 and block_table is not None:
+                rows = sc.reshape(-1, sc.shape[1], 1)
+                return rows[lo:hi, kvh] if hi <= rows.shape[0] else \
+                    real_rows(scale, b, kvh, lo, hi, None, 0)
+            return real_rows(scale, b, kvh, lo, hi, block_table, block_size)
+        monkeypatch.setattr(oa, "scale_rows", flat)
+
+    def attn(q, k, v, lens, ks, vs, block_table=None, block_size=0):
+        if kind == "scale_swap":
+            ks, vs = vs, ks
+        return _attn_i8(q, k, v, lens, ks, vs, block_table, block_size)
+
+    failed = []
+    for chk in (check_int8_sdpa, check_int8_equals_bf16_of_same_values,
+                check_int8_paged_equals_contiguous):
+        try:
+            with np.errstate(all="ignore"):
+                chk(attn)
+        except (AssertionError, IndexError, ValueError):
+            failed.append(chk.__name__)
+    if kind in ("unsigned", "sign_magnitude"):
+        try:
+            test_int8_decode_hand_values()
+        except AssertionError:
+            failed.append("hand_values")
+    assert failed, f"mutant {kind} passed every int8 pin"

@@ -27,6 +27,8 @@ F32 = "f32"
 BF16 = "bf16"
 FP8 = "fp8_e4m3"
 FP8_MAX = 448.0   # largest finite E4M3 magnitude
+INT8 = "int8"
+INT8_MAX = 127.0
 
 # name -> recipe. seed = workload id.
 SPECS = {
@@ -51,6 +53,13 @@ SPECS = {
         wid=2, batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
         max_seq_len=65536, dtype=BF16, kv_dtype=FP8, scale=None,
         paged=False),
+    # The same history in an 8-bit integer cache with one scale per
+    # (position, kv head): each row of K and V divided by amax/127 and
+    # rounded to the nearest integer.
+    "long_gqa_64k_int8": dict(
+        wid=2, batch=1, num_q_heads=16, num_kv_heads=2, head_dim=128,
+        max_seq_len=65536, dtype=BF16, kv_dtype=INT8, scale=None,
+        paged=False),
     # Needle-in-a-haystack structure (the retrieval-style long-context
     # evaluations the "Faster Than Flash" page cites): haystack keys scaled
     # so logits have std ~0.3, and in every 512-token chunk one 16-token
@@ -74,7 +83,7 @@ SPECS = {
 ORDER = ["tiny_mha", "long_gqa_64k", "ultra_long_256k", "ragged_paged",
          "short_batch"]
 # Further measured workloads (variants of the above).
-EXTRA = ["long_gqa_64k_fp8"]
+EXTRA = ["long_gqa_64k_fp8", "long_gqa_64k_int8"]
 
 
 @dataclasses.dataclass
@@ -103,7 +112,9 @@ class Workload:
     block_table: Optional[torch.Tensor]
     hot_positions: Optional[torch.Tensor] = None   # [B, Hkv, n_hot]
     kv_dtype: Optional[str] = None                 # None: same as dtype
-    k_scale: Optional[torch.Tensor] = None         # fp32 [Hkv] (E4M3 cache)
+    # Quantized caches: fp32 [Hkv] (E4M3), or one per (position, kv head)
+    # in the cache's row layout, [B, Hkv, L] or [NB, Hkv, bs] (int8).
+    k_scale: Optional[torch.Tensor] = None
     v_scale: Optional[torch.Tensor] = None
 
     @property
@@ -130,13 +141,15 @@ class Workload:
         return int(self.seq_lens.to(torch.int64).sum())
 
     def kv_bytes(self) -> int:
-        """K+V bytes the call must read: every attended row, once."""
-        esz = {F32: 4, BF16: 2, FP8: 1}[self.cache_dtype]
-        return self.sum_seq_len() * self.num_kv_heads * 2 * self.head_dim * esz
+        """K+V bytes the call must read: every attended row, once (with its
+        two fp32 scales for an int8 cache)."""
+        esz = {F32: 4, BF16: 2, FP8: 1, INT8: 1}[self.cache_dtype]
+        row = 2 * self.head_dim * esz + (8 if self.cache_dtype == INT8 else 0)
+        return self.sum_seq_len() * self.num_kv_heads * row
 
     def numpy_view(self) -> dict:
         """Raw arrays for the oracle: bf16 as uint16 bit patterns, E4M3 as
-        uint8 codes, f32 as is."""
+        uint8 codes, int8 and f32 as they are."""
         def raw(t):
             if t.dtype == torch.bfloat16:
                 return t.view(torch.int16).numpy().view(np.uint16)
@@ -203,7 +216,12 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
       bf16 rounding).
     kv_dtype: "fp8_e4m3" stores K and V as 8-bit E4M3 codes: per kv head,
       scale = amax / 448 over that head's whole pool (fp32), codes =
-      E4M3(x / scale) rounded by torch; q stays bf16.
+      E4M3(x / scale) rounded by torch; q stays bf16. "int8" stores them as
+      8-bit integers with one fp32 scale per (position, kv head): scale =
+      amax / 127 over the row's head_dim values (1 for an all-zero row),
+      codes = round(x / scale) (torch, ties to even), q bf16. With
+      poison_tail an int8 cache's unattended slots get code 127 and scale
+      NaN.
     """
     spec = dict(SPECS.get(name, {}))
     wid = spec.get("wid", 0)
@@ -215,7 +233,7 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
     L = max_seq_len if max_seq_len is not None else spec.get("max_seq_len", 512)
     dt = dtype or spec.get("dtype", BF16)
     kvd = kv_dtype or spec.get("kv_dtype")
-    assert kvd in (None, FP8) and (kvd is None or dt == BF16)
+    assert kvd in (None, FP8, INT8) and (kvd is None or dt == BF16)
     sc = spec.get("scale") if scale == "spec" else scale
     pg = spec.get("paged", False) if paged is None else paged
     bs = (spec.get("block_size", block_size) if pg else 0)
@@ -317,11 +335,44 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
             return (x / sc[None, :, None, None]).to(torch.float8_e4m3fn), sc
         k, ks = quant(k32)
         v, vs = quant(v32)
+    elif kvd == INT8:
+        def quant(x):
+            amax = x.abs().amax(dim=-1)
+            sc = torch.where(amax > 0, amax / INT8_MAX, torch.ones_like(amax))
+            sc = sc.to(torch.float32)
+            c = torch.round(x / sc[..., None]).clamp(-INT8_MAX, INT8_MAX)
+            return c.to(torch.int8), sc
+        k, ks = quant(k32)
+        v, vs = quant(v32)
     else:
         k = _cast(k32, dt)
         v = _cast(v32, dt)
 
-    if poison_tail:
+    if poison_tail and kvd == INT8:
+        # No NaN code: the codes get 127 and the scales NaN instead.
+        nan = float("nan")
+        if pg:
+            used = torch.zeros(k.shape[0], dtype=torch.bool)
+            for b in range(B):
+                n = int(lens[b])
+                nb = (n + bs - 1) // bs
+                for j in range(nb):
+                    used[int(bt[b, j])] = True
+                if n % bs:
+                    last = int(bt[b, nb - 1])
+                    for t, st in ((k, ks), (v, vs)):
+                        t[last, :, n % bs:] = 127
+                        st[last, :, n % bs:] = nan
+            for t, st in ((k, ks), (v, vs)):
+                t[~used] = 127
+                st[~used] = nan
+        else:
+            for b in range(B):
+                n = int(lens[b])
+                for t, st in ((k, ks), (v, vs)):
+                    t[b, :, n:] = 127
+                    st[b, :, n:] = nan
+    elif poison_tail:
         nan = float("nan")
         if kvd == FP8:     # poison through the byte view (0x7F is NaN)
             k = k.view(torch.uint8).to(torch.float32)
@@ -354,7 +405,9 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
                     head_dim=D, max_seq_len=L, dtype=dt, scale=sc,
                     block_size=bs, q=q.contiguous(), k=k.contiguous(),
                     v=v.contiguous(), seq_lens=lens, block_table=bt,
-                    hot_positions=hot, kv_dtype=kvd, k_scale=ks, v_scale=vs)
+                    hot_positions=hot, kv_dtype=kvd,
+                    k_scale=None if ks is None else ks.contiguous(),
+                    v_scale=None if vs is None else vs.contiguous())
 
 
 def to_contiguous(w: Workload) -> Workload:
@@ -364,6 +417,9 @@ def to_contiguous(w: Workload) -> Workload:
                         w.block_size)
     k = torch.zeros(B, Hkv, L, D, dtype=w.k.dtype)
     v = torch.zeros(B, Hkv, L, D, dtype=w.v.dtype)
+    rows = w.k_scale is not None and w.k_scale.dim() == 3
+    ks = torch.zeros(B, Hkv, L) if rows else w.k_scale
+    vs = torch.zeros(B, Hkv, L) if rows else w.v_scale
     for b in range(B):
         n = int(w.seq_lens[b])
         for j in range((n + bs - 1) // bs):
@@ -371,5 +427,9 @@ def to_contiguous(w: Workload) -> Workload:
             t0, t1 = j * bs, min((j + 1) * bs, n)
             k[b, :, t0:t1] = w.k[blk, :, :t1 - t0]
             v[b, :, t0:t1] = w.v[blk, :, :t1 - t0]
+            if rows:
+                ks[b, :, t0:t1] = w.k_scale[blk, :, :t1 - t0]
+                vs[b, :, t0:t1] = w.v_scale[blk, :, :t1 - t0]
     return dataclasses.replace(w, name=w.name + "/contig", k=k, v=v,
-                               block_size=0, block_table=None)
+                               block_size=0, block_table=None, k_scale=ks,
+                               v_scale=vs)
