@@ -139,9 +139,17 @@ class Bench:
         self.bt = None if w.block_table is None else w.block_table.to(dev)
         self.ks = [w.k.to(dev) for _ in range(self.R)]
         self.vs = [w.v.to(dev) for _ in range(self.R)]
-        self.fp8 = w.cache_dtype == "fp8_e4m3"
-        self.kscale = None if w.k_scale is None else w.k_scale.to(dev)
-        self.vscale = None if w.v_scale is None else w.v_scale.to(dev)
+        # 8-bit caches: their calls and scales (one per kv head for E4M3,
+        # rotated with the codes when there is one per position, int8).
+        self.q8 = {"fp8_e4m3": (fb.fd_decode_attn_fp8,
+                                fb.fd_decode_partials_fp8),
+                   "int8": (fb.fd_decode_attn_int8,
+                            fb.fd_decode_partials_int8)}.get(w.cache_dtype)
+        nsc = self.R if w.k_scale is not None and w.k_scale.dim() > 1 else 1
+        self.kscales = ([None] if w.k_scale is None else
+                        [w.k_scale.to(dev) for _ in range(nsc)])
+        self.vscales = ([None] if w.v_scale is None else
+                        [w.v_scale.to(dev) for _ in range(nsc)])
         B, Hq, D = w.batch, w.num_q_heads, w.head_dim
         self.out = torch.empty(B, Hq, D, device=dev)
         self.lse = torch.empty(B, Hq, device=dev)
@@ -155,13 +163,16 @@ class Bench:
                              4 * w.batch * -(-w.max_seq_len // w.block_size)))
         self.bytes_split = kv + B * Hq * D * esz   # K/V + q, per split launch
 
+    def scales(self, r):
+        return (self.kscales[r % len(self.kscales)],
+                self.vscales[r % len(self.vscales)])
+
     def step(self, i):
         r = i % self.R
-        if self.fp8:
-            self.fb.fd_decode_attn_fp8(self.shape, self.q, self.ks[r],
-                                       self.vs[r], self.kscale, self.vscale,
-                                       self.bt, self.lens, self.S, self.ws,
-                                       self.out, self.lse)
+        if self.q8:
+            self.q8[0](self.shape, self.q, self.ks[r], self.vs[r],
+                       *self.scales(r), self.bt, self.lens, self.S, self.ws,
+                       self.out, self.lse)
         else:
             self.fb.fd_decode_attn(self.shape, self.q, self.ks[r], self.vs[r],
                                    self.bt, self.lens, self.S, self.ws,
@@ -169,11 +180,10 @@ class Bench:
 
     def split_only(self, i):
         r = i % self.R
-        if self.fp8:
-            self.fb.fd_decode_partials_fp8(self.shape, self.q, self.ks[r],
-                                           self.vs[r], self.kscale,
-                                           self.vscale, self.bt, self.lens,
-                                           self.S, self.op, self.lp)
+        if self.q8:
+            self.q8[1](self.shape, self.q, self.ks[r], self.vs[r],
+                       *self.scales(r), self.bt, self.lens, self.S, self.op,
+                       self.lp)
         else:
             self.fb.fd_decode_partials(self.shape, self.q, self.ks[r],
                                        self.vs[r], self.bt, self.lens, self.S,

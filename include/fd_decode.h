@@ -60,11 +60,15 @@ typedef enum fd_status {
 typedef enum fd_dtype {
   FD_DTYPE_F32 = 0,         /* q, k, v are IEEE float32 */
   FD_DTYPE_BF16 = 1,        /* q, k, v are bfloat16; math in fp32 */
-  FD_DTYPE_FP8_E4M3 = 2     /* q bfloat16; k, v 8-bit E4M3 codes (OCP 8-bit
+  FD_DTYPE_FP8_E4M3 = 2,    /* q bfloat16; k, v 8-bit E4M3 codes (OCP 8-bit
                                float: sign, 4-bit exponent with bias 7,
                                3-bit mantissa, no infinities) with one fp32
                                scale per kv head for K and one for V; only
                                the *_fp8 entry points take it */
+  FD_DTYPE_INT8 = 3         /* q bfloat16; k, v 8-bit two's-complement
+                               integers with one fp32 scale per (position,
+                               kv head) for K and one for V; only the *_int8
+                               entry points take it */
 } fd_dtype;
 
 /*
@@ -159,8 +163,9 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
                    const int32_t* seq_lens, int num_splits, void* workspace,
                    size_t workspace_bytes, float* out, float* lse_out,
                    void* stream);
-/* (shape->dtype FD_DTYPE_FP8_E4M3 is rejected here with
- * FD_ERR_INVALID_ARG: such a cache needs its scales, fd_decode_attn_fp8.) */
+/* (shape->dtype FD_DTYPE_FP8_E4M3 or FD_DTYPE_INT8 is rejected here with
+ * FD_ERR_INVALID_ARG: such a cache needs its scales, fd_decode_attn_fp8 or
+ * fd_decode_attn_int8.) */
 
 /*
  * The split step alone: per split s, the partial output of attention over
@@ -212,6 +217,44 @@ int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
                            const int32_t* block_table,
                            const int32_t* seq_lens, int num_splits,
                            float* o_part, float* lse_part, void* stream);
+
+/*
+ * Decode attention over an 8-bit integer cache (shape->dtype must be
+ * FD_DTYPE_INT8) with one scale per cached position and kv head: the key
+ * at position i of sequence b, kv head g is code * k_scale[row], the value
+ * code * v_scale[row], where row is that position's row in the cache
+ * layout, and the result is the attention above over those dequantized
+ * values, in fp32 (the same fixed cache precision as fd_decode_attn_fp8,
+ * with a finer scale). Per position this reads 2 * head_dim code bytes and
+ * 8 scale bytes per kv head.
+ *
+ *   q                 device bf16 [batch, Hq, head_dim], 16-byte aligned
+ *   k_cache, v_cache  device int8 codes (two's complement), layouts as for
+ *                     fd_decode_attn (one byte per element), 16-byte
+ *                     aligned
+ *   k_scale, v_scale  device fp32, the cache layout without head_dim:
+ *                     contiguous [batch, Hkv, max_seq_len], paged
+ *                     [num_blocks, Hkv, block_size]; 4-byte aligned. Only
+ *                     the scales of attended positions are used (others
+ *                     may hold anything, NaN included).
+ * Other arguments, outputs and errors as for fd_decode_attn.
+ */
+int fd_decode_attn_int8(const fd_shape* shape, const void* q,
+                        const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        int num_splits, void* workspace,
+                        size_t workspace_bytes, float* out, float* lse_out,
+                        void* stream);
+
+/* The split step alone over an 8-bit integer cache: as fd_decode_partials,
+ * with the cache and scales of fd_decode_attn_int8. */
+int fd_decode_partials_int8(const fd_shape* shape, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table,
+                            const int32_t* seq_lens, int num_splits,
+                            float* o_part, float* lse_part, void* stream);
 
 /*
  * Block-sparse decode ("Faster Than Flash: Exploiting Attention Sparsity

@@ -28,10 +28,10 @@ def shape_for(q, k_cache, seq_lens, block_table=None, max_seq_len=None,
         L = max_seq_len if max_seq_len is not None else maxb * bs
     if max_seq_len is not None:
         L = max_seq_len
-    if k_cache.dtype == torch.float8_e4m3fn:
+    if k_cache.dtype in (torch.float8_e4m3fn, torch.int8):
         if q.dtype != torch.bfloat16:
-            raise ValueError("an E4M3 cache takes a bf16 query")
-        dt = "fp8_e4m3"
+            raise ValueError("an 8-bit cache takes a bf16 query")
+        dt = "fp8_e4m3" if k_cache.dtype == torch.float8_e4m3fn else "int8"
     else:
         if k_cache.dtype != q.dtype or q.dtype not in (torch.bfloat16,
                                                        torch.float32):
@@ -47,7 +47,9 @@ def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
                      k_scale=None, v_scale=None):
     """out[b, h] = softmax attention of q[b, h] over the first seq_lens[b]
     cached positions (fp32). Tensors must be on the current GPU. An E4M3
-    cache (torch.float8_e4m3fn) needs k_scale / v_scale (fp32 [Hkv])."""
+    cache (torch.float8_e4m3fn) needs k_scale / v_scale (fp32 [Hkv]); an
+    int8 cache needs them per (position, kv head), laid out like the cache
+    without head_dim."""
     import torch
     from . import binding
     if v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
@@ -61,12 +63,14 @@ def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
     nbytes = binding.fd_workspace_size(shape, num_splits)
     ws = (torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
           if nbytes else None)
-    if k_cache.dtype == torch.float8_e4m3fn:
+    if k_cache.dtype in (torch.float8_e4m3fn, torch.int8):
         if k_scale is None or v_scale is None:
-            raise ValueError("an E4M3 cache needs k_scale and v_scale")
-        binding.fd_decode_attn_fp8(shape, q, k_cache, v_cache, k_scale,
-                                   v_scale, block_table, seq_lens,
-                                   num_splits, ws, out, lse)
+            raise ValueError("an 8-bit cache needs k_scale and v_scale")
+        call = (binding.fd_decode_attn_fp8
+                if k_cache.dtype == torch.float8_e4m3fn
+                else binding.fd_decode_attn_int8)
+        call(shape, q, k_cache, v_cache, k_scale, v_scale, block_table,
+             seq_lens, num_splits, ws, out, lse)
     else:
         binding.fd_decode_attn(shape, q, k_cache, v_cache, block_table,
                                seq_lens, num_splits, ws, out, lse)

@@ -23,12 +23,14 @@ FD_ERR_HIP = -4
 FD_DTYPE_F32 = 0
 FD_DTYPE_BF16 = 1
 FD_DTYPE_FP8_E4M3 = 2
+FD_DTYPE_INT8 = 3
 _DTYPES = {"f32": FD_DTYPE_F32, "bf16": FD_DTYPE_BF16,
-           "fp8_e4m3": FD_DTYPE_FP8_E4M3}
+           "fp8_e4m3": FD_DTYPE_FP8_E4M3, "int8": FD_DTYPE_INT8}
 
 SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_decode_attn",
            "fd_decode_partials", "fd_decode_attn_fp8",
-           "fd_decode_partials_fp8", "fd_build_key_summary",
+           "fd_decode_partials_fp8", "fd_decode_attn_int8",
+           "fd_decode_partials_int8", "fd_build_key_summary",
            "fd_decode_attn_sparse", "fd_combine_partials", "fd_status_str",
            "fd_version"]
 
@@ -76,6 +78,10 @@ def load() -> ctypes.CDLL:
                                        P, P]
     lib.fd_decode_partials_fp8.argtypes = [SH, P, P, P, P, P, P, P, I, P, P,
                                            P]
+    lib.fd_decode_attn_int8.argtypes = [SH, P, P, P, P, P, P, P, I, P, SZ, P,
+                                        P, P]
+    lib.fd_decode_partials_int8.argtypes = [SH, P, P, P, P, P, P, P, I, P, P,
+                                            P]
     lib.fd_build_key_summary.argtypes = [SH, P, P, P, P, P, P]
     lib.fd_decode_attn_sparse.argtypes = [SH, P, P, P, P, P, P, P,
                                           ctypes.c_float, I, P, SZ, P, P, P,
@@ -184,6 +190,32 @@ def fd_decode_partials_fp8(shape: FdShape, q, k_cache, v_cache, k_scale,
                            v_scale, block_table, seq_lens, num_splits: int,
                            o_part, lse_part, stream=None) -> None:
     _check("fd_decode_partials_fp8", load().fd_decode_partials_fp8(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+        int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(stream)))
+
+
+def fd_decode_attn_int8(shape: FdShape, q, k_cache, v_cache, k_scale,
+                        v_scale, block_table, seq_lens, num_splits: int,
+                        workspace, out, lse_out=None, stream=None,
+                        workspace_bytes: Optional[int] = None) -> None:
+    """Enqueue decode attention over an int8 cache with one fp32 scale per
+    (position, kv head) (shape dtype "int8", q bf16; scales laid out like
+    the cache without head_dim)."""
+    ws_bytes = (workspace_bytes if workspace_bytes is not None else
+                (0 if workspace is None or isinstance(workspace, int)
+                 else workspace.numel() * workspace.element_size()))
+    _check("fd_decode_attn_int8", load().fd_decode_attn_int8(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+        int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse_out),
+        _stream(stream)))
+
+
+def fd_decode_partials_int8(shape: FdShape, q, k_cache, v_cache, k_scale,
+                            v_scale, block_table, seq_lens, num_splits: int,
+                            o_part, lse_part, stream=None) -> None:
+    _check("fd_decode_partials_int8", load().fd_decode_partials_int8(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
         int(num_splits), _ptr(o_part), _ptr(lse_part), _stream(stream)))

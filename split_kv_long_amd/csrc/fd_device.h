@@ -188,6 +188,20 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(unsigned w) {
   return uint2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
 }
 
+// Four 8-bit two's-complement integers (one dword, lowest byte first) ->
+// four bf16, exact: each byte converts to fp32 with sign extension (one
+// instruction per byte), and an integer of magnitude <= 128 has at most 8
+// significant bits, so the fp32's low 16 bits are zero and its high half is
+// the bf16 value; a byte permute gathers the two high halves.
+__device__ __forceinline__ uint2 s8x4_to_bf16x4(unsigned w) {
+  const float f0 = (float)(int8_t)w, f1 = (float)(int8_t)(w >> 8);
+  const float f2 = (float)(int8_t)(w >> 16), f3 = (float)(int8_t)(w >> 24);
+  return uint2{__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0),
+                                     0x07060302u),
+               __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2),
+                                     0x07060302u)};
+}
+
 }  // namespace fd
 
 #endif  // FD_DEVICE_H

@@ -28,7 +28,7 @@ int check_shape(const fd_shape* s, Shape* out) {
   if (s->head_dim <= 0 || (s->head_dim % 16) != 0) return FD_ERR_INVALID_ARG;
   if (s->head_dim != 64 && s->head_dim != 128) return FD_ERR_UNSUPPORTED;
   if (s->dtype != FD_DTYPE_F32 && s->dtype != FD_DTYPE_BF16 &&
-      s->dtype != FD_DTYPE_FP8_E4M3)
+      s->dtype != FD_DTYPE_FP8_E4M3 && s->dtype != FD_DTYPE_INT8)
     return FD_ERR_UNSUPPORTED;
   if (!isfinite(s->scale)) return FD_ERR_INVALID_ARG;
   if (s->batch > 65535) return FD_ERR_UNSUPPORTED;       // grid y
@@ -113,11 +113,15 @@ static int check_inputs(const Shape& s, const void* q, const void* k,
   return FD_OK;
 }
 
-// E4M3 caches come with their scales and only through the *_fp8 calls.
+// Quantized caches come with their scales and only through their own
+// calls: `scaled` is the dtype the entry point takes (FD_DTYPE_FP8_E4M3 or
+// FD_DTYPE_INT8), or -1 for the unscaled calls.
 static int check_scales(const Shape& s, const float* ks, const float* vs,
-                        bool fp8_call) {
-  if ((s.dtype == FD_DTYPE_FP8_E4M3) != fp8_call) return FD_ERR_INVALID_ARG;
-  if (!fp8_call) return FD_OK;
+                        int scaled) {
+  const bool quant =
+      s.dtype == FD_DTYPE_FP8_E4M3 || s.dtype == FD_DTYPE_INT8;
+  if (scaled < 0) return quant ? FD_ERR_INVALID_ARG : FD_OK;
+  if (s.dtype != scaled) return FD_ERR_INVALID_ARG;
   if (!ks || !vs) return FD_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(ks) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(vs) & 3u) != 0)
@@ -236,7 +240,7 @@ namespace fd {
 static int decode_attn(const fd_shape* shape, const void* q,
                        const void* k_cache, const void* v_cache,
                        const float* k_scale, const float* v_scale,
-                       bool fp8_call, const int32_t* block_table,
+                       int scaled, const int32_t* block_table,
                        const int32_t* seq_lens, int num_splits,
                        void* workspace, size_t ws_bytes, float* out,
                        float* lse_out, void* stream) {
@@ -247,7 +251,7 @@ static int decode_attn(const fd_shape* shape, const void* q,
   if (st != FD_OK) return st;
   st = check_inputs(s, q, k_cache, v_cache, block_table, seq_lens);
   if (st != FD_OK) return st;
-  st = check_scales(s, k_scale, v_scale, fp8_call);
+  st = check_scales(s, k_scale, v_scale, scaled);
   if (st != FD_OK) return st;
   if (!out || !aligned16(out)) return FD_ERR_INVALID_ARG;
   if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0)
@@ -292,7 +296,7 @@ static int decode_attn(const fd_shape* shape, const void* q,
 static int decode_partials(const fd_shape* shape, const void* q,
                            const void* k_cache, const void* v_cache,
                            const float* k_scale, const float* v_scale,
-                           bool fp8_call, const int32_t* block_table,
+                           int scaled, const int32_t* block_table,
                            const int32_t* seq_lens, int num_splits,
                            float* o_part, float* lse_part, void* stream) {
   Shape s;
@@ -302,7 +306,7 @@ static int decode_partials(const fd_shape* shape, const void* q,
   if (st != FD_OK) return st;
   st = check_inputs(s, q, k_cache, v_cache, block_table, seq_lens);
   if (st != FD_OK) return st;
-  st = check_scales(s, k_scale, v_scale, fp8_call);
+  st = check_scales(s, k_scale, v_scale, scaled);
   if (st != FD_OK) return st;
   if (!o_part || !lse_part || !aligned16(o_part) ||
       (reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0)
@@ -325,7 +329,7 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
                    const void* v_cache, const int32_t* block_table,
                    const int32_t* seq_lens, int num_splits, void* workspace,
                    size_t ws_bytes, float* out, float* lse_out, void* stream) {
-  return decode_attn(shape, q, k_cache, v_cache, nullptr, nullptr, false,
+  return decode_attn(shape, q, k_cache, v_cache, nullptr, nullptr, -1,
                      block_table, seq_lens, num_splits, workspace, ws_bytes,
                      out, lse_out, stream);
 }
@@ -336,7 +340,8 @@ int fd_decode_attn_fp8(const fd_shape* shape, const void* q,
                        const int32_t* block_table, const int32_t* seq_lens,
                        int num_splits, void* workspace, size_t ws_bytes,
                        float* out, float* lse_out, void* stream) {
-  return decode_attn(shape, q, k_cache, v_cache, k_scale, v_scale, true,
+  return decode_attn(shape, q, k_cache, v_cache, k_scale, v_scale,
+                     FD_DTYPE_FP8_E4M3,
                      block_table, seq_lens, num_splits, workspace, ws_bytes,
                      out, lse_out, stream);
 }
@@ -346,7 +351,7 @@ int fd_decode_partials(const fd_shape* shape, const void* q,
                        const int32_t* block_table, const int32_t* seq_lens,
                        int num_splits, float* o_part, float* lse_part,
                        void* stream) {
-  return decode_partials(shape, q, k_cache, v_cache, nullptr, nullptr, false,
+  return decode_partials(shape, q, k_cache, v_cache, nullptr, nullptr, -1,
                          block_table, seq_lens, num_splits, o_part, lse_part,
                          stream);
 }
@@ -357,9 +362,32 @@ int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
                            const int32_t* block_table,
                            const int32_t* seq_lens, int num_splits,
                            float* o_part, float* lse_part, void* stream) {
-  return decode_partials(shape, q, k_cache, v_cache, k_scale, v_scale, true,
+  return decode_partials(shape, q, k_cache, v_cache, k_scale, v_scale,
+                         FD_DTYPE_FP8_E4M3,
                          block_table, seq_lens, num_splits, o_part, lse_part,
                          stream);
+}
+
+int fd_decode_attn_int8(const fd_shape* shape, const void* q,
+                        const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        int num_splits, void* workspace, size_t ws_bytes,
+                        float* out, float* lse_out, void* stream) {
+  return decode_attn(shape, q, k_cache, v_cache, k_scale, v_scale,
+                     FD_DTYPE_INT8, block_table, seq_lens, num_splits,
+                     workspace, ws_bytes, out, lse_out, stream);
+}
+
+int fd_decode_partials_int8(const fd_shape* shape, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_table,
+                            const int32_t* seq_lens, int num_splits,
+                            float* o_part, float* lse_part, void* stream) {
+  return decode_partials(shape, q, k_cache, v_cache, k_scale, v_scale,
+                         FD_DTYPE_INT8, block_table, seq_lens, num_splits,
+                         o_part, lse_part, stream);
 }
 
 int fd_build_key_summary(const fd_shape* shape, const void* k_cache,

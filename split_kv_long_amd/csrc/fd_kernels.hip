@@ -10,8 +10,9 @@
 // list), so one pass over K and V suffices.
 //
 // Kernels:
-//   split_mfma<D, NW, GM, PAGED, SPEC, F8, BAL>
-//                        bf16 or 8-bit E4M3 K/V, head_dim 64/128. One
+//   split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL>
+//                        bf16, 8-bit E4M3 or int8 K/V (QM), head_dim
+//                        64/128. One
 //                        workgroup per (split, kv head x group of <= GM
 //                        query heads, sequence); NW waves share the split,
 //                        each streaming 32-token subtiles one at a time
@@ -376,26 +377,38 @@ __device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
   return pc;
 }
 
+// Cache encodings of the MFMA kernel.
+enum : int { kCacheBf16 = 0, kCacheE4M3 = 1, kCacheI8 = 2 };
+
 // Waves per SIMD the register allocation targets: two for bf16, whose
 // waves hold two subtiles of registers (the reissue schedule below), three
-// for E4M3.
+// for the 8-bit caches.
 constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
 
-// F8: the cache holds 8-bit E4M3 codes with one scale per kv head for K and
-// one for V. A lane then reads 16 bytes = 16 dims of a key row per request
-// (dims 16(j + 4c)..+15) and 8 bytes = 8 dims of a value row, converts them
-// to bf16 in registers (exact) and runs the same bf16 products; the key
-// scale is folded into the logit scale and the value scale into the final
-// normalisation. The QK contraction order is free, so Q's fragments simply
-// follow the same dim order.
-template <int D, int NW, int GM, bool PAGED, bool SPEC, bool F8,
+// 8-bit caches (QM != kCacheBf16). A lane reads 16 bytes = 16 dims of a key
+// row per request (dims 16(j + 4c)..+15) and 8 bytes = 8 dims of a value
+// row, converts them to bf16 in registers (exact for both encodings) and
+// runs the same bf16 products. The QK contraction order is free, so Q's
+// fragments simply follow the same dim order.
+//   kCacheE4M3: E4M3 codes, one scale per kv head for K and one for V; the
+//     key scale is folded into the logit scale and the value scale into the
+//     final normalisation.
+//   kCacheI8: int8 codes with one fp32 scale per (position, kv head) for K
+//     and for V, laid out like the cache rows. A lane loads the scales of
+//     the 8 positions whose scores it holds (the same rows as its value
+//     requests); the key scale multiplies each score, and the value scale
+//     multiplies each probability on its way into the PV product, while the
+//     softmax sum takes the unscaled probability.
+template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
           bool BAL = false>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(F8))))
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(QM != kCacheBf16))))
 void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
     const int32_t* __restrict__ bt, int bs, SplitArgs a) {
+  constexpr bool F8 = QM != kCacheBf16;     // one byte per element
+  constexpr bool I8 = QM == kCacheI8;
   using KT = typename std::conditional<F8, uint8_t, uint16_t>::type;
   using VT = typename std::conditional<F8, u32x2, u32x4>::type;
   const KT* __restrict__ K = static_cast<const KT*>(Kp);
@@ -465,26 +478,51 @@ void split_mfma(
     return (((size_t)blk * Hkv + kvh) * bs + (t - page * bs)) * D;
   };
 
+  // int8 cache: the per-position scales of the subtile in flight (the
+  // lane's rows 4j + e of each 16-row group, as for its value requests).
+  float ksc[8], vsc8[8];
+  const float* __restrict__ KS = I8 ? a.k_scale : nullptr;
+  const float* __restrict__ VS = I8 ? a.v_scale : nullptr;
+
   // Requests the subtile starting at t0 with every row clamped below `end`.
   // `part` selects the key requests (1), the value requests (2) or both.
   auto load_subtile = [&](int t0, int end, u32x4 (&kr)[2][KL],
                           VT (&vr)[8], int part) {
     const int last0 = min(15, end - 1 - t0);
     const int last1 = end - 1 - (t0 + 16);
-    const KT* K0 = K + group_base(t0);
-    const KT* V0 = V + group_base(t0);
+    const size_t g0 = group_base(t0);
+    const KT* K0 = K + g0;
+    const KT* V0 = V + g0;
     const KT* K1;
     const KT* V1;
+    size_t g1;
     int cap1;
     if (last1 >= 0) {
-      const size_t g1 = group_base(t0 + 16);
+      g1 = group_base(t0 + 16);
       K1 = K + g1;
       V1 = V + g1;
       cap1 = min(15, last1);
     } else {
+      g1 = g0 + (size_t)last0 * D;
       K1 = K0 + (size_t)last0 * D;
       V1 = V0 + (size_t)last0 * D;
       cap1 = 0;
+    }
+    if constexpr (I8) {
+      const size_t s0 = g0 / D, s1 = g1 / D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const size_t r0 = s0 + min(4 * j + e, last0);
+        const size_t r1 = s1 + min(4 * j + e, cap1);
+        if (part & 1) {
+          ksc[e] = __builtin_nontemporal_load(KS + r0);
+          ksc[4 + e] = __builtin_nontemporal_load(KS + r1);
+        }
+        if (part & 2) {
+          vsc8[e] = __builtin_nontemporal_load(VS + r0);
+          vsc8[4 + e] = __builtin_nontemporal_load(VS + r1);
+        }
+      }
     }
     // Element offsets (16-byte requests): bf16 K dims 8j + 32c, E4M3 K
     // dims 16j + 64c.
@@ -555,8 +593,9 @@ void split_mfma(
     len = len < 0 ? 0 : (len > L ? L : len);
     hi = min(lo + P, len);
   }
-  // Logit scale (base 2), with the key scale of a quantized cache folded in.
-  const float sl2 = F8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  // Logit scale (base 2), with an E4M3 cache's key scale folded in.
+  const float sl2 =
+      QM == kCacheE4M3 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
 
   f32x4 o[NV];
 #pragma unroll
@@ -576,12 +615,18 @@ void split_mfma(
   // bytes per request, plus the conversions), which keep the plain loop.
   constexpr bool kPipe = !F8;
 
+  // Four 8-bit codes -> four bf16 (exact).
+  auto cvt4 = [](unsigned w) -> uint2 {
+    if constexpr (I8) return s8x4_to_bf16x4(w);
+    else return e4m3x4_to_bf16x4(w);
+  };
+
   // The k-vector of QK call c for token group tg (bf16 operands).
   auto k_operand = [&](const u32x4 (&kr)[2][KL], int tg, int c) -> bf16x8 {
     if constexpr (F8) {
       const u32x4 x = kr[tg][c >> 1];
-      const uint2 p = e4m3x4_to_bf16x4(x[2 * (c & 1)]);
-      const uint2 q = e4m3x4_to_bf16x4(x[2 * (c & 1) + 1]);
+      const uint2 p = cvt4(x[2 * (c & 1)]);
+      const uint2 q = cvt4(x[2 * (c & 1) + 1]);
       return as_bf16x8(u32x4{p.x, p.y, q.x, q.y});
     } else {
       return as_bf16x8(kr[tg][c]);
@@ -602,12 +647,14 @@ void split_mfma(
     }
     float sv[8];
     float mx = -INFINITY;
+    // Per-score logit scale (an int8 cache's key scale of that position).
+    auto lscale = [&](int e) -> float { return I8 ? sl2 * ksc[e] : sl2; };
     if (t0 + 32 <= hi) {                    // every token valid (uniform)
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = sacc[tg][i] * sl2;
+          const float x = sacc[tg][i] * lscale(4 * tg + i);
           sv[4 * tg + i] = x;
           mx = fmaxf(mx, x);
         }
@@ -617,9 +664,13 @@ void split_mfma(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tok = t0 + 16 * tg + 4 * j + i;
-          const float x = tok < hi ? sacc[tg][i] * sl2 : -INFINITY;
+          const float x =
+              tok < hi ? sacc[tg][i] * lscale(4 * tg + i) : -INFINITY;
           sv[4 * tg + i] = x;
           mx = fmaxf(mx, x);
+          // A masked position's value scale may be anything (even NaN):
+          // its probability is 0 and must stay 0.
+          if constexpr (I8) vsc8[4 * tg + i] = tok < hi ? vsc8[4 * tg + i] : 0.f;
         }
     }
     mx = max_x32(max_x16(mx));
@@ -643,9 +694,10 @@ void split_mfma(
     for (int e = 0; e < 8; ++e) {
       const float p = fexp2(sv[e] - mref);
       psum += p;
-      const __bf16 hb = (__bf16)p;
+      const float pw = I8 ? p * vsc8[e] : p;   // weight of value row e
+      const __bf16 hb = (__bf16)pw;
       ph[e] = hb;
-      pl[e] = (__bf16)(p - (float)hb);
+      pl[e] = (__bf16)(pw - (float)hb);
     }
     l_run = l_run * alpha + psum;
     if constexpr (kPipe) {
@@ -664,8 +716,8 @@ void split_mfma(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if constexpr (F8) {
-        const uint2 p = e4m3x4_to_bf16x4(vraw[e][0]);
-        const uint2 q = e4m3x4_to_bf16x4(vraw[e][1]);
+        const uint2 p = cvt4(vraw[e][0]);
+        const uint2 q = cvt4(vraw[e][1]);
         vr[e] = u32x4{p.x, p.y, q.x, q.y};
       } else {
         vr[e] = vraw[e];
@@ -749,8 +801,8 @@ void split_mfma(
   __syncthreads();
 
   // Merge: thread -> (head g, 4 dims); waves that saw no token carry m = -inf.
-  // A quantized cache's value scale multiplies the normalised output.
-  const float vsc = F8 ? a.v_scale[kvh] : 1.f;
+  // An E4M3 cache's value scale multiplies the normalised output.
+  const float vsc = QM == kCacheE4M3 ? a.v_scale[kvh] : 1.f;
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
     const int g = idx / (D / 4);
     const int d = 4 * (idx - g * (D / 4));
@@ -876,37 +928,38 @@ int split_waves(int P, bool f8) {
 // request; they fit the 14 kernel-argument dwords gfx950 preloads into SGPRs
 // at dispatch, so no wave waits on an argument load before its first
 // request (such loads queue behind other waves' K/V traffic).
-template <int D, int NW, int GM, bool PAGED, bool SPEC, bool F8,
+template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
           bool BAL = false>
 void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, F8, BAL>), grid,
+  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL>), grid,
                      dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
                      a.nhg, a.G, a.block_table, a.bs, a);
 }
 
-template <int D, bool PAGED, int GM, bool SPEC, bool F8, bool BAL = false>
+template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false>
 void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
+  constexpr bool F8 = QM != kCacheBf16;
   if (F8 && nw == 8)
-    launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
+    launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
   else
-    launch_one<D, 4, GM, PAGED, SPEC, F8, BAL>(grid, a, st);
+    launch_one<D, 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
 }
 
 // Speculative first loads pay off for a single sequence (its splits are all
 // full when the caller's bound is its length); for a batch, whose lengths
 // may differ, they could read splits that turn out empty.
-template <int D, bool PAGED, int GM, bool F8>
+template <int D, bool PAGED, int GM, int QM>
 void launch_mfma_gm(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
   if (a.B == 1)
-    launch_mfma_spec<D, PAGED, GM, true, F8>(grid, nw, a, st);
+    launch_mfma_spec<D, PAGED, GM, true, QM>(grid, nw, a, st);
   else if (a.bal_target > 0 && a.B <= 64)       // lane = sequence
-    launch_mfma_spec<D, PAGED, GM, false, F8, true>(grid, nw, a, st);
+    launch_mfma_spec<D, PAGED, GM, false, QM, true>(grid, nw, a, st);
   else
-    launch_mfma_spec<D, PAGED, GM, false, F8>(grid, nw, a, st);
+    launch_mfma_spec<D, PAGED, GM, false, QM>(grid, nw, a, st);
 }
 
-template <int D, bool PAGED, bool F8>
+template <int D, bool PAGED, int QM>
 void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const int gm = s.G <= 8 ? 8 : 16;
   a.nhg = (s.G + gm - 1) / gm;
@@ -914,22 +967,22 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   a.bal_target = a.balance_cus > 0 && a.S > 1
                      ? max(1, 2 * a.balance_cus / (s.Hkv * a.nhg)) : 0;
   const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
-  const int nw = split_waves(a.P, F8);
+  const int nw = split_waves(a.P, QM != kCacheBf16);
   if (gm == 8)
-    launch_mfma_gm<D, PAGED, 8, F8>(grid, nw, a, st);
+    launch_mfma_gm<D, PAGED, 8, QM>(grid, nw, a, st);
   else
-    launch_mfma_gm<D, PAGED, 16, F8>(grid, nw, a, st);
+    launch_mfma_gm<D, PAGED, 16, QM>(grid, nw, a, st);
 }
 
-template <bool F8>
+template <int QM>
 void launch_mfma_dtype(const Shape& s, const SplitArgs& a, hipStream_t st) {
   const bool paged = s.bs > 0;
   if (s.D == 128) {
-    if (paged) launch_mfma<128, true, F8>(s, a, st);
-    else launch_mfma<128, false, F8>(s, a, st);
+    if (paged) launch_mfma<128, true, QM>(s, a, st);
+    else launch_mfma<128, false, QM>(s, a, st);
   } else {
-    if (paged) launch_mfma<64, true, F8>(s, a, st);
-    else launch_mfma<64, false, F8>(s, a, st);
+    if (paged) launch_mfma<64, true, QM>(s, a, st);
+    else launch_mfma<64, false, QM>(s, a, st);
   }
 }
 
@@ -938,9 +991,11 @@ void launch_mfma_dtype(const Shape& s, const SplitArgs& a, hipStream_t st) {
 int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.dtype == FD_DTYPE_BF16) {
-    launch_mfma_dtype<false>(s, a, st);
+    launch_mfma_dtype<kCacheBf16>(s, a, st);
   } else if (s.dtype == FD_DTYPE_FP8_E4M3) {
-    launch_mfma_dtype<true>(s, a, st);
+    launch_mfma_dtype<kCacheE4M3>(s, a, st);
+  } else if (s.dtype == FD_DTYPE_INT8) {
+    launch_mfma_dtype<kCacheI8>(s, a, st);
   } else {
     const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
     const dim3 block(kGenThreads);

@@ -309,6 +309,54 @@ def test_32bit_index_limits_are_enforced():
     assert fb.fd_workspace_size(shp(max_seq_len=2 ** 30), 3) > 0
 
 
+def call_int8(partials=False, **kw):
+    lib = fb.load()
+    args = dict(shape=shp(dtype="int8"), q=FAKE, k=FAKE, v=FAKE,
+                ks=FAKE, vs=FAKE, bt=None, lens=FAKE, S=4, ws=FAKE,
+                ws_bytes=1 << 30, out=FAKE, lse=None)
+    args.update(kw)
+    if partials:
+        return lib.fd_decode_partials_int8(
+            ctypes.byref(args["shape"]), args["q"], args["k"], args["v"],
+            args["ks"], args["vs"], args["bt"], args["lens"], args["S"],
+            args["out"], FAKE, None)
+    return lib.fd_decode_attn_int8(ctypes.byref(args["shape"]), args["q"],
+                                   args["k"], args["v"], args["ks"],
+                                   args["vs"], args["bt"], args["lens"],
+                                   args["S"], args["ws"], args["ws_bytes"],
+                                   args["out"], args["lse"], None)
+
+
+@pytest.mark.parametrize("partials", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), fb.FD_ERR_INVALID_ARG),
+    (dict(vs=None), fb.FD_ERR_INVALID_ARG),
+    (dict(vs=FAKE + 2), fb.FD_ERR_INVALID_ARG),
+    (dict(shape=shp()), fb.FD_ERR_INVALID_ARG),           # bf16 shape
+    (dict(shape=shp(dtype="fp8_e4m3")), fb.FD_ERR_INVALID_ARG),
+    (dict(v=FAKE + 4), fb.FD_ERR_INVALID_ARG),
+    (dict(shape=shp(dtype="int8", head_dim=96)), fb.FD_ERR_UNSUPPORTED),
+    (dict(S=0), fb.FD_ERR_INVALID_ARG),
+])
+def test_int8_calls_are_rejected_on_the_host(kw, status, partials):
+    assert call_int8(partials, **kw) == status
+
+
+def test_int8_shape_needs_the_int8_entry_points():
+    lib = fb.load()
+    s = shp(dtype="int8")
+    assert call(shape=s) == fb.FD_ERR_INVALID_ARG
+    assert call_fp8(shape=s) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_decode_partials(ctypes.byref(s), FAKE, FAKE, FAKE, None,
+                                  FAKE, 4, FAKE, FAKE, None) == fb.FD_ERR_INVALID_ARG
+    assert call_int8(ws_bytes=100) == fb.FD_ERR_WORKSPACE
+    assert fb.fd_plan_splits(s, 256, -1) >= 1
+    assert fb.fd_workspace_size(s, 8) == fb.fd_workspace_size(shp(), 8)
+    # the sparse path takes bf16 keys only
+    assert lib.fd_build_key_summary(ctypes.byref(s), FAKE, None, FAKE, FAKE,
+                                    FAKE, None) == fb.FD_ERR_UNSUPPORTED
+
+
 def test_wrapper_rejects_mismatched_dtypes():
     import torch
     import split_kv_long_amd as fd
@@ -321,3 +369,8 @@ def test_wrapper_rejects_mismatched_dtypes():
     assert s.dtype == fb.FD_DTYPE_FP8_E4M3
     with pytest.raises(ValueError):
         fd.shape_for(q.float(), k8, torch.zeros(1, dtype=torch.int32))
+    ki = torch.zeros(1, 1, 8, 64, dtype=torch.int8)
+    assert fd.shape_for(q, ki, torch.zeros(1, dtype=torch.int32)).dtype == \
+        fb.FD_DTYPE_INT8
+    with pytest.raises(ValueError):
+        fd.shape_for(q.float(), ki, torch.zeros(1, dtype=torch.int32))

@@ -24,9 +24,10 @@ pytestmark = [
     pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
 ]
 
-# fp8_e4m3: bf16 query against an E4M3 cache, fp32 accumulation -- the
-# dequantized values are exact bf16 values, so the bf16 bar applies.
-TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3": 2e-3}
+# fp8_e4m3 / int8: bf16 query against an 8-bit cache, fp32 accumulation --
+# the codes convert exactly to bf16, and the scales add one fp32 rounding
+# per score and per probability, so the bf16 bar applies.
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8_e4m3": 2e-3, "int8": 2e-3}
 LSE_TOL = 1e-4
 LOG = os.environ.get("FD_PARITY_LOG")
 
@@ -57,10 +58,11 @@ def gpu_attention(w, S, t=None):
     nbytes = fb.fd_workspace_size(shape, S)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     print(f"[gpu] {w.name} {w.cache_dtype} S={S}", flush=True)
-    if w.cache_dtype == "fp8_e4m3":
-        fb.fd_decode_attn_fp8(shape, t["q"], t["k"], t["v"], t["ks"],
-                              t["vs"], t["bt"], t["seq_lens"], S, ws, out,
-                              lse)
+    if w.cache_dtype in ("fp8_e4m3", "int8"):
+        call = (fb.fd_decode_attn_fp8 if w.cache_dtype == "fp8_e4m3"
+                else fb.fd_decode_attn_int8)
+        call(shape, t["q"], t["k"], t["v"], t["ks"], t["vs"], t["bt"],
+             t["seq_lens"], S, ws, out, lse)
     else:
         fb.fd_decode_attn(shape, t["q"], t["k"], t["v"], t["bt"],
                           t["seq_lens"], S, ws, out, lse)
@@ -464,6 +466,138 @@ def test_fp8_paged_matches_contiguous_bitwise():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+# ------------------------------- 8-bit integer cache, per-position scales
+
+def test_int8_64k_at_planned_and_forced_splits():
+    w = workloads.make("long_gqa_64k_int8")
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    planned = fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len())
+    for S in sorted({planned, 1, 8, 64, 512}):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"int8-64k/S={S}", "int8", out, lse, ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("d", [128, 64])
+def test_int8_ragged_tails_with_poisoned_cache(paged, d):
+    """Unattended slots hold code 127 and NaN scales: any read of them that
+    reaches the arithmetic turns the output NaN."""
+    lens = [1, 15, 16, 17, 31, 33, 100, 511, 0, 257, 1000]
+    w = workloads.make("ragged_i8", seed=141, batch=len(lens),
+                       num_q_heads=16, num_kv_heads=2, head_dim=d,
+                       max_seq_len=1000, paged=paged, seq_lens=lens,
+                       poison_tail=True, kv_dtype="int8")
+    for S in (1, 3, 8, 32):
+        check(w, S)
+
+
+def test_int8_single_sequence_short_tail_poisoned():
+    # Batch one takes the speculative first requests: rows past the length
+    # are read before it is known, and their NaN scales must stay masked.
+    for L, n in ((1000, 1), (1000, 17), (4096, 4000), (700, 699)):
+        w = workloads.make("spec_i8", seed=142 + n, batch=1, num_q_heads=16,
+                           num_kv_heads=2, head_dim=128, max_seq_len=L,
+                           seq_lens=[n], poison_tail=True, kv_dtype="int8")
+        for S in (1, 4, 16):
+            check(w, S)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (12, 3, 128),
+                                      (64, 2, 128), (40, 2, 64), (4, 4, 64)])
+def test_int8_head_layouts(hq, hkv, d):
+    w = workloads.make("heads_i8", seed=143, batch=2, num_q_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, max_seq_len=2100,
+                       seq_lens=[2100, 777], kv_dtype="int8")
+    for S in (1, 5):
+        check(w, S)
+
+
+def test_int8_long_ragged_paged_batch():
+    w = workloads.make("ragged_paged", seed=144, batch=6, max_seq_len=20000,
+                       kv_dtype="int8")
+    check(w, fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len()))
+    check(w, 1)
+
+
+def test_int8_partials_entry_point():
+    w = workloads.make("ragged_paged", seed=145, batch=3, num_q_heads=16,
+                       num_kv_heads=4, head_dim=128, max_seq_len=900,
+                       min_seq_len=1, poison_tail=True, kv_dtype="int8")
+    S = 7
+    t = device_inputs(w)
+    B, Hq, D = w.batch, w.num_q_heads, w.head_dim
+    op = torch.empty(B, Hq, S, D, device="cuda")
+    lp = torch.empty(B, Hq, S, device="cuda")
+    print("[gpu] int8 partials", flush=True)
+    fb.fd_decode_partials_int8(shape_of(w), t["q"], t["k"], t["v"], t["ks"],
+                               t["vs"], t["bt"], t["seq_lens"], S, op, lp)
+    torch.cuda.synchronize()
+    a = w.numpy_view()
+    ref_op, ref_lp = oracle.split_partials(
+        a["q"], a["k"], a["v"], a["seq_lens"], S, dtype="bf16",
+        max_seq_len=900, block_table=a["block_table"],
+        block_size=a["block_size"], kv_dtype="int8",
+        k_scale=a["k_scale"], v_scale=a["v_scale"])
+    assert_parity("int8-partials", "int8",
+                  op.cpu().double().numpy().reshape(B, Hq * S, D),
+                  lp.cpu().double().numpy().reshape(B, Hq * S),
+                  ref_op.reshape(B, Hq * S, D), ref_lp.reshape(B, Hq * S))
+
+
+def test_int8_paged_matches_contiguous_bitwise():
+    w = workloads.make("ragged_paged", seed=146, batch=5, max_seq_len=3000,
+                       min_seq_len=1, kv_dtype="int8")
+    c = workloads.to_contiguous(w)
+    for S in (1, 6):
+        o1, l1 = gpu_attention(w, S)
+        o2, l2 = gpu_attention(c, S)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("bs", [32, 256])
+def test_int8_larger_page_sizes(bs):
+    lens = [1, 31, 33, 255, 257, 1000, 0, 2047]
+    w = workloads.make("pages_i8", seed=147, batch=len(lens),
+                       num_q_heads=16, num_kv_heads=2, head_dim=128,
+                       max_seq_len=2048, paged=True, block_size=bs,
+                       seq_lens=lens, poison_tail=True, kv_dtype="int8")
+    for S in (1, 3, 8):
+        check(w, S)
+
+
+def test_int8_random_shapes():
+    import random
+    rng = random.Random(2027)
+    for case in range(24):
+        hkv, g = rng.choice([1, 2, 3, 4]), rng.choice([1, 2, 4, 5, 8, 12, 16, 24])
+        b = rng.choice([1, 1, 2, 3, 5, 9])
+        L = rng.choice([1, 15, 33, 100, 257, 511, 700, 1024, 1500, 3000])
+        lens = [rng.randint(0, L) for _ in range(b)]
+        lens[rng.randrange(b)] = L
+        paged = rng.random() < 0.5
+        w = workloads.make(f"random_i8_{case}", seed=5000 + case, batch=b,
+                           num_q_heads=g * hkv, num_kv_heads=hkv,
+                           head_dim=rng.choice([64, 128]), max_seq_len=L,
+                           paged=paged,
+                           block_size=rng.choice([16, 32, 64]) if paged else 16,
+                           seq_lens=lens, poison_tail=True, kv_dtype="int8")
+        check(w, rng.choice([1, 2, 3, 4, 7, 8, 16, 33, 64]))
+
+
+def test_convenience_wrapper_int8_cache():
+    import split_kv_long_amd as fd
+    w = workloads.make("long_gqa_64k_int8", max_seq_len=5000)
+    t = device_inputs(w)
+    out, lse = fd.decode_attention(t["q"], t["k"], t["v"], t["seq_lens"],
+                                   return_lse=True, k_scale=t["ks"],
+                                   v_scale=t["vs"])
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_attention(w)
+    assert_parity("wrapper-int8", "int8", out.cpu().double().numpy(),
+                  lse.cpu().double().numpy(), ref_out, ref_lse)
+
+
 # ------------------------------------------------------------ large sizes
 
 def test_million_token_history_and_max_splits():
@@ -524,6 +658,7 @@ def test_length_aware_pieces_at_the_batch_limit(batch):
     ("long_gqa_64k", dict(max_seq_len=8192)),
     ("ragged_paged", dict(batch=6, max_seq_len=5000, min_seq_len=1)),
     ("long_gqa_64k_fp8", dict(max_seq_len=8192)),
+    ("long_gqa_64k_int8", dict(max_seq_len=8192)),
 ])
 def test_graph_replays_match_eager(name, over):
     """The calls enqueue kernels only (no allocation, no memset), so they
@@ -540,10 +675,11 @@ def test_graph_replays_match_eager(name, over):
                      dtype=torch.uint8, device="cuda")
 
     def call():
-        if w.cache_dtype == "fp8_e4m3":
-            fb.fd_decode_attn_fp8(shape, t["q"], t["k"], t["v"], t["ks"],
-                                  t["vs"], t["bt"], t["seq_lens"], S, ws, out,
-                                  lse)
+        if w.cache_dtype in ("fp8_e4m3", "int8"):
+            q8 = (fb.fd_decode_attn_fp8 if w.cache_dtype == "fp8_e4m3"
+                  else fb.fd_decode_attn_int8)
+            q8(shape, t["q"], t["k"], t["v"], t["ks"], t["vs"], t["bt"],
+               t["seq_lens"], S, ws, out, lse)
         else:
             fb.fd_decode_attn(shape, t["q"], t["k"], t["v"], t["bt"],
                               t["seq_lens"], S, ws, out, lse)
