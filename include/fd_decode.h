@@ -221,22 +221,25 @@ int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
 /*
  * Decode attention over an 8-bit integer cache (shape->dtype must be
  * FD_DTYPE_INT8) with one scale per cached position and kv head: the key
- * at position i of sequence b, kv head g is code * k_scale[row], the value
- * code * v_scale[row], where row is that position's row in the cache
- * layout, and the result is the attention above over those dequantized
- * values, in fp32 (the same fixed cache precision as fd_decode_attn_fp8,
- * with a finer scale). Per position this reads 2 * head_dim code bytes and
- * 8 scale bytes per kv head.
+ * at position i of sequence b, kv head g is code * k_scale[.., i], the
+ * value code * v_scale[.., i], and the result is the attention above over
+ * those dequantized values, in fp32 (the same fixed cache precision as
+ * fd_decode_attn_fp8, with a finer scale). Per position this reads
+ * 2 * head_dim code bytes and 8 scale bytes per kv head.
  *
  *   q                 device bf16 [batch, Hq, head_dim], 16-byte aligned
  *   k_cache, v_cache  device int8 codes (two's complement), layouts as for
  *                     fd_decode_attn (one byte per element), 16-byte
  *                     aligned
- *   k_scale, v_scale  device fp32, the cache layout without head_dim:
- *                     contiguous [batch, Hkv, max_seq_len], paged
- *                     [num_blocks, Hkv, block_size]; 4-byte aligned. Only
- *                     the scales of attended positions are used (others
- *                     may hold anything, NaN included).
+ *   k_scale, v_scale  device fp32, 16-byte aligned, one row of scales per
+ *                     (sequence or block, kv head) in whole 16-position
+ *                     groups: contiguous [batch, Hkv, Lp] with
+ *                     Lp = ceil(max_seq_len / 16) * 16 (position i of
+ *                     sequence b at [b, g, i]); paged [num_blocks, Hkv,
+ *                     block_size] (position i at [block_table[b, i / bs],
+ *                     g, i % bs]). Only the scales of attended positions
+ *                     are used; the others (the row padding included) may
+ *                     hold anything, NaN included, but must be allocated.
  * Other arguments, outputs and errors as for fd_decode_attn.
  */
 int fd_decode_attn_int8(const fd_shape* shape, const void* q,

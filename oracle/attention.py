@@ -87,8 +87,9 @@ def scale_rows(scale, b: int, kvh: int, lo: int, hi: int, block_table=None,
 
     A scale array of one value per kv head ([Hkv]) applies to every
     position. One value per (position, kv head) is laid out like the cache
-    without its last axis: [B, Hkv, L], or [NB, Hkv, bs] for a paged pool,
-    where position i sits in block block_table[b, i // bs] at slot i % bs.
+    without its last axis: [B, Hkv, L'] (any row length L' >= L; entries
+    past L are never read), or [NB, Hkv, bs] for a paged pool, where
+    position i sits in block block_table[b, i // bs] at slot i % bs.
     """
     sc = np.asarray(scale, dtype=np.float64)
     if sc.ndim == 1:

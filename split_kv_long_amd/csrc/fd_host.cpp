@@ -123,8 +123,10 @@ static int check_scales(const Shape& s, const float* ks, const float* vs,
   if (scaled < 0) return quant ? FD_ERR_INVALID_ARG : FD_OK;
   if (s.dtype != scaled) return FD_ERR_INVALID_ARG;
   if (!ks || !vs) return FD_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(ks) & 3u) != 0 ||
-      (reinterpret_cast<uintptr_t>(vs) & 3u) != 0)
+  // Per-position scales are read 4 at a time.
+  const uintptr_t align = s.dtype == FD_DTYPE_INT8 ? 15u : 3u;
+  if ((reinterpret_cast<uintptr_t>(ks) & align) != 0 ||
+      (reinterpret_cast<uintptr_t>(vs) & align) != 0)
     return FD_ERR_INVALID_ARG;
   return FD_OK;
 }

@@ -394,11 +394,13 @@ constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
 //     key scale is folded into the logit scale and the value scale into the
 //     final normalisation.
 //   kCacheI8: int8 codes with one fp32 scale per (position, kv head) for K
-//     and for V, laid out like the cache rows. A lane loads the scales of
-//     the 8 positions whose scores it holds (the same rows as its value
-//     requests); the key scale multiplies each score, and the value scale
-//     multiplies each probability on its way into the PV product, while the
-//     softmax sum takes the unscaled probability.
+//     and for V, in rows of whole 16-position groups. A lane loads the
+//     scales of the 8 positions whose scores it holds (rows 4j..4j+3 of
+//     each 16-row group: one 16-byte request per group, never past the
+//     group) without clamping; the key scale multiplies each score, and the
+//     value scale multiplies each probability on its way into the PV
+//     product, while the softmax sum takes the unscaled probability.
+//     Positions at or past the length are masked, whatever their scales.
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
           bool BAL = false>
 __global__ __launch_bounds__(NW * 64)
@@ -479,10 +481,16 @@ void split_mfma(
   };
 
   // int8 cache: the per-position scales of the subtile in flight (the
-  // lane's rows 4j + e of each 16-row group, as for its value requests).
-  float ksc[8], vsc8[8];
+  // lane's rows 4j + e of each 16-row group). Contiguous scale rows are
+  // padded to whole groups; a paged pool's pages are whole groups.
+  f32x4 ksc[2], vsc8[2];
   const float* __restrict__ KS = I8 ? a.k_scale : nullptr;
   const float* __restrict__ VS = I8 ? a.v_scale : nullptr;
+  const int Lp = (L + 15) & ~15;
+  auto scale_row = [&](size_t g, int t) -> size_t {   // g = group_base(t)
+    if (PAGED) return g / D;
+    return (size_t)(b * Hkv + kvh) * Lp + t;
+  };
 
   // Requests the subtile starting at t0 with every row clamped below `end`.
   // `part` selects the key requests (1), the value requests (2) or both.
@@ -509,19 +517,20 @@ void split_mfma(
       cap1 = 0;
     }
     if constexpr (I8) {
-      const size_t s0 = g0 / D, s1 = g1 / D;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const size_t r0 = s0 + min(4 * j + e, last0);
-        const size_t r1 = s1 + min(4 * j + e, cap1);
-        if (part & 1) {
-          ksc[e] = __builtin_nontemporal_load(KS + r0);
-          ksc[4 + e] = __builtin_nontemporal_load(KS + r1);
-        }
-        if (part & 2) {
-          vsc8[e] = __builtin_nontemporal_load(VS + r0);
-          vsc8[4 + e] = __builtin_nontemporal_load(VS + r1);
-        }
+      // A group wholly past `end` re-reads the first group's scales.
+      const size_t s0 = scale_row(g0, t0) + 4 * j;
+      const size_t s1 = last1 >= 0 ? scale_row(g1, t0 + 16) + 4 * j : s0;
+      if (part & 1) {
+        ksc[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(KS + s0));
+        ksc[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(KS + s1));
+      }
+      if (part & 2) {
+        vsc8[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(VS + s0));
+        vsc8[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(VS + s1));
       }
     }
     // Element offsets (16-byte requests): bf16 K dims 8j + 32c, E4M3 K
@@ -648,7 +657,9 @@ void split_mfma(
     float sv[8];
     float mx = -INFINITY;
     // Per-score logit scale (an int8 cache's key scale of that position).
-    auto lscale = [&](int e) -> float { return I8 ? sl2 * ksc[e] : sl2; };
+    auto lscale = [&](int e) -> float {
+      return I8 ? sl2 * ksc[e >> 2][e & 3] : sl2;
+    };
     if (t0 + 32 <= hi) {                    // every token valid (uniform)
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg)
@@ -670,7 +681,7 @@ void split_mfma(
           mx = fmaxf(mx, x);
           // A masked position's value scale may be anything (even NaN):
           // its probability is 0 and must stay 0.
-          if constexpr (I8) vsc8[4 * tg + i] = tok < hi ? vsc8[4 * tg + i] : 0.f;
+          if constexpr (I8) vsc8[tg][i] = tok < hi ? vsc8[tg][i] : 0.f;
         }
     }
     mx = max_x32(max_x16(mx));
@@ -694,7 +705,7 @@ void split_mfma(
     for (int e = 0; e < 8; ++e) {
       const float p = fexp2(sv[e] - mref);
       psum += p;
-      const float pw = I8 ? p * vsc8[e] : p;   // weight of value row e
+      const float pw = I8 ? p * vsc8[e >> 2][e & 3] : p;   // value row e
       const __bf16 hb = (__bf16)pw;
       ph[e] = hb;
       pl[e] = (__bf16)(pw - (float)hb);

@@ -332,6 +332,7 @@ def call_int8(partials=False, **kw):
     (dict(ks=None), fb.FD_ERR_INVALID_ARG),
     (dict(vs=None), fb.FD_ERR_INVALID_ARG),
     (dict(vs=FAKE + 2), fb.FD_ERR_INVALID_ARG),
+    (dict(ks=FAKE + 8), fb.FD_ERR_INVALID_ARG),       # scales: 16-byte
     (dict(shape=shp()), fb.FD_ERR_INVALID_ARG),           # bf16 shape
     (dict(shape=shp(dtype="fp8_e4m3")), fb.FD_ERR_INVALID_ARG),
     (dict(v=FAKE + 4), fb.FD_ERR_INVALID_ARG),

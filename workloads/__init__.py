@@ -113,7 +113,8 @@ class Workload:
     hot_positions: Optional[torch.Tensor] = None   # [B, Hkv, n_hot]
     kv_dtype: Optional[str] = None                 # None: same as dtype
     # Quantized caches: fp32 [Hkv] (E4M3), or one per (position, kv head)
-    # in the cache's row layout, [B, Hkv, L] or [NB, Hkv, bs] (int8).
+    # (int8): contiguous [B, Hkv, Lp] with rows padded to Lp =
+    # ceil(L / 16) * 16 (padding NaN), paged [NB, Hkv, bs].
     k_scale: Optional[torch.Tensor] = None
     v_scale: Optional[torch.Tensor] = None
 
@@ -219,7 +220,8 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
       E4M3(x / scale) rounded by torch; q stays bf16. "int8" stores them as
       8-bit integers with one fp32 scale per (position, kv head): scale =
       amax / 127 over the row's head_dim values (1 for an all-zero row),
-      codes = round(x / scale) (torch, ties to even), q bf16. With
+      codes = round(x / scale) (torch, ties to even), q bf16; contiguous
+      scale rows are padded with NaN to whole 16-position groups. With
       poison_tail an int8 cache's unattended slots get code 127 and scale
       NaN.
     """
@@ -341,6 +343,11 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
             sc = torch.where(amax > 0, amax / INT8_MAX, torch.ones_like(amax))
             sc = sc.to(torch.float32)
             c = torch.round(x / sc[..., None]).clamp(-INT8_MAX, INT8_MAX)
+            if not pg:      # scale rows padded to whole 16-position groups
+                pad = torch.full(sc.shape[:-1] + (-(-L // 16) * 16,),
+                                 float("nan"))
+                pad[..., :L] = sc
+                sc = pad
             return c.to(torch.int8), sc
         k, ks = quant(k32)
         v, vs = quant(v32)
@@ -418,8 +425,9 @@ def to_contiguous(w: Workload) -> Workload:
     k = torch.zeros(B, Hkv, L, D, dtype=w.k.dtype)
     v = torch.zeros(B, Hkv, L, D, dtype=w.v.dtype)
     rows = w.k_scale is not None and w.k_scale.dim() == 3
-    ks = torch.zeros(B, Hkv, L) if rows else w.k_scale
-    vs = torch.zeros(B, Hkv, L) if rows else w.v_scale
+    Lp = -(-L // 16) * 16
+    ks = torch.full((B, Hkv, Lp), float("nan")) if rows else w.k_scale
+    vs = torch.full((B, Hkv, Lp), float("nan")) if rows else w.v_scale
     for b in range(B):
         n = int(w.seq_lens[b])
         for j in range((n + bs - 1) // bs):
