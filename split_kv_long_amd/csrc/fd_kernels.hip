@@ -978,7 +978,13 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   a.bal_target = a.balance_cus > 0 && a.S > 1
                      ? max(1, 2 * a.balance_cus / (s.Hkv * a.nhg)) : 0;
   const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
-  const int nw = split_waves(a.P, QM != kCacheBf16);
+  // The int8 kernel with length-aware pieces (batches of 2..64) holds
+  // ~148 VGPRs, 3 waves per SIMD: with 8 waves a CU holds one of its
+  // workgroups, with 4 the two per CU the pieces are sized for (measured
+  // 5-6 % faster on the ragged batch of 16, contiguous and paged).
+  const bool pieces = a.B > 1 && a.B <= 64 && a.bal_target > 0;
+  const int nw = QM == kCacheI8 && pieces
+                     ? 4 : split_waves(a.P, QM != kCacheBf16);
   if (gm == 8)
     launch_mfma_gm<D, PAGED, 8, QM>(grid, nw, a, st);
   else
