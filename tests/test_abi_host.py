@@ -375,3 +375,39 @@ def test_wrapper_rejects_mismatched_dtypes():
         fb.FD_DTYPE_INT8
     with pytest.raises(ValueError):
         fd.shape_for(q.float(), ki, torch.zeros(1, dtype=torch.int32))
+
+
+# --------------------------------------------- the header from plain C / C++
+
+def test_header_is_strict_c99_and_cxx(tmp_path):
+    import subprocess
+    inc = os.path.join(ROOT, "include")
+    src = tmp_path / "h.c"
+    src.write_text('#include "fd_decode.h"\nint main(void) { fd_shape s;\n'
+                   '  (void)s; return FD_OK; }\n')
+    subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra",
+                    "-Werror", "-fsyntax-only", "-I", inc, str(src)],
+                   check=True)
+    cxx = tmp_path / "h.cpp"
+    cxx.write_text(src.read_text())
+    subprocess.run(["g++", "-std=c++11", "-pedantic", "-Wall", "-Wextra",
+                    "-Werror", "-fsyntax-only", "-I", inc, str(cxx)],
+                   check=True)
+
+
+def test_c_caller_links_and_runs_host_calls(tmp_path):
+    """A C program linked against the library plans, sizes and reports
+    status strings without a GPU."""
+    import subprocess
+    import __graft_entry__ as ge
+    exe = str(tmp_path / "decode_demo")
+    subprocess.run(ge.c_demo_command(ge.C_DEMO_SRC, exe), check=True)
+    r = subprocess.run([exe, "host"], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 0, r.stderr
+    lines = r.stdout.splitlines()
+    assert lines[0].startswith("splits 128 workspace ")
+    ws = fb.fd_workspace_size(shp(), 128)
+    assert lines[0] == f"splits 128 workspace {ws} version {fb.fd_version()}"
+    assert lines[1] == "status ok | " + fb.fd_status_str(fb.FD_ERR_WORKSPACE)
+    assert lines[2] == f"head_dim 96 -> {fb.FD_ERR_UNSUPPORTED}"
