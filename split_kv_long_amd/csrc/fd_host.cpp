@@ -173,7 +173,7 @@ using namespace fd;
 
 extern "C" {
 
-int fd_version(void) { return 10000; }
+int fd_version(void) { return 10100; }   // 1.1.0: int8 cache calls
 
 const char* fd_status_str(int status) {
   switch (status) {

@@ -48,8 +48,8 @@ struct SplitArgs {
   const void* v;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  const float* k_scale;   // E4M3 caches: per-kv-head scales (else null)
-  const float* v_scale;
+  const float* k_scale;   // E4M3: per-kv-head scales; int8: per-position
+  const float* v_scale;   // scales in whole 16-position rows; else null
   float* o_dst;       // out [B,Hq,D] (final) or o_part [B,Hq,S,D]
   float* lse_dst;     // lse_out [B,Hq] (final, may be null) or lse_part
   int B, Hq, Hkv, G, L;

@@ -533,7 +533,7 @@ void split_mfma(
             reinterpret_cast<const f32x4*>(VS + s1));
       }
     }
-    // Element offsets (16-byte requests): bf16 K dims 8j + 32c, E4M3 K
+    // Element offsets (16-byte requests): bf16 K dims 8j + 32c, 8-bit K
     // dims 16j + 64c.
     constexpr int KJ = F8 ? 16 : 8, KS = F8 ? 64 : 32;
     const unsigned r0 = (unsigned)(min(n, last0) * D + KJ * j);
@@ -620,8 +620,9 @@ void split_mfma(
   // are, each before the current data is used, so a wave's compute never
   // delays its next request (two subtiles of registers; two waves per
   // SIMD). Issuing the next subtile earlier, before the current one lands,
-  // measured slower; so did this schedule for E4M3 subtiles (half the
-  // bytes per request, plus the conversions), which keep the plain loop.
+  // measured slower; so did this schedule for 8-bit subtiles (half the
+  // bytes per request, plus the conversions: E4M3 6-12 %, int8 ~25 %
+  // slower at 64K), which keep the plain loop.
   constexpr bool kPipe = !F8;
 
   // Four 8-bit codes -> four bf16 (exact).
@@ -927,9 +928,10 @@ dim3 split_grid(int units, int B, int S) {
 // on MI355X: bf16 runs best with 4 waves and the reissue schedule at every
 // split length (64K, 256K, the ragged batch and the batch of 64 short
 // histories; 8 waves, or 4 waves with two subtiles requested at once, were
-// 1-4 % slower). E4M3 (64K and 256K, S = 64..256) keeps the plain loop with
-// 8 waves from 9 subtiles per split (the in-register conversion lengthens
-// the compute tail more than extra requests help).
+// 1-4 % slower). The 8-bit caches (E4M3 and int8; 64K and 256K,
+// S = 64..256) keep the plain loop with 8 waves from 9 subtiles per split
+// (the in-register conversion lengthens the compute tail more than extra
+// requests help; 16 waves were no better).
 int split_waves(int P, bool f8) {
   const int nsub = (P + 31) / 32;
   return f8 && nsub > 8 ? 8 : 4;

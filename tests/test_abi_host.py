@@ -43,7 +43,7 @@ def test_status_strings_and_version():
     for st in (-1, -2, -3, -4):
         assert fb.fd_status_str(st) and fb.fd_status_str(st) != "ok"
     assert fb.fd_status_str(7) == "unknown status"
-    assert fb.fd_version() >= 10000
+    assert fb.fd_version() >= 10100
 
 
 def shp(**kw):
