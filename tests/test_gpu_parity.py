@@ -634,6 +634,59 @@ def test_large_ragged_batch():
         assert_parity(f"bigbatch/S={S}", "bf16", out, lse, ref_out, ref_lse)
 
 
+def test_int8_million_token_history_and_max_splits():
+    """A 2^20-token int8 history (256 MB of codes + 8 MB of scales for one
+    kv head) at the planned split count and at 65535 splits."""
+    L = 1 << 20
+    w = workloads.make("million_i8", seed=191, batch=1, num_q_heads=8,
+                       num_kv_heads=1, head_dim=128, max_seq_len=L,
+                       seq_lens=[L - 3], needles=[L // 2 + 1],
+                       needle_logit=9.0, kv_dtype="int8")
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    planned = fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len())
+    for S in (planned, 65535):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"million-int8/S={S}", "int8", out, lse, ref_out,
+                      ref_lse)
+
+
+@pytest.mark.parametrize("kv", ["int8", "fp8_e4m3"])
+def test_8bit_large_ragged_batch(kv):
+    """Hundreds of ragged sequences (uniform splits, no length-aware
+    pieces above 64 sequences), paged with poisoned tails, at the planned
+    and forced split counts."""
+    g = torch.Generator().manual_seed(193)
+    lens = torch.randint(0, 700, (300,), generator=g)
+    lens[::37] = 2000
+    w = workloads.make("bigbatch8", seed=193, batch=300, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, max_seq_len=2000,
+                       seq_lens=lens.tolist(), paged=True, poison_tail=True,
+                       kv_dtype=kv)
+    ref_out, ref_lse = oracle_attention(w)
+    t = device_inputs(w)
+    planned = fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len())
+    for S in sorted({planned, 1, 4}):
+        out, lse = gpu_attention(w, S, t)
+        assert_parity(f"bigbatch8-{kv}/S={S}", kv, out, lse, ref_out,
+                      ref_lse)
+
+
+@pytest.mark.parametrize("batch", [2, 64, 65])
+def test_int8_length_aware_pieces_at_the_batch_limit(batch):
+    """int8 batches run the pieces kernel with 4 waves up to 64 sequences
+    and the uniform splits with 8 above."""
+    g = torch.Generator().manual_seed(194 + batch)
+    lens = torch.randint(1, 3000, (batch,), generator=g)
+    lens[0] = 3000
+    w = workloads.make("pieces_i8", seed=194 + batch, batch=batch,
+                       num_q_heads=32, num_kv_heads=8, head_dim=128,
+                       max_seq_len=3000, seq_lens=lens.tolist(), paged=True,
+                       poison_tail=True, kv_dtype="int8")
+    S = max(2, fb.fd_plan_splits(shape_of(w), num_cus(), w.sum_seq_len()))
+    check(w, S)
+
+
 @pytest.mark.parametrize("batch", [63, 64, 65])
 def test_length_aware_pieces_at_the_batch_limit(batch):
     """Batched calls cut sequences by their lengths when the batch fits one
