@@ -425,9 +425,25 @@ def run_one(args, name, steps, warmup, with_cpu):
         rec["copy_probe"] = copy_probe(torch)
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    rec["platform"] = platform_info(torch)
     del b
     torch.cuda.empty_cache()
     return rec
+
+
+def platform_info(torch):
+    """GPU, ROCm / HIP and torch versions the numbers were taken on."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        root = os.environ.get("ROCM_PATH", "/opt/rocm")
+        with open(os.path.join(root, ".info", "version")) as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "rocm": rocm, "hip": torch.version.hip, "torch": torch.__version__}
 
 
 FRONTIER_B = (1, 4, 16, 64, 256)

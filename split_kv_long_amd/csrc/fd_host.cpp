@@ -416,8 +416,7 @@ int fd_build_key_summary(const fd_shape* shape, const void* k_cache,
   a.bs = s.bs;
   a.max_blocks = s.max_blocks;
   a.num_blocks = s.num_blocks;
-  a.nblk_row = (s.L + 15) / 16;
-  if ((int64_t)a.nblk_row > INT32_MAX - 1) return FD_ERR_UNSUPPORTED;
+  a.nblk_row = (int)(((int64_t)s.L + 15) / 16);   // L may be INT32_MAX
   return launch_summary(s, a, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
@@ -459,7 +458,7 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
   sp.scales = scales;
   sp.kept_out = kept_out;
   sp.delta_log2 = (float)((double)delta * 1.4426950408889634);
-  sp.nblk_row = (s.L + 15) / 16;
+  sp.nblk_row = (int)(((int64_t)s.L + 15) / 16);
   float* o_part = static_cast<float*>(workspace);
   float* lse_part = nullptr;
   if (num_splits == 1) {
