@@ -483,9 +483,9 @@ void split_mfma(
   // int8 cache: the per-position scales of the subtile in flight (the
   // lane's rows 4j + e of each 16-row group). Contiguous scale rows are
   // padded to whole groups; a paged pool's pages are whole groups.
-  f32x4 ksc[2], vsc8[2];
-  const float* __restrict__ KS = I8 ? a.k_scale : nullptr;
-  const float* __restrict__ VS = I8 ? a.v_scale : nullptr;
+  f32x4 k_sc[2], v_sc[2];
+  const float* __restrict__ k_scales = I8 ? a.k_scale : nullptr;
+  const float* __restrict__ v_scales = I8 ? a.v_scale : nullptr;
   const int Lp = (L + 15) & ~15;
   auto scale_row = [&](size_t g, int t) -> size_t {   // g = group_base(t)
     if (PAGED) return g / D;
@@ -521,16 +521,16 @@ void split_mfma(
       const size_t s0 = scale_row(g0, t0) + 4 * j;
       const size_t s1 = last1 >= 0 ? scale_row(g1, t0 + 16) + 4 * j : s0;
       if (part & 1) {
-        ksc[0] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(KS + s0));
-        ksc[1] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(KS + s1));
+        k_sc[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(k_scales + s0));
+        k_sc[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(k_scales + s1));
       }
       if (part & 2) {
-        vsc8[0] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(VS + s0));
-        vsc8[1] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(VS + s1));
+        v_sc[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(v_scales + s0));
+        v_sc[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(v_scales + s1));
       }
     }
     // Element offsets (16-byte requests): bf16 K dims 8j + 32c, 8-bit K
@@ -659,7 +659,7 @@ void split_mfma(
     float mx = -INFINITY;
     // Per-score logit scale (an int8 cache's key scale of that position).
     auto lscale = [&](int e) -> float {
-      return I8 ? sl2 * ksc[e >> 2][e & 3] : sl2;
+      return I8 ? sl2 * k_sc[e >> 2][e & 3] : sl2;
     };
     if (t0 + 32 <= hi) {                    // every token valid (uniform)
 #pragma unroll
@@ -682,7 +682,7 @@ void split_mfma(
           mx = fmaxf(mx, x);
           // A masked position's value scale may be anything (even NaN):
           // its probability is 0 and must stay 0.
-          if constexpr (I8) vsc8[tg][i] = tok < hi ? vsc8[tg][i] : 0.f;
+          if constexpr (I8) v_sc[tg][i] = tok < hi ? v_sc[tg][i] : 0.f;
         }
     }
     mx = max_x32(max_x16(mx));
@@ -706,7 +706,7 @@ void split_mfma(
     for (int e = 0; e < 8; ++e) {
       const float p = fexp2(sv[e] - mref);
       psum += p;
-      const float pw = I8 ? p * vsc8[e >> 2][e & 3] : p;   // value row e
+      const float pw = I8 ? p * v_sc[e >> 2][e & 3] : p;   // value row e
       const __bf16 hb = (__bf16)pw;
       ph[e] = hb;
       pl[e] = (__bf16)(pw - (float)hb);
