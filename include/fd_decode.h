@@ -223,8 +223,11 @@ int fd_decode_partials_fp8(const fd_shape* shape, const void* q,
  * FD_DTYPE_INT8) with one scale per cached position and kv head: the key
  * at position i of sequence b, kv head g is code * k_scale[.., i], the
  * value code * v_scale[.., i], and the result is the attention above over
- * those dequantized values, in fp32 (the same fixed cache precision as
- * fd_decode_attn_fp8, with a finer scale). Per position this reads
+ * those dequantized values, in fp32. As for fd_decode_attn_fp8, the cache
+ * precision is an input that the comparison holds fixed (slavadubrov.com,
+ * "What is Flash-Decoding", section "Interpret the reported result"), and
+ * the cache is read in a low-bit form (the "Faster Than Flash" page,
+ * abstract); here the scale is per position. Per position this reads
  * 2 * head_dim code bytes and 8 scale bytes per kv head.
  *
  *   q                 device bf16 [batch, Hq, head_dim], 16-byte aligned
