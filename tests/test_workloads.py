@@ -73,3 +73,28 @@ def test_needles_dominate_their_head():
         top = torch.topk(logits, 4).indices.tolist()
         assert set(top[:3]) == {0, 300, 511}
         assert logits[[0, 300, 511]].min() > logits.sort().values[-4] + 25
+
+
+def test_int8_recipe():
+    """int8 caches: codes in [-127, 127], every non-zero row reaching 127
+    (scale = amax / 127), fp32 scales laid out like the rows, contiguous
+    rows padded with NaN to whole 16-position groups."""
+    import math
+    import torch
+    w = workloads.make("custom", seed=5, batch=2, num_q_heads=8,
+                       num_kv_heads=2, head_dim=64, max_seq_len=37,
+                       kv_dtype="int8")
+    assert w.k.dtype == torch.int8 and w.cache_dtype == "int8"
+    assert w.k_scale.shape == (2, 2, 48) and w.k_scale.dtype == torch.float32
+    assert torch.isnan(w.k_scale[..., 37:]).all()
+    assert torch.isfinite(w.k_scale[..., :37]).all()
+    for codes in (w.k, w.v):
+        c = codes.to(torch.int32)
+        assert int(c.abs().max()) <= 127
+        assert (c.abs().amax(dim=-1) == 127).all()
+    assert w.kv_bytes() == 2 * 37 * 2 * (2 * 64 + 8)
+    p = workloads.make("custom", seed=5, batch=2, num_q_heads=8,
+                       num_kv_heads=2, head_dim=64, max_seq_len=37,
+                       kv_dtype="int8", paged=True, block_size=16)
+    assert p.k_scale.shape == (p.k.shape[0], 2, 16)
+    assert not math.isnan(float(p.k_scale[0, 0, 0]))
