@@ -339,11 +339,14 @@ def run_one(args, name, steps, warmup, with_cpu):
     ms_loop = time_stream(torch, b.step, steps, warmup)
     warm_steps = min(steps, 50)
     ms_warm, _ = b.time_graph(lambda i: b.step(0), warm_steps, warmup)
-    ms_split, _ = b.time_graph(b.split_only, steps, warmup)
+    # The kernels alone, each the median of five replays like the call.
+    split_spread = {}
+    ms_split, _ = time_graph(torch, b.split_only, steps, warmup, replays=5,
+                             spread=split_spread)
     us_split = ms_split * 1e3 / steps
     us_comb = None
     if b.S > 1:
-        ms_c, _ = b.time_graph(b.combine_only, steps, 2)
+        ms_c, _ = time_graph(torch, b.combine_only, steps, 2, replays=5)
         us_comb = ms_c * 1e3 / steps
     w = b.w
     # Batched calls (2..64 sequences) cut sequences into length-aware pieces
@@ -407,6 +410,10 @@ def run_one(args, name, steps, warmup, with_cpu):
             "bytes_per_launch": b.bytes_split,
             "launch_us": round(us_split, 3),
             "timing": split_timing,
+            "split_only_replays_us": {
+                "min": round(split_spread["min"] * 1e3 / steps, 3),
+                "max": round(split_spread["max"] * 1e3 / steps, 3),
+                "value_is": "median of 5"},
         },
     }
     # The workload recipes that name split counts to compare (the tiny MHA
