@@ -69,6 +69,9 @@ def parse_args():
                    help="time the block-sparse path (fd_decode_attn_sparse, "
                         "top-delta with this delta) on the chosen workload "
                         "instead of the dense one")
+    p.add_argument("--frontier-kv", default="bf16",
+                   choices=["bf16", "fp8_e4m3", "int8"],
+                   help="cache encoding of the --frontier sweep")
     p.add_argument("--frontier", action="store_true",
                    help="instead of the metric: sweep batch x history x "
                         "splits (uniform lengths, 16q/2kv d128 bf16) and "
@@ -466,6 +469,8 @@ def frontier(args):
     import torch
     from split_kv_long_amd import binding as fb
     Hq, Hkv, D = 16, 2, 128
+    kvd = args.frontier_kv
+    esz = 2 if kvd == "bf16" else 1
     dev = torch.device("cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     gen = torch.Generator(device=dev)
@@ -474,17 +479,34 @@ def frontier(args):
             if B * L > FRONTIER_MAX_TOKENS:
                 continue
             gen.manual_seed(1000 * B + L // 512)
-            kv = B * Hkv * L * D * 2
+            kv = B * Hkv * L * D * esz
             R = max(1, min(args.steps, math.ceil(2 * MALL_BYTES / kv)))
             q = torch.randn(B, Hq, D, generator=gen, device=dev).to(
                 torch.bfloat16)
-            ks = [torch.randn(B, Hkv, L, D, generator=gen, device=dev).to(
-                torch.bfloat16) for _ in range(R)]
-            vs = [torch.randn(B, Hkv, L, D, generator=gen, device=dev).to(
-                torch.bfloat16) for _ in range(R)]
+
+            def cache():
+                # Timing inputs: random finite codes (E4M3 codes below 0x7E
+                # with either sign; int8 in [-127, 127]) and unit scales.
+                if kvd == "bf16":
+                    return torch.randn(B, Hkv, L, D, generator=gen,
+                                       device=dev).to(torch.bfloat16)
+                if kvd == "int8":
+                    return torch.randint(-127, 128, (B, Hkv, L, D),
+                                         generator=gen, device=dev,
+                                         dtype=torch.int8)
+                c = torch.randint(0, 0x7E, (B, Hkv, L, D), generator=gen,
+                                  device=dev, dtype=torch.int32)
+                c |= torch.randint(0, 2, c.shape, generator=gen, device=dev,
+                                   dtype=torch.int32) << 7
+                return c.to(torch.uint8).view(torch.float8_e4m3fn)
+            ks = [cache() for _ in range(R)]
+            vs = [cache() for _ in range(R)]
+            sc_shape = (Hkv,) if kvd == "fp8_e4m3" else (B, Hkv, -(-L // 16) * 16)
+            ksc = torch.ones(sc_shape, device=dev)
+            vsc = torch.ones(sc_shape, device=dev)
             lens = torch.full((B,), L, dtype=torch.int32, device=dev)
             out = torch.empty(B, Hq, D, device=dev)
-            shape = fb.make_shape(B, Hq, Hkv, D, L, "bf16")
+            shape = fb.make_shape(B, Hq, Hkv, D, L, kvd)
             planned = fb.fd_plan_splits(shape, cus, B * L)
             res = {}
             for S in sorted(set(FRONTIER_S) | {planned}):
@@ -495,13 +517,19 @@ def frontier(args):
 
                 def step(i, S=S, ws=ws):
                     r = i % R
-                    fb.fd_decode_attn(shape, q, ks[r], vs[r], None, lens, S,
-                                      ws, out)
+                    if kvd == "bf16":
+                        fb.fd_decode_attn(shape, q, ks[r], vs[r], None, lens,
+                                          S, ws, out)
+                    else:
+                        call = (fb.fd_decode_attn_int8 if kvd == "int8"
+                                else fb.fd_decode_attn_fp8)
+                        call(shape, q, ks[r], vs[r], ksc, vsc, None, lens, S,
+                             ws, out)
                 ms, _ = time_graph(torch, step, args.steps, 3)
                 res[S] = ms * 1e3 / args.steps
             best = min(res, key=res.get)
             rec = dict(batch=B, max_seq_len=L, num_q_heads=Hq,
-                       num_kv_heads=Hkv, head_dim=D, dtype="bf16",
+                       num_kv_heads=Hkv, head_dim=D, dtype=kvd,
                        kv_bytes=kv, us_per_call={str(k): round(v, 3)
                                                  for k, v in res.items()},
                        best_splits=best, planned_splits=planned,

@@ -116,9 +116,10 @@ typedef struct fd_shape {
  * a different schedule"; aiexpertsdirectory.org, operational constraints).
  * The rule here: with units = batch * num_kv_heads (times the groups of up
  * to 16 query heads), return 1 if units already cover num_cus, if L is
- * short, or if units cover half of num_cus and L is under 1024; otherwise
- * size splits so that the attended tokens spread over about num_cus
- * workgroups (twice that, for splits over 1024 tokens, when sum_seq_len
+ * short, or if L is under 1024 and units cover half of num_cus (for an
+ * 8-bit cache, 8 units); otherwise size splits so that the attended tokens
+ * spread over about num_cus workgroups (twice that for an int8 cache with
+ * 2 to 64 sequences, and for splits over 1024 tokens when sum_seq_len
  * shows a ragged batch), no split shorter than a minimum length.
  *
  *   shape        host pointer, validated as for fd_decode_attn

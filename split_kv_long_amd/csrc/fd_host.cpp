@@ -198,10 +198,14 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
   const int64_t cmin =
       s.dtype == FD_DTYPE_F32 ? kMinSplitTokensF32 : kMinSplitTokens;
   // No split when the sequences alone fill the CUs, when the history is
-  // shorter than two minimum splits, or when they fill half the CUs and
-  // the history is short (the combine then costs more than it saves).
+  // shorter than two minimum splits, or when they fill half the CUs (an
+  // 8-bit cache: a few units) and the history is short (the combine then
+  // costs more than it saves).
+  const bool q8 = s.dtype == FD_DTYPE_FP8_E4M3 || s.dtype == FD_DTYPE_INT8;
+  const bool short_batch =
+      2 * units >= num_cus || (q8 && units >= kShortHistoryUnits8);
   if (units >= num_cus || s.L < 2 * cmin ||
-      (2 * units >= num_cus && s.L < kShortHistoryTokens)) {
+      (short_batch && s.L < kShortHistoryTokens)) {
     *num_splits = 1;
     return FD_OK;
   }
@@ -213,7 +217,10 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
   // halved, so the length-aware pieces can even out about two workgroups
   // per CU. Uniform histories keep one workgroup per CU.
   const bool ragged = sum_seq_len >= 0 && sum_seq_len < (int64_t)s.B * s.L;
-  if (ragged && per > kLongSplitTokens) per = (per + 1) / 2;
+  // int8 batches of 2..64 run 4-wave pieces, about two per CU: halved at
+  // any length.
+  const bool i8_pieces = s.dtype == FD_DTYPE_INT8 && s.B > 1 && s.B <= 64;
+  if ((ragged && per > kLongSplitTokens) || i8_pieces) per = (per + 1) / 2;
   if (per < cmin) per = cmin;
   const int64_t g = s.bs > 16 ? s.bs : 16;
   per = (per + g - 1) / g * g;

@@ -17,11 +17,18 @@ namespace fd {
 // history {512..256K} x splits {1..256} (16 query / 2 kv heads, d 128,
 // bf16) and the ragged 16-sequence batch on MI355X: with these values the
 // planned split count is within a few percent of the best measured one.
+// The same sweep over 8-bit caches added two rules: below
+// kShortHistoryTokens, kShortHistoryUnits8 units already run unsplit (half
+// the bytes per position make the split pay later), and int8 batches of
+// 2..64 sequences halve their splits at any length (their 4-wave pieces
+// need about two workgroups per CU).
 constexpr int kMinSplitTokens = 128;
 constexpr int kMinSplitTokensF32 = 64;   // fp32 path: latency-bound, split finer
 constexpr int kOccupancy = 1;
 constexpr int kLongSplitTokens = 1024;
 constexpr int kShortHistoryTokens = 1024;
+constexpr int kShortHistoryUnits8 = 8;   // 8-bit caches: unsplit short
+                                         // histories from this many units
 constexpr int kMaxSplits = 65535;
 constexpr int kMaxBlockSize = 4096;
 constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves

@@ -89,6 +89,34 @@ def test_planner_regimes():
                 dtype="f32") == 1
 
 
+def test_planner_regimes_8bit():
+    # batch one: as for bf16
+    for dt in ("fp8_e4m3", "int8"):
+        assert plan(dtype=dt) == 128
+        assert plan(max_seq_len=512, dtype=dt) == 4
+    # a short history with 8 or more units runs unsplit (half the bytes per
+    # position: the split stops paying earlier than for bf16) ...
+    for dt in ("fp8_e4m3", "int8"):
+        assert plan(batch=4, max_seq_len=512, dtype=dt) == 1
+        assert plan(batch=16, max_seq_len=512, dtype=dt) == 1
+    assert plan(batch=4, max_seq_len=512) == 4              # bf16 splits
+    # ... and from 1024 positions on it splits again
+    assert plan(batch=4, max_seq_len=2048, dtype="fp8_e4m3") == 16
+    # int8 batches of 2..64 halve their splits at any length (4-wave
+    # pieces, about two per CU); E4M3 keeps the bf16 sizing
+    assert plan(batch=16, max_seq_len=262144, dtype="int8") == 16
+    assert plan(batch=16, max_seq_len=262144, dtype="fp8_e4m3") == 8
+    assert plan(batch=64, max_seq_len=32768, dtype="int8") == 4
+    assert plan(batch=64, max_seq_len=32768, dtype="fp8_e4m3") == 2
+    assert plan(batch=4, max_seq_len=131072, dtype="int8") == 64
+    # above 64 sequences the uniform splits (8 waves) keep the bf16 sizing
+    assert plan(batch=65, max_seq_len=32768, dtype="int8") == \
+        plan(batch=65, max_seq_len=32768, dtype="fp8_e4m3")
+    # a ragged int8 batch is halved once, like any ragged batch
+    ragged = dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=32768)
+    assert plan(sum_len=245263, dtype="int8", **ragged) == 9
+
+
 def test_planner_properties():
     for L in (512, 1000, 4096, 65536, 262144, 1 << 20):
         for B in (1, 2, 4, 16):
