@@ -158,8 +158,6 @@ class Bench:
         self.lse = torch.empty(B, Hq, device=dev)
         nb = fb.fd_workspace_size(self.shape, self.S)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
-        if nb:
-            fb.fd_workspace_init(self.ws)
         self.op = torch.empty(B, Hq, max(self.S, 1), D, device=dev)
         self.lp = torch.empty(B, Hq, max(self.S, 1), device=dev)
         esz = 4 if w.dtype == "f32" else 2
@@ -516,8 +514,6 @@ def frontier(args):
                     continue
                 nb = fb.fd_workspace_size(shape, S)
                 ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
-                if nb:
-                    fb.fd_workspace_init(ws)
 
                 def step(i, S=S, ws=ws):
                     r = i % R

@@ -37,8 +37,7 @@
  *     [0, max_seq_len] and block ids into [0, num_blocks) on the device so a
  *     broken call cannot read outside the buffers, but its result is
  *     meaningless.)
- *   - For fixed inputs, num_splits and device the result is bitwise
- *     reproducible (see fd_decode_attn for what the device decides).
+ *   - For fixed inputs and num_splits the result is bitwise deterministic.
  */
 #ifndef FD_DECODE_H
 #define FD_DECODE_H
@@ -135,64 +134,30 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
 
 /*
  * Bytes of device workspace fd_decode_attn needs for num_splits splits:
- * 0 when num_splits == 1; else a 256-byte header followed by room for the
- * fp32 partials (o [batch, Hq, S, head_dim] and their log-sum-exp), a
- * multiple of 256. The partials are the per-piece results the final
- * reduction merges (slavadubrov.com, "What is Flash-Decoding, and when does
- * it speed up LLMs?", section "Why decode needs a different schedule").
- * shape and bytes are host pointers; errors as for fd_plan_splits.
+ * 0 when num_splits == 1, else room for the fp32 partials
+ * o_part [batch, Hq, S, head_dim] and lse_part [batch, Hq, S] (natural log),
+ * 256-byte aligned. shape and bytes are host pointers.
  */
 int fd_workspace_size(const fd_shape* shape, int num_splits, size_t* bytes);
 
 /*
- * Prepare a workspace for fd_decode_attn and its variants: enqueues, on
- * `stream`, a kernel that writes the header (a magic word, a clear error
- * word) and fills the rest with the empty pattern (every 32-bit word
- * 0xFFFFFFFF). Call it once per workspace, before its first use: every
- * call that uses a workspace leaves it in this state again, so graph
- * replays and loops need nothing in between. (A workspace that was never
- * prepared makes a single-sequence call write NaN to its outputs and set
- * the header's error word; prepare it again after that. One call at a time
- * per workspace: calls that overlap on one workspace race.)
- *
- *   workspace  device, 16-byte aligned
- *   bytes      0 (nothing to do), or >= 256 and a multiple of 16, e.g.
- *              the largest fd_workspace_size the workspace will serve
- * Returns FD_ERR_INVALID_ARG for a null or misaligned pointer or a bad size.
- */
-int fd_workspace_init(void* workspace, size_t bytes, void* stream);
-
-/*
- * Full decode attention: per-split partials and their log-sum-exp
- * reduction (slavadubrov.com, "What is Flash-Decoding, and when does it
- * speed up LLMs?", sections "What is Flash-Decoding" and "Why decode needs
- * a different schedule"), on `stream`.
- *
- * For one sequence (batch == 1, at most 16 query heads per kv head and a
- * split count a reducer can cover) this is a single kernel launch: the last
- * splits of each kv head merge every split's partial once it lands in the
- * workspace. Otherwise the split kernel is followed by the log-sum-exp
- * combine kernel. For 2 to 64 sequences and num_splits > 1 the split kernel
- * cuts each sequence into up to num_splits equal pieces sized by its own
- * length instead of the uniform splits above (an internal choice: the
- * result is the same attention).
+ * Full decode attention: the split kernel, then (if num_splits > 1) the
+ * log-sum-exp combine kernel, on `stream`. For 2 to 64 sequences and
+ * num_splits > 1 the split kernel cuts each sequence into up to num_splits
+ * equal pieces sized by its own length instead of the uniform splits above
+ * (an internal choice: the result is the same attention, and it stays
+ * deterministic for a given device).
  *
  *   q, k_cache, v_cache  device, dtype per shape, 16-byte aligned
  *   block_table          device int32, non-NULL iff shape->block_size > 0
  *   seq_lens             device int32 [batch]
  *   num_splits           S >= 1 (e.g. from fd_plan_splits); S == 1 writes
  *                        `out` directly and needs no workspace
- *   workspace            device, >= fd_workspace_size bytes, 16-byte
- *                        aligned, prepared once by fd_workspace_init
- *                        (ignored, may be NULL, when S == 1); the call
- *                        leaves it prepared
+ *   workspace            device, >= fd_workspace_size bytes, 16-byte aligned
+ *                        (ignored, may be NULL, when S == 1). Scratch only:
+ *                        its contents on entry do not matter.
  *   out                  device fp32 [batch, Hq, head_dim], 16-byte aligned
  *   lse_out              device fp32 [batch, Hq] natural log, or NULL
- *
- * Determinism: for fixed inputs, num_splits and device the result is
- * bitwise reproducible (the piece sizes of batched calls depend on the
- * device's compute-unit count; the single-launch reduction merges splits in
- * a fixed order whatever order they finish in).
  */
 int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
                    const void* v_cache, const int32_t* block_table,

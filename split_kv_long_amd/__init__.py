@@ -10,22 +10,7 @@ from __future__ import annotations
 
 from typing import Optional
 
-__all__ = ["decode_attention", "shape_for", "make_workspace"]
-
-
-def make_workspace(shape, num_splits: int, device=None):
-    """A prepared workspace (fd_workspace_size bytes, fd_workspace_init run
-    on the current stream) for calls of this shape with up to num_splits
-    splits, or None when none is needed. Reuse it across calls: every call
-    leaves it prepared."""
-    import torch
-    from . import binding
-    nbytes = binding.fd_workspace_size(shape, num_splits)
-    if not nbytes:
-        return None
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
-    binding.fd_workspace_init(ws)
-    return ws
+__all__ = ["decode_attention", "shape_for"]
 
 
 def shape_for(q, k_cache, seq_lens, block_table=None, max_seq_len=None,
@@ -75,7 +60,9 @@ def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
         num_splits = binding.fd_plan_splits(shape, cus, -1)
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    ws = make_workspace(shape, num_splits, q.device)
+    nbytes = binding.fd_workspace_size(shape, num_splits)
+    ws = (torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+          if nbytes else None)
     if k_cache.dtype in (torch.float8_e4m3fn, torch.int8):
         if k_scale is None or v_scale is None:
             raise ValueError("an 8-bit cache needs k_scale and v_scale")

@@ -27,8 +27,7 @@ FD_DTYPE_INT8 = 3
 _DTYPES = {"f32": FD_DTYPE_F32, "bf16": FD_DTYPE_BF16,
            "fp8_e4m3": FD_DTYPE_FP8_E4M3, "int8": FD_DTYPE_INT8}
 
-SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_workspace_init",
-           "fd_decode_attn",
+SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_decode_attn",
            "fd_decode_partials", "fd_decode_attn_fp8",
            "fd_decode_partials_fp8", "fd_decode_attn_int8",
            "fd_decode_partials_int8", "fd_build_key_summary",
@@ -73,7 +72,6 @@ def load() -> ctypes.CDLL:
     SH = ctypes.POINTER(FdShape)
     lib.fd_plan_splits.argtypes = [SH, I, I64, ctypes.POINTER(I)]
     lib.fd_workspace_size.argtypes = [SH, I, ctypes.POINTER(SZ)]
-    lib.fd_workspace_init.argtypes = [P, SZ, P]
     lib.fd_decode_attn.argtypes = [SH, P, P, P, P, P, I, P, SZ, P, P, P]
     lib.fd_decode_partials.argtypes = [SH, P, P, P, P, P, I, P, P, P]
     lib.fd_decode_attn_fp8.argtypes = [SH, P, P, P, P, P, P, P, I, P, SZ, P,
@@ -148,21 +146,6 @@ def fd_workspace_size(shape: FdShape, num_splits: int) -> int:
     _check("fd_workspace_size", load().fd_workspace_size(
         ctypes.byref(shape), int(num_splits), ctypes.byref(out)))
     return out.value
-
-
-def _nbytes(t) -> int:
-    if t is None or isinstance(t, int):
-        return 0
-    return t.numel() * t.element_size()
-
-
-def fd_workspace_init(workspace, stream=None,
-                      workspace_bytes: Optional[int] = None) -> None:
-    """Enqueue the preparation of a workspace (header + empty pattern)."""
-    n = workspace_bytes if workspace_bytes is not None else _nbytes(workspace)
-    n -= n % 16
-    _check("fd_workspace_init", load().fd_workspace_init(
-        _ptr(workspace), n, _stream(stream)))
 
 
 def fd_decode_attn(shape: FdShape, q, k_cache, v_cache, block_table, seq_lens,

@@ -80,19 +80,10 @@ size_t partial_o_bytes(const Shape& s, int num_splits) {
   return round_up((size_t)s.B * s.Hq * num_splits * s.D * sizeof(float), 256);
 }
 
-// The log-sum-exp area holds either the two-launch path's lse_part
-// [B, Hq, S] or the single-launch path's records, one per (kv head, reducer
-// wave, split) with at most D / 4 reducer waves per query head: sized for
-// the larger.
-size_t partial_lse_bytes(const Shape& s, int num_splits) {
-  return round_up((size_t)s.B * s.Hq * num_splits * (s.D / 4) * sizeof(float),
-                  256);
-}
-
 size_t workspace_bytes(const Shape& s, int num_splits) {
   if (num_splits <= 1) return 0;
-  return kWsHeader + partial_o_bytes(s, num_splits) +
-         partial_lse_bytes(s, num_splits);
+  return partial_o_bytes(s, num_splits) +
+         round_up((size_t)s.B * s.Hq * num_splits * sizeof(float), 256);
 }
 
 static int check_splits(const Shape& s, int num_splits) {
@@ -182,7 +173,7 @@ using namespace fd;
 
 extern "C" {
 
-int fd_version(void) { return 10200; }   // 1.2.0: workspace init, single launch
+int fd_version(void) { return 10100; }   // 1.1.0: int8 cache calls
 
 const char* fd_status_str(int status) {
   switch (status) {
@@ -287,30 +278,19 @@ static int decode_attn(const fd_shape* shape, const void* q,
   // slots stay internal to this call, so their layout may differ from
   // fd_decode_partials' uniform splits).
   if (s.B > 1 && num_splits > 1) a.balance_cus = device_cus();
-  int fused = 0;
   if (num_splits == 1) {
     a.o_dst = out;
     a.lse_dst = lse_out;
     a.final_out = 1;
-    return launch_split(s, a, stream, &fused) == 0 ? FD_OK : FD_ERR_HIP;
+    return launch_split(s, a, stream) == 0 ? FD_OK : FD_ERR_HIP;
   }
-  char* ws = static_cast<char*>(workspace);
-  float* o_part = reinterpret_cast<float*>(ws + kWsHeader);
-  float* lse_part = reinterpret_cast<float*>(
-      ws + kWsHeader + partial_o_bytes(s, num_splits));
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             partial_o_bytes(s, num_splits));
   a.o_dst = o_part;
   a.lse_dst = lse_part;
   a.final_out = 0;
-  // One sequence: the launcher may fold the reduction into the split
-  // kernel (its records use the same two areas of the workspace).
-  a.rec = o_part;
-  a.lrec = lse_part;
-  a.ws_hdr = reinterpret_cast<unsigned*>(ws);
-  a.fin_out = out;
-  a.fin_lse = lse_out;
-  a.fuse_ok = 1;
-  if (launch_split(s, a, stream, &fused) != 0) return FD_ERR_HIP;
-  if (fused) return FD_OK;
+  if (launch_split(s, a, stream) != 0) return FD_ERR_HIP;
   CombineArgs c;
   c.o_part = o_part;
   c.lse_part = lse_part;
@@ -319,7 +299,6 @@ static int decode_attn(const fd_shape* shape, const void* q,
   c.B = s.B;
   c.Hq = s.Hq;
   c.S = num_splits;
-  c.reset = 1;
   return launch_combine(s.D, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
@@ -348,8 +327,7 @@ static int decode_partials(const fd_shape* shape, const void* q,
   a.o_dst = o_part;
   a.lse_dst = lse_part;
   a.final_out = 0;
-  int fused = 0;
-  return launch_split(s, a, stream, &fused) == 0 ? FD_OK : FD_ERR_HIP;
+  return launch_split(s, a, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
 }  // namespace fd
@@ -488,16 +466,16 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
   sp.kept_out = kept_out;
   sp.delta_log2 = (float)((double)delta * 1.4426950408889634);
   sp.nblk_row = (int)(((int64_t)s.L + 15) / 16);
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = nullptr;
   if (num_splits == 1) {
     a.o_dst = out;
     a.lse_dst = lse_out;
     a.final_out = 1;
     return launch_sparse(s, a, sp, stream) == 0 ? FD_OK : FD_ERR_HIP;
   }
-  char* ws = static_cast<char*>(workspace);
-  float* o_part = reinterpret_cast<float*>(ws + kWsHeader);
-  float* lse_part = reinterpret_cast<float*>(
-      ws + kWsHeader + partial_o_bytes(s, num_splits));
+  lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      partial_o_bytes(s, num_splits));
   a.o_dst = o_part;
   a.lse_dst = lse_part;
   a.final_out = 0;
@@ -510,7 +488,6 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
   c.B = s.B;
   c.Hq = s.Hq;
   c.S = num_splits;
-  c.reset = 1;
   return launch_combine(s.D, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
@@ -529,24 +506,14 @@ int fd_combine_partials(int batch, int num_q_heads, int head_dim,
       (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0))
     return FD_ERR_INVALID_ARG;
   CombineArgs c;
-  c.o_part = const_cast<float*>(o_part);     // read only (reset = 0)
-  c.lse_part = const_cast<float*>(lse_part);
+  c.o_part = o_part;
+  c.lse_part = lse_part;
   c.out = out;
   c.lse_out = lse_out;
   c.B = batch;
   c.Hq = num_q_heads;
   c.S = num_splits;
-  c.reset = 0;
   return launch_combine(head_dim, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
-}
-
-int fd_workspace_init(void* workspace, size_t bytes, void* stream) {
-  if (bytes == 0) return FD_OK;
-  if (!workspace || !aligned16(workspace) || bytes < kWsHeader ||
-      bytes % 16 != 0)
-    return FD_ERR_INVALID_ARG;
-  return launch_workspace_init(workspace, bytes, stream) == 0 ? FD_OK
-                                                              : FD_ERR_HIP;
 }
 
 }  // extern "C"

@@ -34,23 +34,6 @@ constexpr int kMaxBlockSize = 4096;
 constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves
 constexpr int kMaxSparseSplit = 8192;   // sparse path: tokens per split
 
-// Workspace of fd_decode_attn (num_splits > 1): a header of kWsHeader bytes
-// (word 0 holds kWsMagic once fd_workspace_init has run, word 1 a device
-// error flag), then the partial records. Between calls every partial slot
-// holds the empty pattern (all bits set, 0xFFFFFFFF per 32-bit word): each
-// call restores what it wrote.
-constexpr size_t kWsHeader = 256;
-constexpr unsigned kWsMagic = 0x53574446u;   // "FDWS"
-constexpr unsigned kWsEmpty = 0xFFFFFFFFu;   // never a computed fp32 value
-// Single-launch (fused) calls: the last workgroups of each kv head unit
-// also reduce. At most kFuseMaxWaiters reducer workgroups per call
-// (they wait on the other workgroups, never the reverse), each reducer lane
-// reads at most kFuseLaneSplits splits, and a reducer gives up after
-// kFuseSpinTicks ticks of the 100 MHz real-time counter (one second).
-constexpr int kFuseMaxWaiters = 256;
-constexpr int kFuseLaneSplits = 4;
-constexpr unsigned long long kFuseSpinTicks = 100000000ull;
-
 // A validated, resolved call shape.
 struct Shape {
   int B, Hq, Hkv, G, D, L;
@@ -64,7 +47,6 @@ int tokens_per_split(const Shape& s, int num_splits);   // P
 int head_groups(const Shape& s);                        // ceil(G / 16)
 size_t partial_o_bytes(const Shape& s, int num_splits);
 size_t workspace_bytes(const Shape& s, int num_splits);
-size_t partial_lse_bytes(const Shape& s, int num_splits);
 
 // Kernel arguments (passed by value).
 struct SplitArgs {
@@ -84,25 +66,14 @@ struct SplitArgs {
   int balance_cus;    // > 0 (CU count): length-aware pieces for batches
   int bal_target;     // set by the launcher: pieces per kv head unit
   float scale_log2;   // scale * log2(e)
-  // Single launch with the reduction in its last workgroups (fused): the
-  // launcher sets fuse_R / fuse_FW when it takes that path.
-  float* rec;         // partial records [unit][reducer wave][split][FW]
-  float* lrec;        // their base-2 log-sum-exp [unit][reducer wave][split]
-  unsigned* ws_hdr;   // workspace header (magic, error flag)
-  float* fin_out;     // the call's out / lse_out (the fused path writes them)
-  float* fin_lse;
-  int fuse_ok;        // 1: the caller allows the fused path
-  int fuse_R;         // reducer workgroups per kv head unit (0: not fused)
-  int fuse_FW;        // output floats per reducer wave (4, 8 or 16)
 };
 
 struct CombineArgs {
-  float* o_part;
-  float* lse_part;
+  const float* o_part;
+  const float* lse_part;
   float* out;
   float* lse_out;     // may be null
   int B, Hq, S;
-  int reset;          // 1: leave the partials read as the empty pattern
 };
 
 // Key summary builder (4-bit codes + per-16-token-block scales).
@@ -125,10 +96,7 @@ struct SparseArgs {
 };
 
 // Launchers (fd_kernels.hip, fd_sparse.hip). Return hipError_t as int.
-// launch_split sets *fused to 1 when it ran the single-launch path (the
-// output is then final and no combine follows).
-int launch_split(const Shape& s, const SplitArgs& a, void* stream, int* fused);
-int launch_workspace_init(void* ws, size_t bytes, void* stream);
+int launch_split(const Shape& s, const SplitArgs& a, void* stream);
 int launch_combine(int D, const CombineArgs& a, void* stream);
 int launch_summary(const Shape& s, const SummaryArgs& a, void* stream);
 int launch_sparse(const Shape& s, const SplitArgs& a, const SparseArgs& sp,

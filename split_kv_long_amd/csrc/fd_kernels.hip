@@ -377,200 +377,6 @@ __device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
   return pc;
 }
 
-// ----------------------------------------------------------------------------
-// Single-launch reduction (the combine folded into the split kernel).
-//
-// Every workgroup writes its split's partial (normalised o, base-2
-// log-sum-exp) as records with device-scope stores (cache policy sc1),
-// which go through to the device's coherence point; the last fuse_R
-// splits of each kv head unit then read every split's records of their
-// unit with device-scope loads and merge them (the log-sum-exp reduction of
-// slavadubrov.com, "Why decode needs a different schedule"). Reducers wait
-// on the other workgroups and nothing waits on a reducer; they are the
-// highest split indices, so the workgroups they wait for are dispatched
-// before them, and a call has at most kFuseMaxWaiters of them. A record
-// slot holds the empty pattern until its split's store lands, so a reducer
-// re-reads only the slots it still lacks; once merged it writes the empty
-// pattern back, which leaves the workspace ready for the next call without
-// a clearing pass. A reducer that has waited kFuseSpinTicks (one second),
-// or finds the workspace header without its magic word (never prepared by
-// fd_workspace_init), writes NaN to its outputs, sets the header's error
-// word and clears the magic, so the failure shows and persists.
-//
-// Layout per kv head unit u, F = nh * D floats per split, NWV = F / FW
-// reducer waves (NW per reducer workgroup):
-//   rec  [u][S][F] floats     lrec [u][S][NWV] (one lse copy per wave)
-// so a workgroup writes its partial as one contiguous run. Reducer wave gw
-// owns output floats [gw * FW, (gw + 1) * FW) of the unit (one head, FW
-// consecutive dims); its lane (q, sl), q < FW / 4, reads float4 q of splits
-// sl, sl + 64 / (FW / 4), ... (at most kFuseLaneSplits).
-
-constexpr int kCpolDevice = 16;            // buffer cache policy: sc1
-constexpr unsigned kBufOob = 0x80000000u;  // offset past every buffer bound
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p,
-                                                           unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0,
-                                           (int)bytes, 0x00020000);
-}
-
-template <int D>
-__device__ __forceinline__ void fuse_put(const SplitArgs& a, int u, int nh,
-                                         int s, int g, int d, f32x4 o4,
-                                         float l2) {
-  const int FW = a.fuse_FW;
-  const int F = nh * D;
-  const int f = g * D + d;
-  const unsigned row = (unsigned)(u * a.S + s);        // this split's record
-  __builtin_amdgcn_raw_buffer_store_b128(
-      __builtin_bit_cast(u32x4, o4), buf_rsrc(a.rec, 0x7FFFFFFF),
-      (row * F + f) * 4u, 0, kCpolDevice);
-  if (f % FW == 0)                                     // one copy per wave
-    __builtin_amdgcn_raw_buffer_store_b32(
-        __float_as_uint(l2), buf_rsrc(a.lrec, 0x7FFFFFFF),
-        (row * (F / FW) + f / FW) * 4u, 0, kCpolDevice);
-}
-
-// Reduction over the lane bits >= lq (the split lanes of a reducer wave):
-// DPP inside 16-lane rows, then the row exchanges.
-__device__ __forceinline__ float lanes_max(float v, int lq) {
-  if (lq == 0) v = fmaxf(v, dpp_f<0xB1>(v));
-  if (lq <= 1) v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x124>(v));
-  v = fmaxf(v, dpp_f<0x128>(v));
-  return max_x32(max_x16(v));
-}
-__device__ __forceinline__ float lanes_sum(float v, int lq) {
-  if (lq == 0) v += dpp_f<0xB1>(v);
-  if (lq <= 1) v += dpp_f<0x4E>(v);
-  v += dpp_f<0x124>(v);
-  v += dpp_f<0x128>(v);
-  return sum_x32(sum_x16(v));
-}
-
-template <int D, int NW>
-__device__ void fuse_reduce(const SplitArgs& a, int u, int nh, int s, int b,
-                            int h0) {
-  const int S = a.S, FW = a.fuse_FW;
-  const int r = s - (S - a.fuse_R);
-  if (r < 0) return;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = r * NW + w;
-  const int lq = FW == 4 ? 0 : (FW == 8 ? 1 : 2);
-  const int q = lane & ((1 << lq) - 1), sl = lane >> lq, SL = 64 >> lq;
-  const int F = nh * D, NWV = F / FW;   // floats and reducer waves per unit
-  // Slot of split sp for this lane: data at sp * F + gw * FW + 4q floats,
-  // lse copy at sp * NWV + gw.
-  const auto dr = buf_rsrc(a.rec + (size_t)u * S * F + gw * FW + 4 * q,
-                           (unsigned)(S * F * 4));
-  const auto lr = buf_rsrc(a.lrec + (size_t)u * S * NWV + gw,
-                           (unsigned)(S * NWV * 4));
-  const auto hr = buf_rsrc(a.ws_hdr, (unsigned)kWsHeader);
-  f32x4 v[kFuseLaneSplits];
-  float l[kFuseLaneSplits];
-  unsigned want = 0;
-#pragma unroll
-  for (int c = 0; c < kFuseLaneSplits; ++c) {
-    const int sp = sl + c * SL;
-    const bool ok = sp < S;
-    want |= ok ? 1u << c : 0u;
-    v[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-        dr, ok ? (unsigned)(sp * F) * 4u : kBufOob, 0, kCpolDevice));
-    l[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-        lr, ok ? (unsigned)(sp * NWV) * 4u : kBufOob, 0, kCpolDevice));
-  }
-  const unsigned magic =
-      __builtin_amdgcn_raw_buffer_load_b32(hr, 0, 0, kCpolDevice);
-  bool failed = __builtin_amdgcn_readfirstlane(magic) != kWsMagic;
-  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-  while (!failed) {
-    unsigned bad = 0;
-#pragma unroll
-    for (int c = 0; c < kFuseLaneSplits; ++c) {
-      const u32x4 x = __builtin_bit_cast(u32x4, v[c]);
-      const bool e = x[0] == kWsEmpty || x[1] == kWsEmpty ||
-                     x[2] == kWsEmpty || x[3] == kWsEmpty ||
-                     __float_as_uint(l[c]) == kWsEmpty;
-      bad |= ((want >> c) & 1u) && e ? 1u << c : 0u;
-    }
-    if (__builtin_amdgcn_ballot_w64(bad != 0) == 0) break;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kFuseSpinTicks) {
-      failed = true;
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-    // Re-read only the missing slots (an out-of-bounds offset makes the
-    // others' loads return without touching memory).
-#pragma unroll
-    for (int c = 0; c < kFuseLaneSplits; ++c) {
-      const bool m = (bad >> c) & 1u;
-      const int sp = sl + c * SL;
-      const f32x4 nv = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     dr, m ? (unsigned)(sp * F) * 4u : kBufOob, 0,
-                     kCpolDevice));
-      const float nl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          lr, m ? (unsigned)(sp * NWV) * 4u : kBufOob, 0, kCpolDevice));
-      v[c] = m ? nv : v[c];
-      l[c] = m ? nl : l[c];
-    }
-  }
-  const int f = gw * FW + 4 * q;
-  const int g = f / D, d = f - g * D;
-  float* o = a.o_dst + ((size_t)b * a.Hq + h0 + g) * D + d;
-  float* lo = a.lse_dst ? a.lse_dst + (size_t)b * a.Hq + h0 + g : nullptr;
-  if (failed) {
-    if (sl == 0) {
-      *reinterpret_cast<f32x4*>(o) = f32x4{NAN, NAN, NAN, NAN};
-      if (d == 0 && lo) *lo = NAN;
-    }
-    if (lane == 0) {
-      __builtin_amdgcn_raw_buffer_store_b32(1u, hr, 4, 0, kCpolDevice);
-      __builtin_amdgcn_raw_buffer_store_b32(0u, hr, 0, 0, kCpolDevice);
-    }
-    return;
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int c = 0; c < kFuseLaneSplits; ++c)
-    if ((want >> c) & 1u) M = fmaxf(M, l[c]);
-  M = lanes_max(M, lq);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  float z = 0.f;
-#pragma unroll
-  for (int c = 0; c < kFuseLaneSplits; ++c) {
-    if ((want >> c) & 1u) {
-      const float wt = fexp2(l[c] - Ms);
-      acc += wt * v[c];
-      z += wt;
-    }
-  }
-  z = lanes_sum(z, lq);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = lanes_sum(acc[e], lq);
-  if (sl == 0) {
-    const bool none = M == -INFINITY;
-    *reinterpret_cast<f32x4*>(o) =
-        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / z);
-    if (d == 0 && lo) *lo = none ? -INFINITY : (M + flog2(z)) * kLn2;
-  }
-  // Back to the empty pattern for the next call.
-  const u32x4 empty = u32x4{kWsEmpty, kWsEmpty, kWsEmpty, kWsEmpty};
-#pragma unroll
-  for (int c = 0; c < kFuseLaneSplits; ++c) {
-    if ((want >> c) & 1u) {
-      const int sp = sl + c * SL;
-      __builtin_amdgcn_raw_buffer_store_b128(
-          empty, dr, (unsigned)(sp * F) * 4u, 0, kCpolDevice);
-      if (q == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(
-            kWsEmpty, lr, (unsigned)(sp * NWV) * 4u, 0, kCpolDevice);
-    }
-  }
-}
-
 // Cache encodings of the MFMA kernel.
 enum : int { kCacheBf16 = 0, kCacheE4M3 = 1, kCacheI8 = 2 };
 
@@ -596,7 +402,7 @@ constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
 //     product, while the softmax sum takes the unscaled probability.
 //     Positions at or past the length are masked, whatever their scales.
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
-          bool BAL = false, bool FUSE = false>
+          bool BAL = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(QM != kCacheBf16))))
 void split_mfma(
@@ -639,16 +445,7 @@ void split_mfma(
   const int h0 = kvh * G + hg * GM;
   const int nh = min(GM, G - hg * GM);
   if (__builtin_expect(lo >= hi_max, 0)) {  // no sequence reaches this split
-    if constexpr (FUSE) {
-      for (int i = threadIdx.x; i < nh * (D / 4); i += NW * 64) {
-        const int g = i / (D / 4);
-        fuse_put<D>(a, unit, nh, s, g, 4 * (i - g * (D / 4)),
-                    f32x4{0.f, 0.f, 0.f, 0.f}, -INFINITY);
-      }
-      fuse_reduce<D, NW>(a, unit, nh, s, b, h0);
-    } else {
-      write_empty<D>(a, b, h0, nh, s);
-    }
+    write_empty<D>(a, b, h0, nh, s);
     return;
   }
 
@@ -719,6 +516,23 @@ void split_mfma(
       V1 = V0 + (size_t)last0 * D;
       cap1 = 0;
     }
+    if constexpr (I8) {
+      // A group wholly past `end` re-reads the first group's scales.
+      const size_t s0 = scale_row(g0, t0) + 4 * j;
+      const size_t s1 = last1 >= 0 ? scale_row(g1, t0 + 16) + 4 * j : s0;
+      if (part & 1) {
+        k_sc[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(k_scales + s0));
+        k_sc[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(k_scales + s1));
+      }
+      if (part & 2) {
+        v_sc[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(v_scales + s0));
+        v_sc[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(v_scales + s1));
+      }
+    }
     // Element offsets (16-byte requests): bf16 K dims 8j + 32c, 8-bit K
     // dims 16j + 64c.
     constexpr int KJ = F8 ? 16 : 8, KS = F8 ? 64 : 32;
@@ -746,25 +560,6 @@ void split_mfma(
         }
       }
     }
-    // int8: the scales after the codes (their pointers are kernel arguments
-    // that are not preloaded, so these requests may wait for them).
-    if constexpr (I8) {
-      // A group wholly past `end` re-reads the first group's scales.
-      const size_t s0 = scale_row(g0, t0) + 4 * j;
-      const size_t s1 = last1 >= 0 ? scale_row(g1, t0 + 16) + 4 * j : s0;
-      if (part & 1) {
-        k_sc[0] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(k_scales + s0));
-        k_sc[1] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(k_scales + s1));
-      }
-      if (part & 2) {
-        v_sc[0] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(v_scales + s0));
-        v_sc[1] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(v_scales + s1));
-      }
-    }
   };
 
   // With SPEC the wave's first subtile goes out before anything else,
@@ -785,10 +580,6 @@ void split_mfma(
   u32x4 kp[2][KL];
   VT vp[8];
   load_subtile(min(t_first, (hi - 1) & ~15), hi, kp, vp, 3);
-  // Nothing that waits on a kernel argument outside the preloaded ones
-  // (a scalar load from the argument segment: a memory round trip) may move
-  // above the first requests.
-  __builtin_amdgcn_sched_barrier(0);
 
   // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
   // scores are computed and never used.
@@ -1040,111 +831,59 @@ void split_mfma(
       lsum += wt * ml[ww][g];
     }
     const bool none = M == -INFINITY;       // no token in this split
-    const f32x4 ov = none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (vsc / lsum);
-    if constexpr (FUSE) {
-      fuse_put<D>(a, unit, nh, s, g, d, ov,
-                  none ? -INFINITY : M + flog2(lsum));
-    } else {
-      *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) = ov;
-      if (d == 0) {
-        float* l = lse_dst(a, b, h0 + g, s);
-        if (l) *l = none ? -INFINITY : (M + flog2(lsum)) * kLn2;
-      }
+    *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) =
+        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (vsc / lsum);
+    if (d == 0) {
+      float* l = lse_dst(a, b, h0 + g, s);
+      if (l) *l = none ? -INFINITY : (M + flog2(lsum)) * kLn2;
     }
   }
-  if constexpr (FUSE) fuse_reduce<D, NW>(a, unit, nh, s, b, h0);
 }
 
 // ----------------------------------------------------------------------------
 // Log-sum-exp combine of split partials.
 
-// One workgroup of 256 threads per (sequence, head). Thread t takes the
-// float4 column c = t % (D/4) of the head's output and the splits sl,
-// sl + SLN, ... (sl = t / (D/4), SLN = 256 / (D/4) split lanes), eight at a
-// time with all loads issued before use; each wave instruction reads whole
-// partial rows (512 bytes at D = 128), so no cache line is fetched twice.
-// A lane merges its splits online; lanes of one wave then merge through
-// permlane swaps, and the four waves through LDS. Every split slot holds a
-// valid partial (an empty split is o = 0, lse = -inf), so no length is
-// needed and the arguments are scalars the hardware preloads. With `reset`
-// (partials in a call's workspace) every slot read is left as the empty
-// pattern, the state the workspace keeps between calls.
-__device__ __forceinline__ void lse_merge(float& M, float& z, f32x4& acc,
-                                          float M2, float z2, f32x4 a2) {
-  const float Mn = fmaxf(M, M2);
-  if (Mn == -INFINITY) return;
-  const float f1 = fexp2((M - Mn) * kLog2e), f2 = fexp2((M2 - Mn) * kLog2e);
-  acc = acc * f1 + a2 * f2;
-  z = z * f1 + z2 * f2;
-  M = Mn;
-}
-// Merge with the partner lane of a permlane swap (both orders give the
-// same sums, so the two lanes agree bit for bit).
-template <bool X32>
-__device__ __forceinline__ void lse_merge_swap(float& M, float& z,
-                                               f32x4& acc) {
-  auto sw = [](float x) {
-    const auto r = X32 ? __builtin_amdgcn_permlane32_swap(
-                             __float_as_uint(x), __float_as_uint(x), false, false)
-                       : __builtin_amdgcn_permlane16_swap(
-                             __float_as_uint(x), __float_as_uint(x), false, false);
-    return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
-  };
-  const float2 m2 = sw(M), z2 = sw(z);
-  f32x4 p, q;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float2 x = sw(acc[e]);
-    p[e] = x.x;
-    q[e] = x.y;
-  }
-  float Ma = m2.x, za = z2.x;
-  f32x4 aa = p;
-  lse_merge(Ma, za, aa, m2.y, z2.y, q);
-  M = Ma;
-  z = za;
-  acc = aa;
-}
-
+// One wave per (sequence, head, 16-dim slice of the output). Lane l takes
+// split group g = l/4 and dims 4*(l%4) of the slice; group g reads splits
+// g, g+16, g+32, ... . A chunk's loads (8 splits per lane) are all issued
+// before any is used, so a chunk costs one memory round trip; chunks merge
+// online, and the 16 groups are reduced with cross-lane exchanges. Every
+// split slot holds a valid partial (empty splits are o = 0, lse = -inf and
+// get weight 0), so no length is needed, and the arguments are scalars the
+// hardware preloads: the kernel waits on nothing before its data loads.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(
-    float* __restrict__ o_part, float* __restrict__ lse_part,
-    float* __restrict__ out_base, float* __restrict__ lse_out, int S,
-    int reset) {
-  constexpr int NC = D / 4;                 // float4 columns
-  constexpr int SLN = 256 / NC;             // split lanes (8 or 16)
-  constexpr int CH = 8;                     // splits per lane per round
-  const int t = threadIdx.x;
-  const int c = t % NC, sl = t / NC;
-  const size_t bh = blockIdx.x;
-  float* lse = lse_part + bh * S;
-  float* op = o_part + bh * S * D + 4 * c;
-  const u32x4 empty = u32x4{kWsEmpty, kWsEmpty, kWsEmpty, kWsEmpty};
+__global__ __launch_bounds__(64) void combine_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    float* __restrict__ out_base, float* __restrict__ lse_out, int S) {
+  constexpr int SL = D / 16;                // slices per head
+  constexpr int CH = 8;                     // splits per lane per chunk
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x / SL;
+  const int sl = blockIdx.x - bh * SL;
+  const int g = lane >> 2, qd = lane & 3;
+  const float* lse = lse_part + (size_t)bh * S;
+  const float* op = o_part + (size_t)bh * S * D + 16 * sl + 4 * qd;
 
   float M = -INFINITY, z = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < S; base += SLN * CH) {
+  for (int base = 0; base < S; base += 16 * CH) {
     float lv[CH];
     f32x4 ov[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int sp = base + sl + SLN * k;
+      const int sp = base + g + 16 * k;
       const bool ok = sp < S;
       lv[k] = ok ? lse[sp] : -INFINITY;
       ov[k] = ok ? *reinterpret_cast<const f32x4*>(op + (size_t)sp * D)
                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (reset) {
-#pragma unroll
-      for (int k = 0; k < CH; ++k) {
-        const int sp = base + sl + SLN * k;
-        if (sp < S) *reinterpret_cast<u32x4*>(op + (size_t)sp * D) = empty;
-      }
-    }
     float mx = lv[0];
 #pragma unroll
     for (int k = 1; k < CH; ++k) mx = fmaxf(mx, lv[k]);
-    const float Mn = fmaxf(M, mx);
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    mx = fmaxf(mx, __shfl_xor(mx, 8));
+    mx = max_x32(max_x16(mx));
+    const float Mn = fmaxf(M, mx);           // wave-uniform
     if (Mn == -INFINITY) continue;
     const float f = fexp2((M - Mn) * kLog2e);
     acc *= f;
@@ -1157,40 +896,22 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
     M = Mn;
   }
-  // Split lanes inside a wave: lane t and t ^ 32 (and t ^ 16 at D = 64).
-  if (NC == 16) lse_merge_swap<false>(M, z, acc);
-  lse_merge_swap<true>(M, z, acc);
-  __shared__ f32x4 s_acc[4][NC];
-  __shared__ float s_m[4], s_z[4];
-  const int w = t >> 6;
-  if ((t & 63) < NC) s_acc[w][c] = acc;
-  if ((t & 63) == 0) {
-    s_m[w] = M;
-    s_z[w] = z;
-  }
-  __syncthreads();
-  if (t < NC) {
-    float Mt = s_m[0], zt = s_z[0];
-    f32x4 at = s_acc[0][c];
 #pragma unroll
-    for (int k = 1; k < 4; ++k) lse_merge(Mt, zt, at, s_m[k], s_z[k], s_acc[k][c]);
-    *reinterpret_cast<f32x4*>(out_base + bh * D + 4 * c) =
-        Mt == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : at * (1.f / zt);
-    if (t == 0 && lse_out)
-      lse_out[bh] = Mt == -INFINITY ? -INFINITY : Mt + flog2(zt) * kLn2;
+  for (int i = 0; i < 4; ++i) {
+    float x = acc[i];
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    acc[i] = sum_x32(sum_x16(x));
   }
-  // Every lane's lse loads were consumed before the barrier.
-  if (reset)
-    for (int i = t; i < S; i += 256) lse[i] = __uint_as_float(kWsEmpty);
-}
-
-// Fills a workspace with its between-calls state: the header's magic word,
-// a clear error word, and the empty pattern everywhere else.
-__global__ __launch_bounds__(256) void ws_init_kernel(unsigned* ws,
-                                                      size_t words) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words;
-       i += (size_t)gridDim.x * 256)
-    ws[i] = i == 0 ? kWsMagic : (i < kWsHeader / 4 ? 0u : kWsEmpty);
+  z += __shfl_xor(z, 4);
+  z += __shfl_xor(z, 8);
+  z = sum_x32(sum_x16(z));
+  float* out = out_base + (size_t)bh * D + 16 * sl + 4 * qd;
+  if (g == 0)
+    *reinterpret_cast<f32x4*>(out) =
+        M == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / z);
+  if (lane == 0 && sl == 0 && lse_out)
+    lse_out[bh] = M == -INFINITY ? -INFINITY : M + flog2(z) * kLn2;
 }
 
 // Grid of the split kernels: x = kv head (x head group), y = sequence,
@@ -1221,22 +942,21 @@ int split_waves(int P, bool f8) {
 // at dispatch, so no wave waits on an argument load before its first
 // request (such loads queue behind other waves' K/V traffic).
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
-          bool BAL = false, bool FUSE = false>
+          bool BAL = false>
 void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL, FUSE>),
-                     grid, dim3(NW * 64), 0, st, a.k, a.v,
+  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL>), grid,
+                     dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
                      a.nhg, a.G, a.block_table, a.bs, a);
 }
 
-template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false,
-          bool FUSE = false>
+template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false>
 void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
   constexpr bool F8 = QM != kCacheBf16;
   if (F8 && nw == 8)
-    launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, QM, BAL, FUSE>(grid, a, st);
+    launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
   else
-    launch_one<D, 4, GM, PAGED, SPEC, QM, BAL, FUSE>(grid, a, st);
+    launch_one<D, 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
 }
 
 // Speculative first loads pay off for a single sequence (its splits are all
@@ -1244,9 +964,7 @@ void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
 // may differ, they could read splits that turn out empty.
 template <int D, bool PAGED, int GM, int QM>
 void launch_mfma_gm(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
-  if (a.B == 1 && a.fuse_R > 0)
-    launch_mfma_spec<D, PAGED, GM, true, QM, false, true>(grid, nw, a, st);
-  else if (a.B == 1)
+  if (a.B == 1)
     launch_mfma_spec<D, PAGED, GM, true, QM>(grid, nw, a, st);
   else if (a.bal_target > 0 && a.B <= 64)       // lane = sequence
     launch_mfma_spec<D, PAGED, GM, false, QM, true>(grid, nw, a, st);
@@ -1254,31 +972,8 @@ void launch_mfma_gm(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
     launch_mfma_spec<D, PAGED, GM, false, QM>(grid, nw, a, st);
 }
 
-// The single-launch (fused) plan for one sequence with at most 16 query
-// heads per kv head: the smallest FW in {4, 8, 16} output floats per
-// reducer wave such that the F = G * D floats of a kv head unit split into
-// R = F / (NW * FW) <= S reducer workgroups, a reducer lane reads at most
-// kFuseLaneSplits splits, and the call has at most kFuseMaxWaiters
-// reducers. FW = 4 at the 64K batch-one shape (S = 128: 64 reducers per kv
-// head, two splits per lane); the 256K shape (S = 32) takes FW = 8.
-bool fuse_plan(const Shape& s, int S, int nw, int* R, int* FW) {
-  if (s.B != 1 || S < 2 || s.G > kHeadsPerGroup) return false;
-  const int F = s.G * s.D;
-  for (int fw = 4; fw <= 16; fw *= 2) {
-    if (F % (nw * fw) != 0) continue;
-    const int r = F / (nw * fw);
-    const int lane_splits = (S + (64 / (fw / 4)) - 1) / (64 / (fw / 4));
-    if (r > S || lane_splits > kFuseLaneSplits) continue;
-    if ((long long)s.Hkv * r > kFuseMaxWaiters) continue;
-    *R = r;
-    *FW = fw;
-    return true;
-  }
-  return false;
-}
-
 template <int D, bool PAGED, int QM>
-void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st, int* fused) {
+void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const int gm = s.G <= 8 ? 8 : 16;
   a.nhg = (s.G + gm - 1) / gm;
   // About two workgroups per CU in total, spread over the kv head units.
@@ -1292,13 +987,6 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st, int* fused) {
   const bool pieces = a.B > 1 && a.B <= 64 && a.bal_target > 0;
   const int nw = QM == kCacheI8 && pieces
                      ? 4 : split_waves(a.P, QM != kCacheBf16);
-  a.fuse_R = 0;
-  if (a.fuse_ok && fuse_plan(s, a.S, nw, &a.fuse_R, &a.fuse_FW)) {
-    a.o_dst = a.fin_out;
-    a.lse_dst = a.fin_lse;
-    a.final_out = 1;
-    *fused = 1;
-  }
   if (gm == 8)
     launch_mfma_gm<D, PAGED, 8, QM>(grid, nw, a, st);
   else
@@ -1306,30 +994,27 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st, int* fused) {
 }
 
 template <int QM>
-void launch_mfma_dtype(const Shape& s, const SplitArgs& a, hipStream_t st,
-                       int* fused) {
+void launch_mfma_dtype(const Shape& s, const SplitArgs& a, hipStream_t st) {
   const bool paged = s.bs > 0;
   if (s.D == 128) {
-    if (paged) launch_mfma<128, true, QM>(s, a, st, fused);
-    else launch_mfma<128, false, QM>(s, a, st, fused);
+    if (paged) launch_mfma<128, true, QM>(s, a, st);
+    else launch_mfma<128, false, QM>(s, a, st);
   } else {
-    if (paged) launch_mfma<64, true, QM>(s, a, st, fused);
-    else launch_mfma<64, false, QM>(s, a, st, fused);
+    if (paged) launch_mfma<64, true, QM>(s, a, st);
+    else launch_mfma<64, false, QM>(s, a, st);
   }
 }
 
 }  // namespace
 
-int launch_split(const Shape& s, const SplitArgs& a, void* stream,
-                 int* fused) {
+int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  *fused = 0;
   if (s.dtype == FD_DTYPE_BF16) {
-    launch_mfma_dtype<kCacheBf16>(s, a, st, fused);
+    launch_mfma_dtype<kCacheBf16>(s, a, st);
   } else if (s.dtype == FD_DTYPE_FP8_E4M3) {
-    launch_mfma_dtype<kCacheE4M3>(s, a, st, fused);
+    launch_mfma_dtype<kCacheE4M3>(s, a, st);
   } else if (s.dtype == FD_DTYPE_INT8) {
-    launch_mfma_dtype<kCacheI8>(s, a, st, fused);
+    launch_mfma_dtype<kCacheI8>(s, a, st);
   } else {
     const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
     const dim3 block(kGenThreads);
@@ -1343,24 +1028,14 @@ int launch_split(const Shape& s, const SplitArgs& a, void* stream,
 
 int launch_combine(int D, const CombineArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(a.B * a.Hq));
   if (D == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, st,
-                       a.o_part, a.lse_part, a.out, a.lse_out, a.S, a.reset);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)(a.B * a.Hq * 8)),
+                       dim3(64), 0, st, a.o_part, a.lse_part, a.out,
+                       a.lse_out, a.S);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, st,
-                       a.o_part, a.lse_part, a.out, a.lse_out, a.S, a.reset);
-  return (int)hipGetLastError();
-}
-
-int launch_workspace_init(void* ws, size_t bytes, void* stream) {
-  const size_t words = bytes / 4;
-  if (words == 0) return 0;
-  const size_t blocks = (words + 255) / 256;
-  hipLaunchKernelGGL(ws_init_kernel,
-                     dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256),
-                     0, static_cast<hipStream_t>(stream),
-                     static_cast<unsigned*>(ws), words);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3((unsigned)(a.B * a.Hq * 4)),
+                       dim3(64), 0, st, a.o_part, a.lse_part, a.out,
+                       a.lse_out, a.S);
   return (int)hipGetLastError();
 }
 

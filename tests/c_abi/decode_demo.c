@@ -115,11 +115,6 @@ static int run(const char* in_path, const char* out_path) {
 
   hipStream_t stream;
   CHECK_HIP(hipStreamCreate(&stream));
-  st = fd_workspace_init(dws, ws_bytes, (void*)stream);
-  if (st != FD_OK) {
-    fprintf(stderr, "fd_workspace_init: %s\n", fd_status_str(st));
-    return 1;
-  }
   st = fd_decode_attn(&s, dq, dk, dv, NULL, (const int32_t*)dl, splits, dws,
                       ws_bytes, dout, dlse, (void*)stream);
   if (st != FD_OK) {

@@ -5,8 +5,7 @@
 // suitably aligned device addresses, which the host code never
 // dereferences. The stubs check the invariants a kernel relies on:
 //   - splits cover the history;
-//   - the workspace holds the partials it is handed, after its header, and
-//     the records of the single-launch path;
+//   - the workspace holds the partials it is handed;
 //   - scale pointers exist exactly for the quantized dtypes.
 // Prints "ok <calls> launches" and exits 0 when every check holds.
 #include <hip/hip_runtime_api.h>
@@ -63,32 +62,16 @@ static void check_split_args(const Shape& s, const SplitArgs& a) {
     const uintptr_t o = (uintptr_t)a.o_dst, l = (uintptr_t)a.lse_dst;
     const size_t no = (size_t)a.B * a.Hq * a.S * s.D * 4;
     const size_t nl = (size_t)a.B * a.Hq * a.S * 4;
-    EXPECT(o == g_ws + kWsHeader && (o & 15) == 0);
+    EXPECT(o == g_ws && (o & 15) == 0);
     EXPECT(l >= o + no && l + nl <= g_ws + g_ws_bytes);
-  }
-  if (a.fuse_ok) {                  // single-launch records: the same areas
-    EXPECT(g_ws && !a.final_out && a.S > 1);
-    EXPECT((uintptr_t)a.ws_hdr == g_ws && a.rec == a.o_dst &&
-           a.lrec == a.lse_dst && a.fin_out);
-    // lse records: at most D / 4 per query head and split
-    EXPECT((uintptr_t)a.lrec + (size_t)a.B * a.Hq * a.S * (s.D / 4) * 4 <=
-           g_ws + g_ws_bytes);
   }
   EXPECT(a.balance_cus == 0 || a.balance_cus == 256);
   if (a.balance_cus) EXPECT(a.B > 1 && a.S > 1);
 }
 
-int launch_split(const Shape& s, const SplitArgs& a, void*, int* fused) {
+int launch_split(const Shape& s, const SplitArgs& a, void*) {
   ++g_launches;
   check_split_args(s, a);
-  *fused = 0;                       // the stub always takes two launches
-  return 0;
-}
-
-int launch_workspace_init(void* ws, size_t bytes, void*) {
-  ++g_launches;
-  EXPECT(ws && ((uintptr_t)ws & 15) == 0);
-  EXPECT(bytes >= kWsHeader && bytes % 16 == 0);
   return 0;
 }
 
@@ -98,11 +81,10 @@ int launch_combine(int D, const CombineArgs& c, void*) {
   EXPECT(c.B >= 1 && c.Hq >= 1 && c.S >= 1);
   EXPECT(c.o_part && c.lse_part && c.out);
   if (g_ws) {
-    EXPECT((uintptr_t)c.o_part == g_ws + kWsHeader);
+    EXPECT((uintptr_t)c.o_part == g_ws);
     EXPECT((uintptr_t)c.lse_part + (size_t)c.B * c.Hq * c.S * 4 <=
            g_ws + g_ws_bytes);
   }
-  EXPECT(c.reset == (g_ws ? 1 : 0));  // only workspace partials are reset
   return 0;
 }
 
@@ -195,10 +177,9 @@ int main() {
     const bool paged = s.block_size > 0;
     const int32_t* tbl = paged ? bt : nullptr;
     const long before = g_launches;
-    const int which = (int)(rnd() % 8);
+    const int which = (int)(rnd() % 7);
     if (which == 1 || which == 6) g_ws = 0;   // caller's own partials
     int st;
-    size_t init_bytes = 1;
     switch (which) {
       case 0:
         st = fd_decode_attn(&s, q, k, v, tbl, lens, S, (void*)ws, g_ws_bytes,
@@ -224,12 +205,6 @@ int main() {
                                    (rnd() % 2) ? 3.f : INFINITY, S, (void*)ws,
                                    g_ws_bytes, out, lse, nullptr, nullptr);
         break;
-      case 7:
-        g_ws = 0;
-        init_bytes = (size_t)(rnd() % 3) * (rnd() % 4096) * 8;
-        st = fd_workspace_init((void*)(ws + (rnd() % 2) * 8), init_bytes,
-                               nullptr);
-        break;
       default:
         st = fd_combine_partials(s.batch, s.num_q_heads, s.head_dim, S,
                                  (const float*)ws,
@@ -241,7 +216,7 @@ int main() {
            st == FD_ERR_UNSUPPORTED || st == FD_ERR_WORKSPACE);
     if (st == FD_OK) {
       ++oks;
-      if (init_bytes != 0) EXPECT(g_launches > before);   // 0 bytes: no-op
+      EXPECT(g_launches > before);
     } else {
       EXPECT(g_launches == before);   // a refused call launches nothing
     }

@@ -135,8 +135,6 @@ def run_sparse(w, t, codes, scales, delta, S):
     shape = shape_of(w)
     nbytes = fb.fd_workspace_size(shape, S)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=d)
-    if nbytes:
-        fb.fd_workspace_init(ws)
     print(f"[gpu] sparse {w.name} paged={w.paged} D={D} delta={delta} S={S}",
           flush=True)
     fb.fd_decode_attn_sparse(shape, t["q"], t["k"], t["v"], codes, scales,
