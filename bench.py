@@ -56,6 +56,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time for the oracle baseline")
+    p.add_argument("--no-read-probe", action="store_true",
+                   help="skip the bare HBM read probe (fd_read_probe)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (for "
                         "scaling HBM byte counters)")
@@ -276,6 +278,42 @@ def copy_probe(torch):
                 GBps_read_plus_write=2 * n / (ms * 1e6))
 
 
+# Shapes the read probe is timed at: the split kernel's launch shape at
+# the headline workload (256 workgroups of 4 waves, 8 KB per wave in
+# flight) and the others a sweep found fastest on MI355X.
+PROBE_SHAPES = [(256, 4, 8), (256, 16, 2), (256, 16, 4), (512, 4, 8),
+                (2048, 8, 2)]
+
+
+def read_probe(torch, nbytes, steps, warmup):
+    """Bare streaming reads of nbytes (rounded down to what every probe
+    shape divides) from buffers rotated over >= 512 MiB, each shape timed
+    like the call: a graph of back-to-back launches, median of 5 replays."""
+    from split_kv_long_amd import binding as fb
+    unit = max(w * nw * 64 * 16 * u for w, nw, u in PROBE_SHAPES)
+    n = nbytes // unit * unit
+    if n == 0:
+        return None
+    R = max(1, math.ceil(2 * MALL_BYTES / n))
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    shapes = {}
+    for wg, nw, u in PROBE_SHAPES:
+        def fn(i, wg=wg, nw=nw, u=u):
+            fb.fd_read_probe(bufs[i % R], wg, nw, u, sink, nbytes=n)
+        ms, _ = time_graph(torch, fn, steps, warmup, replays=5)
+        us = ms * 1e3 / steps
+        shapes[f"{wg}x{nw}w_{u * 16}B"] = {"us": round(us, 3),
+                                           "GBps": round(n / (us * 1e3), 1)}
+    del bufs
+    best = max(shapes, key=lambda k: shapes[k]["GBps"])
+    return {"bytes": n, "copies_rotated": R, "shapes": shapes,
+            "split_grid_shape": "256x4w_128B", "best_shape": best,
+            "best_GBps": shapes[best]["GBps"]}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -431,6 +469,14 @@ def run_one(args, name, steps, warmup, with_cpu):
             del b2
         rec["split_comparison_us_per_call"] = res
         rec["split_comparison_planned"] = b.S
+    if name == args.workload and not args.no_read_probe:
+        probe = read_probe(torch, b.bytes_split - (b.bytes_split % 16), steps,
+                           warmup)
+        if probe:
+            rec["roofline"]["probe_GBps"] = probe["best_GBps"]
+            rec["roofline"]["frac_of_probe"] = round(
+                split_gbps / probe["best_GBps"], 4)
+            rec["read_probe"] = probe
     if args.copy_probe and name == args.workload:
         rec["copy_probe"] = copy_probe(torch)
     if with_cpu:

@@ -37,7 +37,11 @@
  *     [0, max_seq_len] and block ids into [0, num_blocks) on the device so a
  *     broken call cannot read outside the buffers, but its result is
  *     meaningless.)
- *   - For fixed inputs and num_splits the result is bitwise deterministic.
+ *   - Determinism: for fixed inputs, num_splits and device the result is
+ *     bitwise reproducible (no atomics; every reduction runs in a fixed
+ *     order). Only fd_decode_attn on 2 to 64 sequences consults the device:
+ *     it sizes its length-aware pieces from the device's compute-unit
+ *     count, so two devices with different counts may round differently.
  */
 #ifndef FD_DECODE_H
 #define FD_DECODE_H
@@ -136,17 +140,26 @@ int fd_plan_splits(const fd_shape* shape, int num_cus, int64_t sum_seq_len,
  * Bytes of device workspace fd_decode_attn needs for num_splits splits:
  * 0 when num_splits == 1, else room for the fp32 partials
  * o_part [batch, Hq, S, head_dim] and lse_part [batch, Hq, S] (natural log),
- * 256-byte aligned. shape and bytes are host pointers.
+ * 256-byte aligned. These are the per-piece partial outputs and their
+ * log-sum-exp values that the final reduction merges (slavadubrov.com,
+ * "What is Flash-Decoding, and when does it speed up LLMs?", section "Why
+ * decode needs a different schedule"). shape and bytes are host pointers;
+ * shape is validated as for fd_decode_attn and num_splits must be in
+ * [1, 65535] (FD_ERR_INVALID_ARG otherwise).
  */
 int fd_workspace_size(const fd_shape* shape, int num_splits, size_t* bytes);
 
 /*
- * Full decode attention: the split kernel, then (if num_splits > 1) the
- * log-sum-exp combine kernel, on `stream`. For 2 to 64 sequences and
- * num_splits > 1 the split kernel cuts each sequence into up to num_splits
- * equal pieces sized by its own length instead of the uniform splits above
- * (an internal choice: the result is the same attention, and it stays
- * deterministic for a given device).
+ * Full decode attention, the operation of slavadubrov.com, "What is
+ * Flash-Decoding, and when does it speed up LLMs?" (sections "What is
+ * Flash-Decoding" and "Why decode needs a different schedule"): the split
+ * kernel computes every split's partial output and log-sum-exp in
+ * parallel, then (if num_splits > 1) the log-sum-exp combine kernel merges
+ * them into exact attention over the whole history, both on `stream`. For 2
+ * to 64 sequences and num_splits > 1 the split kernel cuts each sequence
+ * into up to num_splits equal pieces sized by its own length instead of the
+ * uniform splits above (an internal choice: the result is the same
+ * attention; see Determinism above).
  *
  *   q, k_cache, v_cache  device, dtype per shape, 16-byte aligned
  *   block_table          device int32, non-NULL iff shape->block_size > 0

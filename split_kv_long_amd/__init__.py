@@ -2,32 +2,40 @@
 
 The compute lives in ``lib/libfd_decode.so`` (hand-written HIP kernels behind
 the C ABI in ``include/fd_decode.h``); ``binding`` exposes the same calls to
-Python, and ``decode_attention`` below is a convenience wrapper that sizes
-and allocates the outputs with torch before calling ``fd_decode_attn``.
+Python, and ``decode_attention`` below is a convenience wrapper that checks
+the tensors, sizes and allocates the outputs with torch before calling
+``fd_decode_attn``.
 """
 
 from __future__ import annotations
 
 from typing import Optional
 
-__all__ = ["decode_attention", "shape_for"]
+__all__ = ["decode_attention", "shape_for", "validate_inputs"]
 
 
 def shape_for(q, k_cache, seq_lens, block_table=None, max_seq_len=None,
               scale=None):
-    """fd_shape for torch tensors laid out as the C ABI describes."""
+    """fd_shape for torch tensors laid out as the C ABI describes.
+
+    For a contiguous cache [B, Hkv, L, D] the length dimension L is also the
+    row stride the kernels use, so ``max_seq_len`` may only repeat it; for a
+    paged pool it bounds the lengths (default: every block-table entry)."""
     import torch
     from . import binding
     B, Hq, D = q.shape
     if block_table is None:
         _, Hkv, L, _ = k_cache.shape
+        if max_seq_len is not None and int(max_seq_len) != L:
+            raise ValueError(
+                f"max_seq_len={max_seq_len} for a contiguous cache of length "
+                f"{L}: the cache's length dimension is its row stride, so "
+                "the bound must equal it (slice the cache instead)")
         bs = maxb = nb = 0
     else:
         nb, Hkv, bs, _ = k_cache.shape
         maxb = block_table.shape[1]
-        L = max_seq_len if max_seq_len is not None else maxb * bs
-    if max_seq_len is not None:
-        L = max_seq_len
+        L = int(max_seq_len) if max_seq_len is not None else maxb * bs
     if k_cache.dtype in (torch.float8_e4m3fn, torch.int8):
         if q.dtype != torch.bfloat16:
             raise ValueError("an 8-bit cache takes a bf16 query")
@@ -41,20 +49,79 @@ def shape_for(q, k_cache, seq_lens, block_table=None, max_seq_len=None,
     return binding.make_shape(B, Hq, Hkv, D, L, dt, bs, maxb, nb, scale or 0.0)
 
 
+def validate_inputs(q, k_cache, v_cache, seq_lens, block_table=None,
+                    k_scale=None, v_scale=None, max_seq_len=None,
+                    device=None):
+    """Raise ValueError unless the tensors have the dtypes, shapes, layout
+    and device the C ABI reads them with (the library trusts its pointers:
+    a wrong dtype or stride would give wrong results, not an error)."""
+    import torch
+    dev = q.device if device is None else torch.device(device)
+
+    def need(cond, msg):
+        if not cond:
+            raise ValueError(msg)
+
+    def on_dev(name, t):
+        need(t.device == dev,
+             f"{name} is on device {t.device}, expected {dev}")
+        need(t.is_contiguous(), f"{name} must be contiguous")
+
+    need(q.dim() == 3, "q must be [batch, num_q_heads, head_dim]")
+    need(k_cache.dim() == 4 and v_cache.shape == k_cache.shape
+         and v_cache.dtype == k_cache.dtype,
+         "k_cache and v_cache must match in dtype and 4-D shape")
+    B, Hq, D = q.shape
+    need(k_cache.shape[-1] == D, "the caches' head_dim differs from q's")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("seq_lens", seq_lens)):
+        on_dev(name, t)
+    need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,),
+         f"seq_lens must be int32 [{B}] (got {seq_lens.dtype} "
+         f"{tuple(seq_lens.shape)})")
+    if block_table is not None:
+        on_dev("block_table", block_table)
+        need(block_table.dtype == torch.int32 and block_table.dim() == 2
+             and block_table.shape[0] == B,
+             f"block_table must be int32 [{B}, max_blocks_per_seq]")
+    shape = shape_for(q, k_cache, seq_lens, block_table, max_seq_len)
+    Hkv = shape.num_kv_heads
+    if k_cache.dtype == torch.float8_e4m3fn:
+        want = (Hkv,)
+    elif k_cache.dtype == torch.int8:
+        if block_table is None:
+            want = (B, Hkv, -(-shape.max_seq_len // 16) * 16)
+        else:
+            want = (shape.num_blocks, Hkv, shape.block_size)
+    else:
+        need(k_scale is None and v_scale is None,
+             "scales are only taken with an 8-bit cache")
+        return shape
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        need(t is not None, f"an 8-bit cache needs {name}")
+        on_dev(name, t)
+        need(t.dtype == torch.float32 and tuple(t.shape) == want,
+             f"{name} must be fp32 {want} (got {t.dtype} {tuple(t.shape)})")
+    return shape
+
+
 def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
                      num_splits: Optional[int] = None, scale=None,
                      max_seq_len=None, return_lse: bool = False,
                      k_scale=None, v_scale=None):
     """out[b, h] = softmax attention of q[b, h] over the first seq_lens[b]
-    cached positions (fp32). Tensors must be on the current GPU. An E4M3
-    cache (torch.float8_e4m3fn) needs k_scale / v_scale (fp32 [Hkv]); an
-    int8 cache needs them per (position, kv head), laid out like the cache
-    without head_dim."""
+    cached positions (fp32). Tensors must be contiguous on the current GPU;
+    seq_lens and block_table are int32. An E4M3 cache
+    (torch.float8_e4m3fn) needs k_scale / v_scale fp32 [Hkv]; an int8
+    cache needs them per (position, kv head): contiguous [B, Hkv, Lp] with
+    Lp = ceil(L / 16) * 16 (rows padded to whole 16-position groups), paged
+    [num_blocks, Hkv, block_size]."""
     import torch
     from . import binding
-    if v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must match in dtype and shape")
-    shape = shape_for(q, k_cache, seq_lens, block_table, max_seq_len, scale)
+    shape = validate_inputs(q, k_cache, v_cache, seq_lens, block_table,
+                            k_scale, v_scale, max_seq_len)
+    if scale:
+        shape.scale = float(scale)
     if num_splits is None:
         cus = torch.cuda.get_device_properties(q.device).multi_processor_count
         num_splits = binding.fd_plan_splits(shape, cus, -1)
@@ -64,8 +131,6 @@ def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
     ws = (torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
           if nbytes else None)
     if k_cache.dtype in (torch.float8_e4m3fn, torch.int8):
-        if k_scale is None or v_scale is None:
-            raise ValueError("an 8-bit cache needs k_scale and v_scale")
         call = (binding.fd_decode_attn_fp8
                 if k_cache.dtype == torch.float8_e4m3fn
                 else binding.fd_decode_attn_int8)

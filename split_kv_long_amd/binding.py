@@ -32,7 +32,7 @@ SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_decode_attn",
            "fd_decode_partials_fp8", "fd_decode_attn_int8",
            "fd_decode_partials_int8", "fd_build_key_summary",
            "fd_decode_attn_sparse", "fd_combine_partials", "fd_status_str",
-           "fd_version"]
+           "fd_version", "fd_read_probe"]
 
 
 class FdShape(ctypes.Structure):
@@ -90,6 +90,7 @@ def load() -> ctypes.CDLL:
     lib.fd_status_str.argtypes = [I]
     lib.fd_status_str.restype = ctypes.c_char_p
     lib.fd_version.argtypes = []
+    lib.fd_read_probe.argtypes = [P, SZ, I, I, I, P, P]
     for name in SYMBOLS:
         if name != "fd_status_str":
             getattr(lib, name).restype = ctypes.c_int
@@ -253,3 +254,12 @@ def fd_combine_partials(batch: int, num_q_heads: int, head_dim: int,
         int(batch), int(num_q_heads), int(head_dim), int(num_splits),
         _ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse_out),
         _stream(stream)))
+
+
+def fd_read_probe(buf, workgroups: int, waves: int, loads_per_lane: int,
+                  sink, stream=None, nbytes: Optional[int] = None) -> None:
+    """Enqueue the HBM read probe (fd_probe.h) over a device tensor."""
+    n = nbytes if nbytes is not None else buf.numel() * buf.element_size()
+    _check("fd_read_probe", load().fd_read_probe(
+        _ptr(buf), int(n), int(workgroups), int(waves), int(loads_per_lane),
+        _ptr(sink), _stream(stream)))

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libfd_decode.so")
-SOURCES = ["fd_host.cpp", "fd_kernels.hip", "fd_sparse.hip"]
+SOURCES = ["fd_host.cpp", "fd_kernels.hip", "fd_sparse.hip", "fd_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -308,12 +308,13 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-__device__ Piece balanced_piece(const SplitArgs& a, int L, int P, int units) {
+__device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
+                                int L, int P, int units) {
   const int lane = threadIdx.x & 63;
   const int B = a.B, S = a.S;
   int len = 0;
   if (lane < B) {
-    len = a.seq_lens[lane];
+    len = lens[lane];
     len = len < 0 ? 0 : (len > L ? L : len);
   }
   // Smallest T (multiple of 16, >= P) with sum ceil(len / T) <= target.
@@ -408,7 +409,7 @@ __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(QM != kCacheBf16))))
 void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
-    const int32_t* __restrict__ bt, int bs, SplitArgs a) {
+    const int32_t* __restrict__ bt_or_lens, int bs, SplitArgs a) {
   constexpr bool F8 = QM != kCacheBf16;     // one byte per element
   constexpr bool I8 = QM == kCacheI8;
   using KT = typename std::conditional<F8, uint8_t, uint16_t>::type;
@@ -423,6 +424,11 @@ void split_mfma(
   __shared__ int pg_s[PAGED ? kMaxPages : 1];
   __shared__ float mm[NW][GM], ml[NW][GM];
 
+  // A contiguous cache has no block table: its preloaded slot carries the
+  // lengths, so the length load waits on no kernel-argument read (those go
+  // to memory and would delay the wave's first compute).
+  const int32_t* __restrict__ bt = PAGED ? bt_or_lens : nullptr;
+  const int32_t* __restrict__ lens = PAGED ? a.seq_lens : bt_or_lens;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, j = lane >> 4;
@@ -433,7 +439,7 @@ void split_mfma(
   if constexpr (BAL) {
     // Length-aware pieces (batched calls): every wave derives the same plan
     // from the lengths; the workgroup takes the piece of its dispatch rank.
-    const Piece pc = balanced_piece(a, L, P, Hkv * nhg);
+    const Piece pc = balanced_piece(a, lens, L, P, Hkv * nhg);
     unit = pc.unit;
     b = pc.b;
     s = pc.slot;
@@ -486,7 +492,7 @@ void split_mfma(
   f32x4 k_sc[2], v_sc[2];
   const float* __restrict__ k_scales = I8 ? a.k_scale : nullptr;
   const float* __restrict__ v_scales = I8 ? a.v_scale : nullptr;
-  const int Lp = (L + 15) & ~15;
+  const size_t Lp = ((size_t)L + 15) & ~(size_t)15;    // L may be INT32_MAX
   auto scale_row = [&](size_t g, int t) -> size_t {   // g = group_base(t)
     if (PAGED) return g / D;
     return (size_t)(b * Hkv + kvh) * Lp + t;
@@ -568,7 +574,7 @@ void split_mfma(
   // first and nothing past it is read.
   int hi = hi_max;
   if (!SPEC && !BAL) {
-    int len = a.seq_lens[b];
+    int len = lens[b];
     len = len < 0 ? 0 : (len > L ? L : len);
     hi = min(lo + P, len);
     if (__builtin_expect(lo >= hi, 0)) {
@@ -598,7 +604,7 @@ void split_mfma(
   // past the end of its sequence computes nothing and is written as empty
   // at the merge.
   if (SPEC) {
-    int len = a.seq_lens[b];
+    int len = lens[b];
     len = len < 0 ? 0 : (len > L ? L : len);
     hi = min(lo + P, len);
   }
@@ -947,7 +953,7 @@ void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL>), grid,
                      dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
-                     a.nhg, a.G, a.block_table, a.bs, a);
+                     a.nhg, a.G, PAGED ? a.block_table : a.seq_lens, a.bs, a);
 }
 
 template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false>

@@ -530,8 +530,9 @@ void launch_sparse_d(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
 
 int launch_summary(const Shape& s, const SummaryArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)((s.L + kSumBlock - 1) / kSumBlock), (unsigned)s.Hkv,
-                  (unsigned)s.B);
+  // a.nblk_row = ceil(L / 16), formed in 64 bits by the host (L may be
+  // INT32_MAX)
+  const dim3 grid((unsigned)a.nblk_row, (unsigned)s.Hkv, (unsigned)s.B);
   if (grid.x == 0) return 0;
   if (s.D == 128)
     hipLaunchKernelGGL((summary_kernel<128>), grid, dim3(64), 0, st, a);

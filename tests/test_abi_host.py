@@ -10,16 +10,21 @@ import pytest
 from split_kv_long_amd import binding as fb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fd_decode.h")
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(fb.LIB_PATH),
                                 reason="library not built")
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fd_[a-z0-9_]+)\s*\(", text)))
+    """Every fd_* function the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fd_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
@@ -31,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_shape_struct_matches_header():
-    text = open(HEADER).read()
+    text = open(os.path.join(ROOT, "include", "fd_decode.h")).read()
     body = re.search(r"typedef struct fd_shape \{(.*?)\} fd_shape;", text, re.S)
     fields = re.findall(r"(int32_t|float)\s+(\w+);", body.group(1))
     assert [f for _, f in fields] == [f for f, _ in fb.FdShape._fields_]
@@ -411,7 +416,8 @@ def test_header_is_strict_c99_and_cxx(tmp_path):
     import subprocess
     inc = os.path.join(ROOT, "include")
     src = tmp_path / "h.c"
-    src.write_text('#include "fd_decode.h"\nint main(void) { fd_shape s;\n'
+    src.write_text('#include "fd_decode.h"\n#include "fd_probe.h"\n'
+                   'int main(void) { fd_shape s;\n'
                    '  (void)s; return FD_OK; }\n')
     subprocess.run(["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra",
                     "-Werror", "-fsyntax-only", "-I", inc, str(src)],

@@ -116,7 +116,8 @@ def test_workload_at_planned_splits(name):
 
 @pytest.mark.parametrize("name,splits", [
     ("tiny_mha", [1, 4]),
-    ("long_gqa_64k", [1, 2, 8, 512]),
+    ("long_gqa_64k", [1, 2, 4, 8, 512]),
+    ("ultra_long_256k", [8, 64, 256]),
     ("ragged_paged", [1, 16]),
     ("short_batch", [2, 8]),
 ])
@@ -246,8 +247,12 @@ def test_head_layouts_bf16(hq, hkv, d):
         check(w, S)
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (6, 3, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(16, 2, 128), (6, 3, 64), (40, 2, 64),
+                                     (34, 1, 128)])
 def test_head_layouts_f32(hq, hkv, d):
+    """fp32 caches, including groups of more than 16 query heads per kv
+    head (two head groups, the second partial: 20 = 16 + 4, 34 = 16 + 16
+    + 2)."""
     w = workloads.make("heads32", seed=27, batch=2, num_q_heads=hq,
                        num_kv_heads=hkv, head_dim=d, max_seq_len=300,
                        seq_lens=[300, 129], dtype="f32")

@@ -5,12 +5,19 @@ The "Faster Than Flash" page prints no worked example, so each pin checks
 the oracle against something it does not compute itself: the nearest-integer
 property of the quantizer, hand-packed nibbles, the dense oracle (delta =
 inf, one block per split), torch's float64 SDPA with a mask built from the
-kept blocks, brute-force estimates by explicit loops, and invariants of the
-keep rule. The last test plants plausible mistakes in copies of the keep
-step and shows each is caught.
+kept blocks, brute-force estimates by explicit loops, invariants of the
+keep rule, hand-derived estimates and kept sets on inputs every step
+represents exactly (``tests/golden/sparse_keep.json``), and the bound the
+4-bit keys and 8-bit query put on an estimate's error against the block's
+true largest logit. The last tests plant plausible mistakes in copies of
+the keep step and show each is caught (the unit mistakes -- the estimate
+left without its logit scale, delta used without conversion -- by a pin
+other than the brute-force restatement).
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -224,8 +231,84 @@ def check_keep_invariants(fn):
     assert kept[0, 0, 200 // 16] and kept[1, 0, 200 // 16]
 
 
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                   "sparse_keep.json")))
+
+
+def _golden_inputs():
+    """The inputs of tests/golden/sparse_keep.json, built from its recipe."""
+    c = GOLDEN["construction"]
+    D, L = c["head_dim"], c["seq_len"]
+    q = np.zeros((1, 2, D), np.float32)
+    q[0, 0, 0] = q[0, 1, 1] = 31.75
+    k = np.zeros((1, 1, L, D), np.float32)
+    for j in range(c["blocks"]):
+        for t in range(16):
+            i = 16 * j + t
+            k[0, 0, i, 0] = max(c["c0"][j] - t % 3, -7) / 4
+            k[0, 0, i, 1] = max(c["c1"][j] - t % 2, -7) / 4
+            if t == 0:
+                k[0, 0, i, 63] = -7 / 4
+    v = np.ones((1, 1, L, D), np.float32)
+    v[0, 0, :, 0] = np.arange(L)
+    qb, kb, vb = _bf16(q), _bf16(k), _bf16(v)
+    # every value is exact in bfloat16, so the hand derivation applies
+    assert np.array_equal(oracle.decode_values(kb, "bf16"), k)
+    assert np.array_equal(oracle.decode_values(qb, "bf16"), q)
+    return qb, kb, vb
+
+
+def check_hand_derived_keep(fn):
+    """Estimates equal the hand-derived largest logits times log2 e, and
+    the kept sets match the ones worked out by hand from the logits."""
+    qb, kb, vb = _golden_inputs()
+    codes, scales = osp.key_summary(kb, [64])
+    assert np.all(scales == np.float32(0.25))       # amax 7/4 in every block
+    logit = np.array([GOLDEN["max_logit"]["head0"],
+                      GOLDEN["max_logit"]["head1"]])
+    for case in GOLDEN["keep"]:
+        delta = math.inf if case["delta"] == "inf" else float(case["delta"])
+        _, _, est, kept = fn(qb, kb, vb, [64], codes, scales, delta=delta,
+                             num_splits=case["num_splits"], max_seq_len=64)
+        assert kept[0, 0, :4].astype(int).tolist() == case["kept"], case
+        want = logit * 1.4426950408889634
+        assert np.allclose(est[0, :, :4], want,
+                           rtol=GOLDEN["est_tol_rel"], atol=0), case
+
+
+def check_estimate_error_bound(fn):
+    """|est * ln 2 - T| <= the quantization bound, T = the block's largest
+    logit over its attended tokens (float64 from the bf16 values). With
+    amax_q = 127 s_q, amax_j = 7 scale_j, each key off its code by at most
+    scale_j / 2 and the query by s_q / 2, a dot product moves by at most
+    D * s_q * scale_j * (127/2 + 7/2 + 1/4), and so does a maximum."""
+    for seed, D, L, lens in ((65, 64, 160, (160, 97)), (66, 128, 96, (96,))):
+        a, codes, scales = _case(seed, B=len(lens), Hq=4, Hkv=2, D=D, L=L,
+                                 lens=lens)
+        _, _, est, _ = fn(a["q"], a["k"], a["v"], a["seq_lens"], codes,
+                          scales, delta=1.0, num_splits=2, max_seq_len=L)
+        q = oracle.decode_values(a["q"], "bf16")
+        k = oracle.decode_values(a["k"], "bf16")
+        sc = 1.0 / math.sqrt(D)
+        checked = 0
+        for b, n in enumerate(lens):
+            for h in range(4):
+                sq = np.abs(q[b, h]).max() / 127.0
+                for j in range(-(-n // 16)):
+                    rows = k[b, h // 2, 16 * j:min(16 * j + 16, n)]
+                    sj = np.abs(rows).max() / 7.0
+                    T = sc * (rows @ q[b, h]).max()
+                    bound = sc * D * sq * sj * 67.25 * (1 + 1e-5) \
+                        + 1e-6 * abs(T) + 1e-30
+                    assert abs(float(est[b, h, j]) * math.log(2) - T) \
+                        <= bound, (seed, b, h, j)
+                    checked += 1
+        assert checked > 20
+
+
 CHECKS = [check_dense_limit, check_one_block_per_split_is_dense,
-          check_brute_force_keep, check_masked_sdpa, check_keep_invariants]
+          check_brute_force_keep, check_masked_sdpa, check_keep_invariants,
+          check_hand_derived_keep, check_estimate_error_bound]
 
 
 def test_reference_passes_every_check():
@@ -266,7 +349,9 @@ def _mutant(kind):
                     for g in range(G):
                         e = np.float32(np.float32(red[g]) * qq[g][1])
                         e = np.float32(e * sj)
-                        est[b, kvh * G + g, j] = np.float32(e * sl2)
+                        est[b, kvh * G + g, j] = (
+                            e if kind == "no_logit_scale"
+                            else np.float32(e * sl2))
                 for s_ in range(num_splits):
                     j0 = s_ * P // 16
                     j1 = -(-min((s_ + 1) * P, n) // 16)
@@ -281,6 +366,8 @@ def _mutant(kind):
                                       keepdims=True).astype(np.float32)
                     d2 = osp.log2_units(delta) if math.isfinite(delta) \
                         else np.float32(np.inf)
+                    if kind == "delta_not_converted":
+                        d2 = np.float32(delta)
                     ok = e >= (M - d2).astype(np.float32)
                     kept[b, kvh, j0:j1] = (ok.all(axis=0) if kind == "all_heads"
                                            else ok.any(axis=0))
@@ -297,7 +384,8 @@ def _mutant(kind):
 
 
 MUTANTS = ["no_block_scale", "mean_not_max", "split_off_by_one",
-           "global_threshold", "all_heads"]
+           "global_threshold", "all_heads", "no_logit_scale",
+           "delta_not_converted"]
 
 
 def test_mutant_copy_without_mistake_passes():
@@ -317,3 +405,21 @@ def test_planted_mistake_is_caught(kind):
         except (AssertionError, IndexError, ValueError):
             failed.append(chk.__name__)
     assert failed, f"mutant {kind} passed every sparse pin"
+
+
+@pytest.mark.parametrize("kind", ["no_logit_scale", "delta_not_converted"])
+def test_unit_mistakes_caught_without_the_restatement(kind):
+    """The estimate's units and delta's conversion are pinned by the
+    hand-derived cases and the error bound, not only by the brute-force
+    check that restates the oracle's own arithmetic."""
+    fn = _mutant(kind)
+    failed = []
+    for chk in CHECKS:
+        if chk is check_brute_force_keep:
+            continue
+        try:
+            with np.errstate(all="ignore"):
+                chk(fn)
+        except (AssertionError, IndexError, ValueError):
+            failed.append(chk.__name__)
+    assert failed, f"mutant {kind} passed every pin but the restatement"
