@@ -182,6 +182,26 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
  * fd_decode_attn_int8.) */
 
 /*
+ * fd_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the partials go to a 4 MiB
+ * array the library keeps on each device it runs on (from the first such
+ * call on that device until the process ends). The call allocates nothing.
+ *
+ * Arguments, outputs and errors as for fd_decode_attn, plus
+ * FD_ERR_WORKSPACE (nothing launched) when the call's workspace
+ * (fd_workspace_size) would exceed 4 MiB (4194304 bytes), and FD_ERR_HIP if
+ * the array's device address cannot be obtained. Every call on a device
+ * shares that device's array: calls that overlap on one device (other
+ * streams, other threads) race and give wrong results; serialise them.
+ */
+int fd_decode_attn_noalloc(const fd_shape* shape, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table,
+                           const int32_t* seq_lens, int num_splits,
+                           float* out, float* lse_out, void* stream);
+
+/*
  * The split step alone: per split s, the partial output of attention over
  * that split's positions, normalised by its own softmax sum, and its
  * log-sum-exp (the per-piece result of slavadubrov.com, "Why decode needs a

@@ -32,7 +32,7 @@ SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_decode_attn",
            "fd_decode_partials_fp8", "fd_decode_attn_int8",
            "fd_decode_partials_int8", "fd_build_key_summary",
            "fd_decode_attn_sparse", "fd_combine_partials", "fd_status_str",
-           "fd_version", "fd_read_probe"]
+           "fd_version", "fd_read_probe", "fd_decode_attn_noalloc"]
 
 
 class FdShape(ctypes.Structure):
@@ -91,6 +91,7 @@ def load() -> ctypes.CDLL:
     lib.fd_status_str.restype = ctypes.c_char_p
     lib.fd_version.argtypes = []
     lib.fd_read_probe.argtypes = [P, SZ, I, I, I, P, P]
+    lib.fd_decode_attn_noalloc.argtypes = [SH, P, P, P, P, P, I, P, P, P]
     for name in SYMBOLS:
         if name != "fd_status_str":
             getattr(lib, name).restype = ctypes.c_int
@@ -160,6 +161,16 @@ def fd_decode_attn(shape: FdShape, q, k_cache, v_cache, block_table, seq_lens,
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_table), _ptr(seq_lens), int(num_splits), _ptr(workspace),
         ws_bytes, _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def fd_decode_attn_noalloc(shape: FdShape, q, k_cache, v_cache,
+                           block_table, seq_lens, num_splits: int, out,
+                           lse_out=None, stream=None) -> None:
+    """fd_decode_attn with the library's per-device scratch (no workspace)."""
+    _check("fd_decode_attn_noalloc", load().fd_decode_attn_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens), int(num_splits), _ptr(out),
+        _ptr(lse_out), _stream(stream)))
 
 
 def fd_decode_partials(shape: FdShape, q, k_cache, v_cache, block_table,

@@ -343,6 +343,25 @@ int fd_decode_attn(const fd_shape* shape, const void* q, const void* k_cache,
                      out, lse_out, stream);
 }
 
+int fd_decode_attn_noalloc(const fd_shape* shape, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_table,
+                           const int32_t* seq_lens, int num_splits,
+                           float* out, float* lse_out, void* stream) {
+  Shape s;
+  int st = check_shape(shape, &s);
+  if (st != FD_OK) return st;
+  st = check_splits(s, num_splits);
+  if (st != FD_OK) return st;
+  const size_t need = workspace_bytes(s, num_splits);
+  if (need > kScratchBytes) return FD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && scratch_address(&ws) != 0) return FD_ERR_HIP;
+  return decode_attn(shape, q, k_cache, v_cache, nullptr, nullptr, -1,
+                     block_table, seq_lens, num_splits, ws, need, out,
+                     lse_out, stream);
+}
+
 int fd_decode_attn_fp8(const fd_shape* shape, const void* q,
                        const void* k_cache, const void* v_cache,
                        const float* k_scale, const float* v_scale,

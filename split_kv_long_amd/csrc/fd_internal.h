@@ -33,6 +33,9 @@ constexpr int kMaxSplits = 65535;
 constexpr int kMaxBlockSize = 4096;
 constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves
 constexpr int kMaxSparseSplit = 8192;   // sparse path: tokens per split
+// Device-resident scratch of fd_decode_attn_noalloc (one array per device):
+// the largest workspace it serves.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
 
 // A validated, resolved call shape.
 struct Shape {
@@ -99,6 +102,9 @@ struct SparseArgs {
 int launch_split(const Shape& s, const SplitArgs& a, void* stream);
 int launch_combine(int D, const CombineArgs& a, void* stream);
 int launch_summary(const Shape& s, const SummaryArgs& a, void* stream);
+// Device address of the current device's scratch array (looked up once per
+// device); returns a hipError_t as int.
+int scratch_address(void** ptr);
 int launch_sparse(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                   void* stream);
 

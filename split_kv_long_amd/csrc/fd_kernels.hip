@@ -31,6 +31,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fd_device.h"
@@ -1030,6 +1031,32 @@ int launch_split(const Shape& s, const SplitArgs& a, void* stream) {
       hipLaunchKernelGGL((split_f32<64>), grid, block, 0, st, a);
   }
   return (int)hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Scratch for fd_decode_attn_noalloc: the partials of one call live in this
+// array instead of a caller's workspace. Each device holds its own copy
+// (until the process ends); host code never uses the array's name as an
+// address, only the pointer hipGetSymbolAddress returns for the current
+// device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return (int)hipErrorInvalidDevice;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int launch_combine(int D, const CombineArgs& a, void* stream) {

@@ -75,6 +75,13 @@ int launch_split(const Shape& s, const SplitArgs& a, void*) {
   return 0;
 }
 
+// The allocation-free entry point's scratch: a fake device address.
+static const uintptr_t kScratchAddr = 0x7e0000000000ull;
+int scratch_address(void** ptr) {
+  *ptr = (void*)kScratchAddr;
+  return 0;
+}
+
 int launch_combine(int D, const CombineArgs& c, void*) {
   ++g_launches;
   EXPECT(D == 64 || D == 128);
@@ -177,7 +184,7 @@ int main() {
     const bool paged = s.block_size > 0;
     const int32_t* tbl = paged ? bt : nullptr;
     const long before = g_launches;
-    const int which = (int)(rnd() % 7);
+    const int which = (int)(rnd() % 8);
     if (which == 1 || which == 6) g_ws = 0;   // caller's own partials
     int st;
     switch (which) {
@@ -204,6 +211,14 @@ int main() {
         st = fd_decode_attn_sparse(&s, q, k, v, codes, cscales, tbl, lens,
                                    (rnd() % 2) ? 3.f : INFINITY, S, (void*)ws,
                                    g_ws_bytes, out, lse, nullptr, nullptr);
+        break;
+      case 7:                                   // partials in the scratch
+        g_ws = fd::kScratchAddr;
+        g_ws_bytes = fd::kScratchBytes;
+        st = fd_decode_attn_noalloc(&s, q, k, v, tbl, lens, S, out, lse,
+                                    nullptr);
+        if (wst == FD_OK && bytes > fd::kScratchBytes)
+          EXPECT(st == FD_ERR_WORKSPACE);
         break;
       default:
         st = fd_combine_partials(s.batch, s.num_q_heads, s.head_dim, S,

@@ -445,3 +445,23 @@ def test_c_caller_links_and_runs_host_calls(tmp_path):
     assert lines[0] == f"splits 128 workspace {ws} version {fb.fd_version()}"
     assert lines[1] == "status ok | " + fb.fd_status_str(fb.FD_ERR_WORKSPACE)
     assert lines[2] == f"head_dim 96 -> {fb.FD_ERR_UNSUPPORTED}"
+
+
+def test_noalloc_entry_point_refuses_oversized_calls():
+    """The allocation-free call serves workspaces up to 4 MiB; a larger one
+    is refused on the host (FD_ERR_WORKSPACE) before any device access."""
+    s = fb.make_shape(64, 32, 8, 128, 1024)
+    assert fb.fd_workspace_size(s, 8) > 4 << 20
+    with pytest.raises(fb.FdError) as e:
+        fb.fd_decode_attn_noalloc(s, 16, 16, 16, None, 16, 8, 16, None,
+                                  stream=0)
+    assert e.value.status == fb.FD_ERR_WORKSPACE
+    # bad shapes and split counts keep their own codes
+    with pytest.raises(fb.FdError) as e:
+        fb.fd_decode_attn_noalloc(fb.make_shape(1, 3, 2, 128, 64), 16, 16,
+                                  16, None, 16, 2, 16, None, stream=0)
+    assert e.value.status == fb.FD_ERR_INVALID_ARG
+    with pytest.raises(fb.FdError) as e:
+        fb.fd_decode_attn_noalloc(fb.make_shape(1, 2, 2, 128, 64), 16, 16,
+                                  16, None, 16, 0, 16, None, stream=0)
+    assert e.value.status == fb.FD_ERR_INVALID_ARG
