@@ -339,12 +339,14 @@ int fd_build_key_summary(const fd_shape* shape, const void* k_cache,
  *
  *   delta      >= 0, natural-log units (not NaN)
  *   num_splits as for fd_decode_attn, with at most 8192 tokens per split
- *              (FD_ERR_UNSUPPORTED otherwise)
+ *              and tokens per split x max(16, Hq / Hkv) <= 131072 (the
+ *              block estimates of a split live in on-chip memory);
+ *              FD_ERR_UNSUPPORTED otherwise
  *   kept_out   device uint8 [batch, Hkv, ceil(max_seq_len/16)] receiving
  *              1 (kept) / 0 for every block holding an attended token
  *              (other entries untouched), or NULL
  * Supported: bf16 (shape->dtype FD_DTYPE_BF16), head_dim 64 / 128, at most
- * 16 query heads per kv head. Other arguments as for fd_decode_attn.
+ * 128 query heads per kv head. Other arguments as for fd_decode_attn.
  */
 int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
                           const void* k_cache, const void* v_cache,

@@ -457,11 +457,13 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
   Shape s;
   int st = check_shape(shape, &s);
   if (st != FD_OK) return st;
-  if (s.dtype != FD_DTYPE_BF16 || s.G > kHeadsPerGroup)
+  if (s.dtype != FD_DTYPE_BF16 || s.G > kMaxSparseG)
     return FD_ERR_UNSUPPORTED;
   st = check_splits(s, num_splits);
   if (st != FD_OK) return st;
-  if (tokens_per_split(s, num_splits) > kMaxSparseSplit)
+  const int64_t P = tokens_per_split(s, num_splits);
+  if (P > kMaxSparseSplit ||
+      P * (s.G > kHeadsPerGroup ? s.G : kHeadsPerGroup) > kMaxSparseEst)
     return FD_ERR_UNSUPPORTED;
   st = check_inputs(s, q, k_cache, v_cache, block_table, seq_lens);
   if (st != FD_OK) return st;

@@ -33,6 +33,10 @@ constexpr int kMaxSplits = 65535;
 constexpr int kMaxBlockSize = 4096;
 constexpr int kHeadsPerGroup = 16;   // query heads one workgroup serves
 constexpr int kMaxSparseSplit = 8192;   // sparse path: tokens per split
+constexpr int kMaxSparseG = 128;        // sparse path: query heads per kv head
+// Sparse path: tokens per split x max(16, query heads per kv head), the
+// block estimates one workgroup keeps in LDS.
+constexpr int kMaxSparseEst = kMaxSparseSplit * kHeadsPerGroup;
 // Device-resident scratch of fd_decode_attn_noalloc (one array per device):
 // the largest workspace it serves.
 constexpr size_t kScratchBytes = (size_t)4 << 20;

@@ -18,12 +18,15 @@
 //                       + D/8 - 1 hold piece p (dims D/4 * p ..) of row n, so
 //                       every lane's request is contiguous with its
 //                       neighbours'.
-//   split_sparse<D, NW, GM, PAGED>
+//   split_sparse<D, NW, GM, PAGED, CHUNK, MULTI>
 //                       one workgroup per (split, kv head, sequence):
 //                       phase 1 scans the split's summary blocks (8-bit
 //                       query x 4-bit codes, exact, on the int8 matrix
 //                       cores), phase 2 keeps blocks per top-delta, phase 3
 //                       runs exact bf16 attention over the kept blocks.
+//                       A kv head with more than GM query heads is served
+//                       GM heads at a time in phases 1 and 3 (the keep
+//                       decision in phase 2 needs every head's estimates).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -125,6 +128,9 @@ __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
 // Sparse split kernel.
 
 constexpr int kMaxSparseBlocks = kMaxSparseSplit / kSumBlock;
+// Estimates held in LDS: blocks per split x query heads per kv head (the
+// host bounds tokens per split x heads per kv head accordingly).
+constexpr int kMaxSparseEstimates = kMaxSparseEst / kSumBlock;
 
 // Lane layout as in the dense MFMA kernel (lane l: n = l % 16, j = l / 16;
 // S^T = K * Q^T so a lane holds one head n and tokens 4j..4j+3 of a 16-token
@@ -133,16 +139,18 @@ constexpr int kMaxSparseBlocks = kMaxSparseSplit / kSumBlock;
 // query bytes of each lane follow the order its code bytes arrive in, and
 // since every (lane group, byte) pair names one k-slot of the product for
 // both operands alike, the sum runs over every dim exactly once.
-template <int D, int NW, int GM, bool PAGED, int CHUNK>
+template <int D, int NW, int GM, bool PAGED, int CHUNK, bool MULTI>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void split_sparse(SplitArgs a, SparseArgs sp) {
   constexpr int KC = D / 32;
   constexpr int NV = D / 16;
   constexpr int DP = D + 4;
   constexpr int CB = D / 8;                    // code bytes per lane per row
-  __shared__ float est_s[kMaxSparseBlocks][GM];
-  __shared__ float wmax_s[NW][GM];
-  __shared__ float thr_s[GM];                  // per-head keep threshold
+  constexpr int HMAX = MULTI ? kMaxSparseG : GM;   // heads per kv head
+  __shared__ float est_s[MULTI ? kMaxSparseEstimates
+                               : kMaxSparseBlocks * GM];  // [block][head]
+  __shared__ float wmax_s[NW][HMAX];
+  __shared__ float thr_s[HMAX];                // per-head keep threshold
   __shared__ int cnt_s[NW];                    // kept blocks per wave slice
   __shared__ int16_t list_s[kMaxSparseBlocks]; // kept blocks, ascending
   static_assert(NW * 64 >= kMaxSparseBlocks, "one block per thread");
@@ -157,6 +165,7 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   const int G = a.G, Hkv = a.Hkv, L = a.L, bs = a.bs;
   const int h0 = kvh * G;
   const int nh = G;
+  const int nhg = MULTI ? (G + GM - 1) / GM : 1;   // passes of GM heads
   const int lo = s * a.P;
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > L ? L : len);
@@ -190,8 +199,12 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
            (t - page * bs) / kSumBlock;
   };
 
-  const int qh = h0 + (n < nh ? n : 0);        // padded columns reuse head h0
-  const uint16_t* qrow = Q + ((size_t)b * a.Hq + qh) * D;
+  // Query row of lane column n in the pass over heads hb .. hb + GM - 1;
+  // padded columns reuse the pass's first head.
+  auto q_row = [&](int hb, int ng) -> const uint16_t* {
+    const int qh = h0 + hb + (n < ng ? n : 0);
+    return Q + ((size_t)b * a.Hq + qh) * D;
+  };
 
   // ---- phase 1: scan the summary -----------------------------------------
   // The query is rounded to 8 bits per head (q8 = rint(q * 127 / amax_q));
@@ -199,7 +212,9 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   // and the block estimate is ((float(max dot) * s_q) * scale_blk) *
   // scale_log2, the same float32 operations in the same order as the
   // reference, so every keep decision is reproduced exactly.
-  {
+  for (int hg = 0; hg < nhg; ++hg) {
+    const int hb = hg * GM, ng = min(GM, G - hb);
+    const uint16_t* qrow = q_row(hb, ng);
     constexpr int SD = D / 4;                  // scan dims per lane group
     constexpr int NG = SD / 8;                 // 8-dim groups per lane
     constexpr int KM = D / 64;                 // int8 MFMA calls per tile
@@ -304,7 +319,7 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         float e = (float)(dm >> 4) * s_q;      // block max, reference order
         e = e * bscale[u];
         e = e * a.scale_log2;                  // base-2 logit units
-        if (j == 0 && n < GM) est_s[jl][n] = e;
+        if (j == 0 && n < ng) est_s[jl * G + hb + n] = e;
         wmax = fmaxf(wmax, e);
       }
     };
@@ -332,14 +347,14 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
       scan_chunk(jl0, cwB, bsB, lrB);
       jl0 = jn;
     }
-    if (j == 0 && n < GM) wmax_s[w][n] = wmax;
+    if (j == 0 && n < ng) wmax_s[w][hb + n] = wmax;
   }
   __syncthreads();
 
   // ---- phase 2: top-delta inside the split --------------------------------
   // Thread t decides block t (a split has at most NW * 64 blocks) and the
   // kept blocks are compacted, in ascending order, into list_s.
-  if (threadIdx.x < GM) {
+  if ((int)threadIdx.x < G) {
     const int h = threadIdx.x;
     float M = wmax_s[0][h];
 #pragma unroll
@@ -352,7 +367,7 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
     const int jl = threadIdx.x;
     bool keep = false;
     if (jl < nb) {
-      for (int h = 0; h < nh; ++h) keep |= est_s[jl][h] >= thr_s[h];
+      for (int h = 0; h < nh; ++h) keep |= est_s[jl * G + h] >= thr_s[h];
       if (sp.kept_out)
         sp.kept_out[(size_t)(b * Hkv + kvh) * sp.nblk_row + jg0 + jl] =
             keep ? 1 : 0;
@@ -377,153 +392,161 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   __syncthreads();
 
   // ---- phase 3: exact attention over the kept blocks ----------------------
-  bf16x8 qf[KC];
+  for (int hg = 0; hg < nhg; ++hg) {
+    const int hb = hg * GM, ng = min(GM, G - hb);
+    const uint16_t* qrow = q_row(hb, ng);
+    bf16x8 qf[KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c)
-    qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 8 * j + 32 * c));
-  f32x4 o[NV];
+    for (int c = 0; c < KC; ++c)
+      qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 8 * j + 32 * c));
+    f32x4 o[NV];
 #pragma unroll
-  for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
 
-  // Wave w takes kept blocks 2w, 2w + 1, then 2(w + NW), ... in pairs.
-  for (int k = 2 * w; k < nkept; k += 2 * NW) {
-    const int ja = __builtin_amdgcn_readfirstlane((int)list_s[k]);
-    const int jb = k + 1 < nkept                // -1: second half masked
-                       ? __builtin_amdgcn_readfirstlane((int)list_s[k + 1])
-                       : -1;
-    const int ta = lo + ja * kSumBlock;
-    const int tb = jb >= 0 ? lo + jb * kSumBlock : ta;
-    const int lasta = min(kSumBlock, hi - ta) - 1;
-    const int lastb = jb >= 0 ? min(kSumBlock, hi - tb) - 1 : lasta;
-    const size_t ra = row_of(ta), rb = row_of(tb);
-    // Rows of a page block are consecutive (16 | page size).
-    const uint16_t* K0 = K + ra * D;
-    const uint16_t* K1 = K + rb * D;
-    const uint16_t* V0 = V + ra * D;
-    const uint16_t* V1 = V + rb * D;
-    u32x4 kr[2][KC], vr[8];
-    const unsigned r0 = (unsigned)(min(n, lasta) * D + 8 * j);
-    const unsigned r1 = (unsigned)(min(n, lastb) * D + 8 * j);
+    // Wave w takes kept blocks 2w, 2w + 1, then 2(w + NW), ... in pairs.
+    for (int k = 2 * w; k < nkept; k += 2 * NW) {
+      const int ja = __builtin_amdgcn_readfirstlane((int)list_s[k]);
+      const int jb = k + 1 < nkept                // -1: second half masked
+                         ? __builtin_amdgcn_readfirstlane((int)list_s[k + 1])
+                         : -1;
+      const int ta = lo + ja * kSumBlock;
+      const int tb = jb >= 0 ? lo + jb * kSumBlock : ta;
+      const int lasta = min(kSumBlock, hi - ta) - 1;
+      const int lastb = jb >= 0 ? min(kSumBlock, hi - tb) - 1 : lasta;
+      const size_t ra = row_of(ta), rb = row_of(tb);
+      // Rows of a page block are consecutive (16 | page size).
+      const uint16_t* K0 = K + ra * D;
+      const uint16_t* K1 = K + rb * D;
+      const uint16_t* V0 = V + ra * D;
+      const uint16_t* V1 = V + rb * D;
+      u32x4 kr[2][KC], vr[8];
+      const unsigned r0 = (unsigned)(min(n, lasta) * D + 8 * j);
+      const unsigned r1 = (unsigned)(min(n, lastb) * D + 8 * j);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      kr[0][c] = ld16<true>(K0 + r0 + 32 * c);
-      kr[1][c] = ld16<true>(K1 + r1 + 32 * c);
+      for (int c = 0; c < KC; ++c) {
+        kr[0][c] = ld16<true>(K0 + r0 + 32 * c);
+        kr[1][c] = ld16<true>(K1 + r1 + 32 * c);
+      }
+      const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vr[e] = ld16<true>(V0 + (unsigned)(min(4 * j + e, lasta) * D + vcol));
+        vr[4 + e] = ld16<true>(V1 + (unsigned)(min(4 * j + e, lastb) * D + vcol));
+      }
+      f32x4 sacc[2];
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg) {
+        sacc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(kr[tg][c]), qf[c], sacc[tg], 0, 0, 0);
+      }
+      float sv[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          const bool ok = tg == 0 ? r <= lasta : (jb >= 0 && r <= lastb);
+          const float x = ok ? sacc[tg][i] * a.scale_log2 : -INFINITY;
+          sv[4 * tg + i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = max_x32(max_x16(mx));
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = fexp2(m_run - mn);     // m_run = -inf: 0
+      m_run = mn;
+      bf16x8 ph, pl;
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fexp2(sv[e] - mn);
+        psum += p;
+        const __bf16 hb = (__bf16)p;
+        ph[e] = hb;
+        pl[e] = (__bf16)(p - (float)hb);
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int cc = 0; cc < NV; ++cc) {
+        o[cc] *= alpha;
+        const bf16x8 vk = v_kvec<D>(vr, cc, n);
+        o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, ph, o[cc], 0, 0, 0);
+        o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, pl, o[cc], 0, 0, 0);
+      }
     }
-    const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vr[e] = ld16<true>(V0 + (unsigned)(min(4 * j + e, lasta) * D + vcol));
-      vr[4 + e] = ld16<true>(V1 + (unsigned)(min(4 * j + e, lastb) * D + vcol));
-    }
-    f32x4 sacc[2];
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg) {
-      sacc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-        sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(kr[tg][c]), qf[c], sacc[tg], 0, 0, 0);
-    }
-    float sv[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg)
+
+    // ---- merge the waves (as in the dense kernel) ---------------------------
+    l_run = sum_x32(sum_x16(l_run));
+    if (n < ng) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 4 * j + i;
-        const bool ok = tg == 0 ? r <= lasta : (jb >= 0 && r <= lastb);
-        const float x = ok ? sacc[tg][i] * a.scale_log2 : -INFINITY;
-        sv[4 * tg + i] = x;
-        mx = fmaxf(mx, x);
+        float* rowp = &mo[w][n][out_dim<D>(0, i, j)];
+        *reinterpret_cast<f32x4*>(rowp) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
+        if (D == 128)
+          *reinterpret_cast<f32x4*>(rowp + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
       }
-    mx = max_x32(max_x16(mx));
-    const float mn = fmaxf(m_run, mx);
-    const float alpha = fexp2(m_run - mn);     // m_run = -inf: 0
-    m_run = mn;
-    bf16x8 ph, pl;
-    float psum = 0.f;
+      if (j == 0) {
+        mm[w][n] = m_run;
+        ml[w][n] = l_run;
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ng * (D / 4); idx += NW * 64) {
+      const int g = idx / (D / 4);
+      const int d = 4 * (idx - g * (D / 4));
+      float Mx = mm[0][g];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fexp2(sv[e] - mn);
-      psum += p;
-      const __bf16 hb = (__bf16)p;
-      ph[e] = hb;
-      pl[e] = (__bf16)(p - (float)hb);
-    }
-    l_run = l_run * alpha + psum;
+      for (int ww = 1; ww < NW; ++ww) Mx = fmaxf(Mx, mm[ww][g]);
+      const float Ms = Mx == -INFINITY ? 0.f : Mx;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      float lsum = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < NV; ++cc) {
-      o[cc] *= alpha;
-      const bf16x8 vk = v_kvec<D>(vr, cc, n);
-      o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, ph, o[cc], 0, 0, 0);
-      o[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vk, pl, o[cc], 0, 0, 0);
+      for (int ww = 0; ww < NW; ++ww) {
+        const float wt = fexp2(mm[ww][g] - Ms);
+        acc += wt * *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
+        lsum += wt * ml[ww][g];
+      }
+      const bool none = Mx == -INFINITY;
+      *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + hb + g, s) + d) =
+          none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / lsum);
+      if (d == 0) {
+        float* l = lse_dst(a, b, h0 + hb + g, s);
+        if (l) *l = none ? -INFINITY : (Mx + flog2(lsum)) * kLn2;
+      }
     }
-  }
-
-  // ---- merge the waves (as in the dense kernel) ---------------------------
-  l_run = sum_x32(sum_x16(l_run));
-  if (n < nh) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* rowp = &mo[w][n][out_dim<D>(0, i, j)];
-      *reinterpret_cast<f32x4*>(rowp) = f32x4{o[0][i], o[1][i], o[2][i], o[3][i]};
-      if (D == 128)
-        *reinterpret_cast<f32x4*>(rowp + 4) = f32x4{o[4][i], o[5][i], o[6][i], o[7][i]};
-    }
-    if (j == 0) {
-      mm[w][n] = m_run;
-      ml[w][n] = l_run;
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
-    const int g = idx / (D / 4);
-    const int d = 4 * (idx - g * (D / 4));
-    float Mx = mm[0][g];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) Mx = fmaxf(Mx, mm[ww][g]);
-    const float Ms = Mx == -INFINITY ? 0.f : Mx;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float wt = fexp2(mm[ww][g] - Ms);
-      acc += wt * *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
-      lsum += wt * ml[ww][g];
-    }
-    const bool none = Mx == -INFINITY;
-    *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) =
-        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / lsum);
-    if (d == 0) {
-      float* l = lse_dst(a, b, h0 + g, s);
-      if (l) *l = none ? -INFINITY : (Mx + flog2(lsum)) * kLn2;
-    }
+    if (hg + 1 < nhg) __syncthreads();       // mo is reused by the next pass
   }
 }
 
 // Blocks a wave requests per scan round: 8 for splits of 2048 tokens or
 // more (256K, cold summary: 35.3 -> 33.2 us), else 4 (a 512-token split
 // gives each wave only 4 blocks; 8 measured 3 % slower at 64K).
-template <int D, int GM, bool PAGED>
+// MULTI: more than GM query heads per kv head (served GM at a time).
+template <int D, int GM, bool PAGED, bool MULTI>
 void launch_sparse_gm(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                       hipStream_t st) {
   const dim3 grid((unsigned)s.Hkv, (unsigned)s.B, (unsigned)a.S);
   if (a.P >= 2048)
-    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 8>), grid, dim3(8 * 64),
-                       0, st, a, sp);
+    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 8, MULTI>), grid,
+                       dim3(8 * 64), 0, st, a, sp);
   else
-    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 4>), grid, dim3(8 * 64),
-                       0, st, a, sp);
+    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 4, MULTI>), grid,
+                       dim3(8 * 64), 0, st, a, sp);
 }
 
 template <int D, bool PAGED>
 void launch_sparse_d(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                      hipStream_t st) {
   if (s.G <= 8)
-    launch_sparse_gm<D, 8, PAGED>(s, a, sp, st);
+    launch_sparse_gm<D, 8, PAGED, false>(s, a, sp, st);
+  else if (s.G <= 16)
+    launch_sparse_gm<D, 16, PAGED, false>(s, a, sp, st);
   else
-    launch_sparse_gm<D, 16, PAGED>(s, a, sp, st);
+    launch_sparse_gm<D, 16, PAGED, true>(s, a, sp, st);
 }
 
 }  // namespace

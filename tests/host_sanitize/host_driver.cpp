@@ -109,6 +109,9 @@ int launch_sparse(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
   ++g_launches;
   check_split_args(s, a);
   EXPECT(a.P <= kMaxSparseSplit);
+  EXPECT(s.G <= kMaxSparseG);
+  EXPECT((int64_t)a.P * (s.G > kHeadsPerGroup ? s.G : kHeadsPerGroup) <=
+         kMaxSparseEst);
   EXPECT(sp.codes && sp.scales && sp.delta_log2 >= 0.f);
   EXPECT(sp.nblk_row == ((int64_t)s.L + 15) / 16);
   return 0;

@@ -300,11 +300,16 @@ def test_sparse_and_summary_reject_bad_args():
     assert sparse(delta=-1.0) == fb.FD_ERR_INVALID_ARG
     assert sparse(delta=float("nan")) == fb.FD_ERR_INVALID_ARG
     assert sparse(ws_bytes=10) == fb.FD_ERR_WORKSPACE
-    # more than 8192 tokens per split, more than 16 query heads per kv head,
-    # fp32 or E4M3 caches: not supported on this path
+    # more than 8192 tokens per split, more than 128 query heads per kv
+    # head, more than 131072 (tokens per split x heads per kv head), fp32 or
+    # E4M3 caches: not supported on this path
     assert sparse(shape=shp(max_seq_len=16384), S=1) == fb.FD_ERR_UNSUPPORTED
-    assert sparse(shape=shp(max_seq_len=8192, num_q_heads=64, num_kv_heads=2)
-                  ) == fb.FD_ERR_UNSUPPORTED
+    assert sparse(shape=shp(max_seq_len=8192, num_q_heads=258, num_kv_heads=2),
+                  S=64) == fb.FD_ERR_UNSUPPORTED
+    assert sparse(shape=shp(max_seq_len=8192, num_q_heads=64, num_kv_heads=2),
+                  S=1) == fb.FD_ERR_UNSUPPORTED               # 8192 x 32
+    assert sparse(shape=shp(max_seq_len=8192, num_q_heads=256, num_kv_heads=2),
+                  S=4) == fb.FD_ERR_UNSUPPORTED               # 2048 x 128
     assert sparse(shape=shp(max_seq_len=8192, dtype="f32")) == fb.FD_ERR_UNSUPPORTED
     assert sparse(shape=shp(max_seq_len=8192, dtype="fp8_e4m3")
                   ) == fb.FD_ERR_UNSUPPORTED

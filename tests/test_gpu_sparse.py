@@ -241,3 +241,17 @@ def test_sparse_random_shapes():
                            poison_tail=True)
         check_sparse(w, rng.choice([0.0, 0.5, 2.0, 5.0]),
                      rng.choice([1, 2, 3, 5, 8]), expect_dropped=False)
+
+
+@pytest.mark.parametrize("d,hq,hkv,L,S,paged", [
+    (128, 64, 2, 4000, 2, False),    # 32 heads per kv head: two passes
+    (64, 40, 2, 3000, 3, True),      # 20: a full pass and a partial one
+    (128, 128, 1, 2048, 2, False),   # 128 heads, 1024 tokens per split
+    (128, 20, 1, 4000, 1, True),     # one split, the output written directly
+])
+def test_sparse_more_than_16_heads_per_kv_head(d, hq, hkv, L, S, paged):
+    # A kv head with more query heads than one pass serves: the keep
+    # decision takes every head's estimates, attention runs pass by pass.
+    w = sparse_case(86, paged, d=d, hq=hq, hkv=hkv, L=L,
+                    lens=[L, 17, L // 2 + 5])
+    check_sparse(w, 2.0, S, expect_dropped=False)
