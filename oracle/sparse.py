@@ -33,6 +33,12 @@ The page defines neither the quantizer nor the rule; the readings taken here
 * result: exact softmax attention (as ``decode_attention``) over the tokens
   of every kept block; delta = +inf keeps every block and gives the dense
   result.
+* an E4M3 cache (codes with one float32 scale per kv head for K and one
+  for V): the summary quantizes the keys as float32(decode(code) * k_scale)
+  -- the exact product rounded once to float32, the precision in which
+  both implementations take every decision -- and the rest is unchanged;
+  the exact attention runs over the dequantized cache, decode(code) times
+  its scale in float64 (as ``decode_attention``).
 """
 
 from __future__ import annotations
@@ -51,7 +57,25 @@ BLOCK = 16
 def quantize_block(rows_bf16_bits) -> Tuple[np.ndarray, np.float32]:
     """One block's attended key rows (bf16 bit patterns, [n, D]) ->
     (int codes [n, D], float32 scale), per the reading above."""
-    x = decode_values(rows_bf16_bits, "bf16").astype(np.float32)
+    return quantize_block_values(
+        decode_values(rows_bf16_bits, "bf16").astype(np.float32))
+
+
+def summary_keys(rows, kv_dtype: str = "bf16", k_scale=None) -> np.ndarray:
+    """Key rows as the summary sees them, float32: bf16 exactly; E4M3 as
+    float32(decode(code) * k_scale) (one rounding of the exact product)."""
+    if kv_dtype == "bf16":
+        return decode_values(rows, "bf16").astype(np.float32)
+    if kv_dtype == "fp8_e4m3":
+        x = decode_values(rows, "fp8_e4m3").astype(np.float32)
+        return (x * np.float32(k_scale)).astype(np.float32)
+    raise ValueError(f"no key summary for {kv_dtype!r} caches")
+
+
+def quantize_block_values(x) -> Tuple[np.ndarray, np.float32]:
+    """One block's attended key rows as float32 values [n, D] -> (int
+    codes [n, D], float32 scale), per the reading above."""
+    x = np.asarray(x, dtype=np.float32)
     amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
     if amax == 0:
         return np.zeros(x.shape, dtype=np.int64), np.float32(0)
@@ -79,12 +103,15 @@ def log2_units(x: float) -> np.float32:
     return np.float32(float(np.float32(x)) * 1.4426950408889634)
 
 
-def key_summary(k, seq_lens, block_table=None, block_size: int = 0):
+def key_summary(k, seq_lens, block_table=None, block_size: int = 0,
+                kv_dtype: str = "bf16", k_scale=None):
     """Codes (int, same layout as k) and scales for every attended block.
 
     Contiguous k [B, Hkv, L, D]: scales [B, Hkv, ceil(L/16)].
     Paged pool [NB, Hkv, bs, D]: scales [NB, Hkv, bs/16] (sub-block s of a
     page covers its slots 16s..16s+15). Unattended rows/blocks stay 0.
+    k holds bf16 bit patterns, or E4M3 codes (kv_dtype "fp8_e4m3") with
+    k_scale [Hkv].
     """
     paged = block_table is not None and block_size
     codes = np.zeros(k.shape, dtype=np.int64)
@@ -102,7 +129,8 @@ def key_summary(k, seq_lens, block_table=None, block_size: int = 0):
                 lo, hi = j * BLOCK, min((j + 1) * BLOCK, n)
                 rows = history_rows(k, b, kvh, lo, hi, block_table,
                                     block_size)
-                c, s = quantize_block(rows)
+                ks = None if k_scale is None else np.asarray(k_scale)[kvh]
+                c, s = quantize_block_values(summary_keys(rows, kv_dtype, ks))
                 if paged:
                     pos = np.arange(lo, hi)
                     blk = np.asarray(block_table)[b, pos // block_size]
@@ -149,10 +177,12 @@ def block_scale(scales, b, kvh, j, block_table=None, block_size: int = 0):
 def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
                             num_splits: int, max_seq_len: int,
                             scale: Optional[float] = None, block_table=None,
-                            block_size: int = 0):
+                            block_size: int = 0, kv_dtype: str = "bf16",
+                            k_scale=None, v_scale=None):
     """Block-sparse decode (readings in the module docstring).
 
-    q [B, Hq, D] bf16 bits; k, v bf16 bits (contiguous or paged);
+    q [B, Hq, D] bf16 bits; k, v bf16 bits or E4M3 codes (kv_dtype
+    "fp8_e4m3", with k_scale / v_scale [Hkv]), contiguous or paged;
     codes int (layout of k), scales as ``key_summary`` returns.
     Returns out [B, Hq, D], lse [B, Hq], est [B, Hq, nblk] (float32 values
     in base-2 units; NaN where no block), kept [B, Hkv, nblk] (bool), with
@@ -205,11 +235,15 @@ def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
             if not toks:
                 continue
             kr = np.concatenate([decode_values(history_rows(
-                k, b, kvh, t, t + 1, block_table, block_size), "bf16")
+                k, b, kvh, t, t + 1, block_table, block_size), kv_dtype)
                 for t in toks])
             vr = np.concatenate([decode_values(history_rows(
-                v, b, kvh, t, t + 1, block_table, block_size), "bf16")
+                v, b, kvh, t, t + 1, block_table, block_size), kv_dtype)
                 for t in toks])
+            if k_scale is not None:
+                kr = kr * np.asarray(k_scale, dtype=np.float64)[kvh]
+            if v_scale is not None:
+                vr = vr * np.asarray(v_scale, dtype=np.float64)[kvh]
             o, l = softmax_attention(sc * (qf[b, heads] @ kr.T), vr)
             out[b, heads] = o
             lse[b, heads] = l

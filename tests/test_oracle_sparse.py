@@ -423,3 +423,70 @@ def test_unit_mistakes_caught_without_the_restatement(kind):
         except (AssertionError, IndexError, ValueError):
             failed.append(chk.__name__)
     assert failed, f"mutant {kind} passed every pin but the restatement"
+
+
+# ------------------------------------------------------------- E4M3 caches
+# Every E4M3 value is a bf16 value, and a power-of-two scale only moves the
+# exponent, so with such scales the E4M3 path must reproduce the bf16 path
+# (pinned above) on the dequantized values exactly: the same summary codes,
+# scales equal to the bf16 summary's, the same estimates and kept sets, the
+# same result.
+
+KS = np.array([2.0 ** -3, 2.0 ** 2])      # per kv head
+VS = np.array([2.0 ** 1, 2.0 ** -4])
+
+
+def _e4m3_view(seed, lens=(200, 77), L=200, paged=False):
+    w = workloads.make("sp8", seed=seed, batch=len(lens), num_q_heads=4,
+                       num_kv_heads=2, head_dim=32, max_seq_len=L,
+                       seq_lens=list(lens), needles=[3, L // 2],
+                       needle_logit=12.0, kv_dtype="fp8_e4m3", paged=paged)
+    return w.numpy_view()
+
+
+def _bf16_equivalent(codes, per_head):
+    """E4M3 codes times a power of two per kv head (axis 1), as bf16 bits."""
+    x = oracle.fp8_e4m3_to_f64(codes) * per_head[None, :, None, None]
+    return _bf16(x)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_e4m3_summary_is_the_bf16_summary_of_the_scaled_keys(paged):
+    a = _e4m3_view(61, paged=paged)
+    bt, bs = a["block_table"], a["block_size"] if paged else 0
+    c8, s8 = osp.key_summary(a["k"], a["seq_lens"], bt, bs,
+                             kv_dtype="fp8_e4m3", k_scale=KS)
+    kb = _bf16_equivalent(a["k"], KS)
+    cb, sb = osp.key_summary(kb, a["seq_lens"], bt, bs)
+    assert np.array_equal(c8, cb)
+    assert np.array_equal(s8, sb)
+    assert np.any(s8 != 0)
+    # Planted mistake: the key scale left out of the summary. The codes do
+    # not see it (they are scale-free), the block scales do.
+    _, s_bad = osp.key_summary(a["k"], a["seq_lens"], bt, bs,
+                               kv_dtype="fp8_e4m3", k_scale=np.ones(2))
+    assert not np.array_equal(s_bad, sb)
+
+
+@pytest.mark.parametrize("delta,S", [(0.5, 1), (2.0, 3), (math.inf, 2)])
+def test_e4m3_sparse_attention_equals_bf16_on_the_same_values(delta, S):
+    a = _e4m3_view(62)
+    c8, s8 = osp.key_summary(a["k"], a["seq_lens"], kv_dtype="fp8_e4m3",
+                             k_scale=KS)
+    r8 = osp.sparse_decode_attention(
+        a["q"], a["k"], a["v"], a["seq_lens"], c8, s8, delta=delta,
+        num_splits=S, max_seq_len=200, scale=a["scale"],
+        kv_dtype="fp8_e4m3", k_scale=KS, v_scale=VS)
+    kb, vb = _bf16_equivalent(a["k"], KS), _bf16_equivalent(a["v"], VS)
+    cb, sb = osp.key_summary(kb, a["seq_lens"])
+    rb = osp.sparse_decode_attention(
+        a["q"], kb, vb, a["seq_lens"], cb, sb, delta=delta, num_splits=S,
+        max_seq_len=200, scale=a["scale"])
+    for x8, xb in zip(r8, rb):
+        assert np.array_equal(x8, xb, equal_nan=True)
+    if math.isinf(delta):       # every block kept: the dense E4M3 oracle
+        ref = oracle.decode_attention(
+            a["q"], a["k"], a["v"], a["seq_lens"], dtype="bf16",
+            kv_dtype="fp8_e4m3", k_scale=KS, v_scale=VS, scale=a["scale"])
+        assert np.abs(r8[0] - ref[0]).max() < 1e-12
+        assert np.abs(r8[1] - ref[1]).max() < 1e-12
