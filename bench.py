@@ -600,30 +600,46 @@ def sparse_run(args):
     b = Bench(args.workload, args.splits, args.steps,
               parse_overrides(args.set), step_fraction=1 / 8)
     w, dev = b.w, torch.device("cuda")
+    if w.cache_dtype not in ("bf16", "fp8_e4m3"):
+        raise SystemExit("the block-sparse path takes bf16 or E4M3 caches")
+    f8 = w.cache_dtype == "fp8_e4m3"
     steps = max(args.steps, b.R)
     D, Hkv = w.head_dim, w.num_kv_heads
     nblk = -(-w.max_seq_len // 16)
+
+    def build_into(r, c, sc):
+        if f8:
+            fb.fd_build_key_summary_fp8(b.shape, b.ks[r], b.scales(r)[0],
+                                        b.bt, b.lens, c, sc)
+        else:
+            fb.fd_build_key_summary(b.shape, b.ks[r], b.bt, b.lens, c, sc)
     codes, scales = [], []
     for r in range(b.R):
         nrec = ((w.k.shape[0], Hkv, w.block_size // 16) if w.paged
                 else (w.batch, Hkv, nblk))
         c = torch.empty(nrec + (8 * D,), dtype=torch.uint8, device=dev)
         sc = torch.empty(nrec, device=dev)
-        fb.fd_build_key_summary(b.shape, b.ks[r], b.bt, b.lens, c, sc)
+        build_into(r, c, sc)
         codes.append(c)
         scales.append(sc)
 
     def build(i):
         r = i % b.R
-        fb.fd_build_key_summary(b.shape, b.ks[r], b.bt, b.lens, codes[r],
-                                scales[r])
+        build_into(r, codes[r], scales[r])
     kept = torch.zeros(w.batch, Hkv, nblk, dtype=torch.uint8, device=dev)
 
     def step(i):
         r = i % b.R
-        fb.fd_decode_attn_sparse(b.shape, b.q, b.ks[r], b.vs[r], codes[r],
-                                 scales[r], b.bt, b.lens, args.sparse_delta,
-                                 b.S, b.ws, b.out, b.lse, kept)
+        if f8:
+            fb.fd_decode_attn_sparse_fp8(
+                b.shape, b.q, b.ks[r], b.vs[r], *b.scales(r), codes[r],
+                scales[r], b.bt, b.lens, args.sparse_delta, b.S, b.ws, b.out,
+                b.lse, kept)
+        else:
+            fb.fd_decode_attn_sparse(b.shape, b.q, b.ks[r], b.vs[r], codes[r],
+                                     scales[r], b.bt, b.lens,
+                                     args.sparse_delta, b.S, b.ws, b.out,
+                                     b.lse, kept)
     ms, _ = time_graph(torch, step, steps, args.warmup)
     us = ms * 1e3 / steps
     ms_b, _ = time_graph(torch, build, max(1, args.steps // 4), 2)
@@ -638,7 +654,7 @@ def sparse_run(args):
             attended += n
             kept_tok += int(m[:-1].sum()) * 16 + (
                 (n - 16 * (nb - 1)) if nb and m[-1] else 0)
-    row = D * 2                                       # bf16 bytes per row
+    row = D * (1 if f8 else 2)                        # cache bytes per row
     scan = attended * D // 2 + attended // 16 * 4     # codes + scales
     bytes_read = scan + 2 * kept_tok * row + w.batch * w.num_q_heads * D * 2
     dense = 2 * attended * row
@@ -649,7 +665,8 @@ def sparse_run(args):
         "steps": steps, "warmup": args.warmup,
         "higher_is_better": False, "dtype": "bf16",
         "data": "synthetic (seeded, see workloads/)",
-        "config": {"workload": args.workload, "delta": args.sparse_delta,
+        "config": {"workload": args.workload, "kv_dtype": w.cache_dtype,
+                   "delta": args.sparse_delta,
                    "copies_rotated": b.R,
                    "num_splits": b.S, "tokens_per_split": b.P,
                    "overrides": parse_overrides(args.set)},

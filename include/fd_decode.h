@@ -358,6 +358,39 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
                           uint8_t* kept_out, void* stream);
 
 /*
+ * The same two block-sparse calls over an 8-bit float cache
+ * (shape->dtype FD_DTYPE_FP8_E4M3, codes and scales as for
+ * fd_decode_attn_fp8): the summary quantizes every attended key element as
+ * the fp32 product decode(code) * k_scale[g] (one rounding; g its kv head),
+ * otherwise exactly as fd_build_key_summary; the estimates, the top-delta
+ * rule and the result are those of fd_decode_attn_sparse, with exact
+ * attention over the dequantized cache (keys decode(code) * k_scale[g],
+ * values decode(code) * v_scale[g]). The "Faster Than Flash" abstract
+ * scans a low-bit copy of the keys; here the cache itself is low-bit too,
+ * its precision held fixed as slavadubrov.com, "Interpret the reported
+ * result", asks of comparisons.
+ *
+ *   k_scale, v_scale  device fp32 [Hkv], 4-byte aligned
+ * Other arguments, limits and layouts as for the bf16 calls. A shape of
+ * another dtype, or a missing or misaligned scale, is FD_ERR_INVALID_ARG
+ * (and an E4M3 shape passed to the bf16 calls is FD_ERR_UNSUPPORTED).
+ */
+int fd_build_key_summary_fp8(const fd_shape* shape, const void* k_cache,
+                             const float* k_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, void* codes,
+                             float* scales, void* stream);
+int fd_decode_attn_sparse_fp8(const fd_shape* shape, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const void* codes, const float* scales,
+                              const int32_t* block_table,
+                              const int32_t* seq_lens, float delta,
+                              int num_splits, void* workspace,
+                              size_t workspace_bytes, float* out,
+                              float* lse_out, uint8_t* kept_out,
+                              void* stream);
+
+/*
  * The reduction step alone: for each (b, h), with M = max_s lse_part[b,h,s],
  *   out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M},
  *   lse = M + ln sum_s e^{lse_s - M};

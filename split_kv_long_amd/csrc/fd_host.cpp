@@ -418,21 +418,36 @@ int fd_decode_partials_int8(const fd_shape* shape, const void* q,
                          o_part, lse_part, stream);
 }
 
-int fd_build_key_summary(const fd_shape* shape, const void* k_cache,
-                         const int32_t* block_table, const int32_t* seq_lens,
-                         void* codes, float* scales, void* stream) {
+// The sparse calls take bf16 caches (scaled = -1) or E4M3 caches with their
+// per-kv-head scales (scaled = FD_DTYPE_FP8_E4M3), each through its own
+// entry point.
+static int check_sparse_dtype(const Shape& s, int scaled) {
+  if (scaled < 0) return s.dtype == FD_DTYPE_BF16 ? FD_OK : FD_ERR_UNSUPPORTED;
+  return s.dtype == FD_DTYPE_FP8_E4M3 ? FD_OK : FD_ERR_INVALID_ARG;
+}
+
+static int build_key_summary(const fd_shape* shape, const void* k_cache,
+                             const float* k_scale, int scaled,
+                             const int32_t* block_table,
+                             const int32_t* seq_lens, void* codes,
+                             float* scales, void* stream) {
   Shape s;
   int st = check_shape(shape, &s);
   if (st != FD_OK) return st;
-  if (s.dtype != FD_DTYPE_BF16) return FD_ERR_UNSUPPORTED;
+  st = check_sparse_dtype(s, scaled);
+  if (st != FD_OK) return st;
   st = check_inputs(s, k_cache, k_cache, k_cache, block_table, seq_lens);
   if (st != FD_OK) return st;
+  if (scaled >= 0 &&
+      (!k_scale || (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0))
+    return FD_ERR_INVALID_ARG;
   if (!codes || !scales || !aligned16(codes) ||
       (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
     return FD_ERR_INVALID_ARG;
   SummaryArgs a;
   memset(&a, 0, sizeof(a));
-  a.k = static_cast<const uint16_t*>(k_cache);
+  a.k = k_cache;
+  a.k_scale = scaled >= 0 ? k_scale : nullptr;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.codes = static_cast<uint8_t*>(codes);
@@ -446,19 +461,36 @@ int fd_build_key_summary(const fd_shape* shape, const void* k_cache,
   return launch_summary(s, a, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 
-int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
-                          const void* k_cache, const void* v_cache,
-                          const void* codes, const float* scales,
-                          const int32_t* block_table,
-                          const int32_t* seq_lens, float delta,
-                          int num_splits, void* workspace, size_t ws_bytes,
-                          float* out, float* lse_out, uint8_t* kept_out,
-                          void* stream) {
+int fd_build_key_summary(const fd_shape* shape, const void* k_cache,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         void* codes, float* scales, void* stream) {
+  return build_key_summary(shape, k_cache, nullptr, -1, block_table, seq_lens,
+                           codes, scales, stream);
+}
+
+int fd_build_key_summary_fp8(const fd_shape* shape, const void* k_cache,
+                             const float* k_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, void* codes,
+                             float* scales, void* stream) {
+  return build_key_summary(shape, k_cache, k_scale, FD_DTYPE_FP8_E4M3,
+                           block_table, seq_lens, codes, scales, stream);
+}
+
+static int decode_attn_sparse(const fd_shape* shape, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              int scaled, const void* codes,
+                              const float* scales, const int32_t* block_table,
+                              const int32_t* seq_lens, float delta,
+                              int num_splits, void* workspace,
+                              size_t ws_bytes, float* out, float* lse_out,
+                              uint8_t* kept_out, void* stream) {
   Shape s;
   int st = check_shape(shape, &s);
   if (st != FD_OK) return st;
-  if (s.dtype != FD_DTYPE_BF16 || s.G > kMaxSparseG)
-    return FD_ERR_UNSUPPORTED;
+  st = check_sparse_dtype(s, scaled);
+  if (st != FD_OK) return st;
+  if (s.G > kMaxSparseG) return FD_ERR_UNSUPPORTED;
   st = check_splits(s, num_splits);
   if (st != FD_OK) return st;
   const int64_t P = tokens_per_split(s, num_splits);
@@ -466,6 +498,8 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
       P * (s.G > kHeadsPerGroup ? s.G : kHeadsPerGroup) > kMaxSparseEst)
     return FD_ERR_UNSUPPORTED;
   st = check_inputs(s, q, k_cache, v_cache, block_table, seq_lens);
+  if (st != FD_OK) return st;
+  st = check_scales(s, k_scale, v_scale, scaled);
   if (st != FD_OK) return st;
   if (!codes || !scales || !aligned16(codes) ||
       (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
@@ -481,6 +515,8 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
   }
   SplitArgs a = make_split_args(s, q, k_cache, v_cache, block_table, seq_lens,
                                 num_splits);
+  a.k_scale = scaled >= 0 ? k_scale : nullptr;
+  a.v_scale = scaled >= 0 ? v_scale : nullptr;
   SparseArgs sp;
   sp.codes = static_cast<const uint8_t*>(codes);
   sp.scales = scales;
@@ -510,6 +546,35 @@ int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
   c.Hq = s.Hq;
   c.S = num_splits;
   return launch_combine(s.D, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
+}
+
+int fd_decode_attn_sparse(const fd_shape* shape, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          const void* codes, const float* scales,
+                          const int32_t* block_table,
+                          const int32_t* seq_lens, float delta,
+                          int num_splits, void* workspace, size_t ws_bytes,
+                          float* out, float* lse_out, uint8_t* kept_out,
+                          void* stream) {
+  return decode_attn_sparse(shape, q, k_cache, v_cache, nullptr, nullptr, -1,
+                            codes, scales, block_table, seq_lens, delta,
+                            num_splits, workspace, ws_bytes, out, lse_out,
+                            kept_out, stream);
+}
+
+int fd_decode_attn_sparse_fp8(const fd_shape* shape, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const void* codes, const float* scales,
+                              const int32_t* block_table,
+                              const int32_t* seq_lens, float delta,
+                              int num_splits, void* workspace,
+                              size_t ws_bytes, float* out, float* lse_out,
+                              uint8_t* kept_out, void* stream) {
+  return decode_attn_sparse(shape, q, k_cache, v_cache, k_scale, v_scale,
+                            FD_DTYPE_FP8_E4M3, codes, scales, block_table,
+                            seq_lens, delta, num_splits, workspace, ws_bytes,
+                            out, lse_out, kept_out, stream);
 }
 
 int fd_combine_partials(int batch, int num_q_heads, int head_dim,

@@ -85,7 +85,8 @@ struct CombineArgs {
 
 // Key summary builder (4-bit codes + per-16-token-block scales).
 struct SummaryArgs {
-  const uint16_t* k;            // bf16 keys, contiguous or paged
+  const void* k;                // bf16 keys or E4M3 codes, contiguous or paged
+  const float* k_scale;         // E4M3: one scale per kv head; else null
   const int32_t* block_table;
   const int32_t* seq_lens;
   uint8_t* codes;               // one 8*D-byte record per 16-token block

@@ -9,7 +9,10 @@
 // through the ordinary log-sum-exp combine.
 //
 // Kernels:
-//   summary_kernel<D>   bf16 keys -> 4-bit codes (two per byte, even dim in
+//   summary_kernel<D, F8>
+//                       bf16 keys (or E4M3 codes times their kv head's
+//                       scale, rounded once to fp32)
+//                       -> 4-bit codes (two per byte, even dim in
 //                       the low nibble) + one fp32 scale per 16-token block
 //                       and kv head: scale = amax / 7, code =
 //                       rint(k * (7 / amax)). A block's codes form one
@@ -18,12 +21,15 @@
 //                       + D/8 - 1 hold piece p (dims D/4 * p ..) of row n, so
 //                       every lane's request is contiguous with its
 //                       neighbours'.
-//   split_sparse<D, NW, GM, PAGED, CHUNK, MULTI>
+//   split_sparse<D, NW, GM, PAGED, CHUNK, MULTI, F8>
 //                       one workgroup per (split, kv head, sequence):
 //                       phase 1 scans the split's summary blocks (8-bit
 //                       query x 4-bit codes, exact, on the int8 matrix
 //                       cores), phase 2 keeps blocks per top-delta, phase 3
-//                       runs exact bf16 attention over the kept blocks.
+//                       runs exact attention over the kept blocks (bf16
+//                       products; an E4M3 cache's codes are converted to
+//                       bf16 in registers, exactly, and its scales folded
+//                       into the logit scale and the output).
 //                       A kv head with more than GM query heads is served
 //                       GM heads at a time in phases 1 and 3 (the keep
 //                       decision in phase 2 needs every head's estimates).
@@ -50,7 +56,7 @@ constexpr int kSumBlock = 16;   // tokens per summary block
 // of the block and the quarter l % 4 of its dims. Blocks with no attended
 // token are skipped; rows past the length (all 16 rows of a record exist)
 // get code 0.
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
   constexpr int QD = D / 4;                  // dims per lane
   const int lane = threadIdx.x;
@@ -81,8 +87,27 @@ __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
   }
   float x[QD];
   float amax = 0.f;
-  if (valid) {
-    const uint16_t* kp = a.k + row * D + part * QD;
+  if (valid && F8) {
+    // E4M3: codes -> bf16 (exact) -> fp32, times the kv head's scale (one
+    // fp32 rounding).
+    const uint8_t* kp = static_cast<const uint8_t*>(a.k) + row * D + part * QD;
+    const float ks = a.k_scale[kvh];
+#pragma unroll
+    for (int c = 0; c < QD / 16; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(kp + 16 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 p = e4m3x4_to_bf16x4(w[e]);
+        x[16 * c + 4 * e] = __uint_as_float(p.x << 16) * ks;
+        x[16 * c + 4 * e + 1] = __uint_as_float(p.x & 0xffff0000u) * ks;
+        x[16 * c + 4 * e + 2] = __uint_as_float(p.y << 16) * ks;
+        x[16 * c + 4 * e + 3] = __uint_as_float(p.y & 0xffff0000u) * ks;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < QD; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  } else if (valid) {
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + row * D + part * QD;
 #pragma unroll
     for (int c = 0; c < QD / 8; ++c) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(kp + 8 * c);
@@ -139,7 +164,7 @@ constexpr int kMaxSparseEstimates = kMaxSparseEst / kSumBlock;
 // query bytes of each lane follow the order its code bytes arrive in, and
 // since every (lane group, byte) pair names one k-slot of the product for
 // both operands alike, the sum runs over every dim exactly once.
-template <int D, int NW, int GM, bool PAGED, int CHUNK, bool MULTI>
+template <int D, int NW, int GM, bool PAGED, int CHUNK, bool MULTI, bool F8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void split_sparse(SplitArgs a, SparseArgs sp) {
   constexpr int KC = D / 32;
@@ -176,8 +201,9 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   }
   const int nb = (hi - lo + kSumBlock - 1) / kSumBlock;   // blocks here
   const int jg0 = lo / kSumBlock;
-  const uint16_t* K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* V = static_cast<const uint16_t*>(a.v);
+  using KT = typename std::conditional<F8, uint8_t, uint16_t>::type;
+  const KT* K = static_cast<const KT*>(a.k);
+  const KT* V = static_cast<const KT*>(a.v);
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
 
   // Row index (not yet times D) of token t of (b, kvh).
@@ -392,13 +418,23 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   __syncthreads();
 
   // ---- phase 3: exact attention over the kept blocks ----------------------
+  // bf16: lane (n, j) requests 16 bytes of key row n at dims 32c + 8j. E4M3
+  // (as in the dense kernel): 16 codes at dims 64c' + 16j, which feed two
+  // products (dims 64c' + 16j and + 8), and 8 value codes per row; the
+  // query fragments follow the same dim order. The key scale joins the
+  // logit scale and the value scale the final normalisation.
+  constexpr int KL = F8 ? D / 64 : KC;         // 16-byte key requests per row
+  const float sl2 = F8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float vsc = F8 ? a.v_scale[kvh] : 1.f;
   for (int hg = 0; hg < nhg; ++hg) {
     const int hb = hg * GM, ng = min(GM, G - hb);
     const uint16_t* qrow = q_row(hb, ng);
     bf16x8 qf[KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 8 * j + 32 * c));
+    for (int c = 0; c < KC; ++c) {
+      const int d0 = F8 ? 16 * j + 64 * (c >> 1) + 8 * (c & 1) : 8 * j + 32 * c;
+      qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + d0));
+    }
     f32x4 o[NV];
 #pragma unroll
     for (int cc = 0; cc < NV; ++cc) o[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -416,32 +452,52 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
       const int lastb = jb >= 0 ? min(kSumBlock, hi - tb) - 1 : lasta;
       const size_t ra = row_of(ta), rb = row_of(tb);
       // Rows of a page block are consecutive (16 | page size).
-      const uint16_t* K0 = K + ra * D;
-      const uint16_t* K1 = K + rb * D;
-      const uint16_t* V0 = V + ra * D;
-      const uint16_t* V1 = V + rb * D;
-      u32x4 kr[2][KC], vr[8];
-      const unsigned r0 = (unsigned)(min(n, lasta) * D + 8 * j);
-      const unsigned r1 = (unsigned)(min(n, lastb) * D + 8 * j);
+      const KT* K0 = K + ra * D;
+      const KT* K1 = K + rb * D;
+      const KT* V0 = V + ra * D;
+      const KT* V1 = V + rb * D;
+      using VT = typename std::conditional<F8, u32x2, u32x4>::type;
+      u32x4 kr[2][KL];
+      VT vraw[8];
+      constexpr int KJ = F8 ? 16 : 8, KS = F8 ? 64 : 32;
+      const unsigned r0 = (unsigned)(min(n, lasta) * D + KJ * j);
+      const unsigned r1 = (unsigned)(min(n, lastb) * D + KJ * j);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        kr[0][c] = ld16<true>(K0 + r0 + 32 * c);
-        kr[1][c] = ld16<true>(K1 + r1 + 32 * c);
+      for (int c = 0; c < KL; ++c) {
+        kr[0][c] = ld16<true>(K0 + r0 + KS * c);
+        kr[1][c] = ld16<true>(K1 + r1 + KS * c);
       }
       const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vr[e] = ld16<true>(V0 + (unsigned)(min(4 * j + e, lasta) * D + vcol));
-        vr[4 + e] = ld16<true>(V1 + (unsigned)(min(4 * j + e, lastb) * D + vcol));
+        const unsigned va = (unsigned)(min(4 * j + e, lasta) * D + vcol);
+        const unsigned vb = (unsigned)(min(4 * j + e, lastb) * D + vcol);
+        if constexpr (F8) {
+          vraw[e] = ld8<true>(V0 + va);
+          vraw[4 + e] = ld8<true>(V1 + vb);
+        } else {
+          vraw[e] = ld16<true>(V0 + va);
+          vraw[4 + e] = ld16<true>(V1 + vb);
+        }
       }
       f32x4 sacc[2];
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg) {
         sacc[tg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(kr[tg][c]), qf[c], sacc[tg], 0, 0, 0);
+        for (int c = 0; c < KC; ++c) {
+          bf16x8 kop;
+          if constexpr (F8) {
+            const u32x4 x = kr[tg][c >> 1];
+            const uint2 p = e4m3x4_to_bf16x4(x[2 * (c & 1)]);
+            const uint2 q = e4m3x4_to_bf16x4(x[2 * (c & 1) + 1]);
+            kop = as_bf16x8(u32x4{p.x, p.y, q.x, q.y});
+          } else {
+            kop = as_bf16x8(kr[tg][c]);
+          }
+          sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qf[c],
+                                                             sacc[tg], 0, 0, 0);
+        }
       }
       float sv[8];
       float mx = -INFINITY;
@@ -451,7 +507,7 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i;
           const bool ok = tg == 0 ? r <= lasta : (jb >= 0 && r <= lastb);
-          const float x = ok ? sacc[tg][i] * a.scale_log2 : -INFINITY;
+          const float x = ok ? sacc[tg][i] * sl2 : -INFINITY;
           sv[4 * tg + i] = x;
           mx = fmaxf(mx, x);
         }
@@ -470,6 +526,17 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         pl[e] = (__bf16)(p - (float)hb);
       }
       l_run = l_run * alpha + psum;
+      u32x4 vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (F8) {
+          const uint2 p = e4m3x4_to_bf16x4(vraw[e][0]);
+          const uint2 q = e4m3x4_to_bf16x4(vraw[e][1]);
+          vr[e] = u32x4{p.x, p.y, q.x, q.y};
+        } else {
+          vr[e] = vraw[e];
+        }
+      }
 #pragma unroll
       for (int cc = 0; cc < NV; ++cc) {
         o[cc] *= alpha;
@@ -512,7 +579,7 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
       }
       const bool none = Mx == -INFINITY;
       *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + hb + g, s) + d) =
-          none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / lsum);
+          none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (vsc / lsum);
       if (d == 0) {
         float* l = lse_dst(a, b, h0 + hb + g, s);
         if (l) *l = none ? -INFINITY : (Mx + flog2(lsum)) * kLn2;
@@ -526,27 +593,40 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
 // more (256K, cold summary: 35.3 -> 33.2 us), else 4 (a 512-token split
 // gives each wave only 4 blocks; 8 measured 3 % slower at 64K).
 // MULTI: more than GM query heads per kv head (served GM at a time).
-template <int D, int GM, bool PAGED, bool MULTI>
+template <int D, int GM, bool PAGED, bool MULTI, bool F8>
 void launch_sparse_gm(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                       hipStream_t st) {
   const dim3 grid((unsigned)s.Hkv, (unsigned)s.B, (unsigned)a.S);
   if (a.P >= 2048)
-    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 8, MULTI>), grid,
+    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 8, MULTI, F8>), grid,
                        dim3(8 * 64), 0, st, a, sp);
   else
-    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 4, MULTI>), grid,
+    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 4, MULTI, F8>), grid,
                        dim3(8 * 64), 0, st, a, sp);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool F8>
 void launch_sparse_d(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                      hipStream_t st) {
   if (s.G <= 8)
-    launch_sparse_gm<D, 8, PAGED, false>(s, a, sp, st);
+    launch_sparse_gm<D, 8, PAGED, false, F8>(s, a, sp, st);
   else if (s.G <= 16)
-    launch_sparse_gm<D, 16, PAGED, false>(s, a, sp, st);
+    launch_sparse_gm<D, 16, PAGED, false, F8>(s, a, sp, st);
   else
-    launch_sparse_gm<D, 16, PAGED, true>(s, a, sp, st);
+    launch_sparse_gm<D, 16, PAGED, true, F8>(s, a, sp, st);
+}
+
+template <bool F8>
+void launch_sparse_dtype(const Shape& s, const SplitArgs& a,
+                         const SparseArgs& sp, hipStream_t st) {
+  const bool paged = s.bs > 0;
+  if (s.D == 128) {
+    if (paged) launch_sparse_d<128, true, F8>(s, a, sp, st);
+    else launch_sparse_d<128, false, F8>(s, a, sp, st);
+  } else {
+    if (paged) launch_sparse_d<64, true, F8>(s, a, sp, st);
+    else launch_sparse_d<64, false, F8>(s, a, sp, st);
+  }
 }
 
 }  // namespace
@@ -557,24 +637,24 @@ int launch_summary(const Shape& s, const SummaryArgs& a, void* stream) {
   // INT32_MAX)
   const dim3 grid((unsigned)a.nblk_row, (unsigned)s.Hkv, (unsigned)s.B);
   if (grid.x == 0) return 0;
-  if (s.D == 128)
-    hipLaunchKernelGGL((summary_kernel<128>), grid, dim3(64), 0, st, a);
-  else
-    hipLaunchKernelGGL((summary_kernel<64>), grid, dim3(64), 0, st, a);
+  const bool f8 = s.dtype == FD_DTYPE_FP8_E4M3;
+  if (s.D == 128) {
+    if (f8) hipLaunchKernelGGL((summary_kernel<128, true>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((summary_kernel<128, false>), grid, dim3(64), 0, st, a);
+  } else {
+    if (f8) hipLaunchKernelGGL((summary_kernel<64, true>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((summary_kernel<64, false>), grid, dim3(64), 0, st, a);
+  }
   return (int)hipGetLastError();
 }
 
 int launch_sparse(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                   void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool paged = s.bs > 0;
-  if (s.D == 128) {
-    if (paged) launch_sparse_d<128, true>(s, a, sp, st);
-    else launch_sparse_d<128, false>(s, a, sp, st);
-  } else {
-    if (paged) launch_sparse_d<64, true>(s, a, sp, st);
-    else launch_sparse_d<64, false>(s, a, sp, st);
-  }
+  if (s.dtype == FD_DTYPE_FP8_E4M3)
+    launch_sparse_dtype<true>(s, a, sp, st);
+  else
+    launch_sparse_dtype<false>(s, a, sp, st);
   return (int)hipGetLastError();
 }
 

@@ -97,7 +97,8 @@ int launch_combine(int D, const CombineArgs& c, void*) {
 
 int launch_summary(const Shape& s, const SummaryArgs& a, void*) {
   ++g_launches;
-  EXPECT(s.dtype == FD_DTYPE_BF16);
+  EXPECT(s.dtype == FD_DTYPE_BF16 || s.dtype == FD_DTYPE_FP8_E4M3);
+  EXPECT((a.k_scale != nullptr) == (s.dtype == FD_DTYPE_FP8_E4M3));
   EXPECT(a.k && a.seq_lens && a.codes && a.scales);
   EXPECT(a.nblk_row == ((int64_t)s.L + 15) / 16);
   EXPECT((a.block_table != nullptr) == (s.bs > 0));
@@ -187,7 +188,7 @@ int main() {
     const bool paged = s.block_size > 0;
     const int32_t* tbl = paged ? bt : nullptr;
     const long before = g_launches;
-    const int which = (int)(rnd() % 8);
+    const int which = (int)(rnd() % 10);
     if (which == 1 || which == 6) g_ws = 0;   // caller's own partials
     int st;
     switch (which) {
@@ -214,6 +215,16 @@ int main() {
         st = fd_decode_attn_sparse(&s, q, k, v, codes, cscales, tbl, lens,
                                    (rnd() % 2) ? 3.f : INFINITY, S, (void*)ws,
                                    g_ws_bytes, out, lse, nullptr, nullptr);
+        break;
+      case 8:
+        st = fd_build_key_summary_fp8(&s, k, ks, tbl, lens, codes, cscales,
+                                      nullptr);
+        break;
+      case 9:
+        st = fd_decode_attn_sparse_fp8(&s, q, k, v, ks, vs, codes, cscales,
+                                       tbl, lens, (rnd() % 2) ? 3.f : INFINITY,
+                                       S, (void*)ws, g_ws_bytes, out, lse,
+                                       nullptr, nullptr);
         break;
       case 7:                                   // partials in the scratch
         g_ws = fd::kScratchAddr;

@@ -314,6 +314,45 @@ def test_sparse_and_summary_reject_bad_args():
     assert sparse(shape=shp(max_seq_len=8192, dtype="fp8_e4m3")
                   ) == fb.FD_ERR_UNSUPPORTED
 
+    # The E4M3 calls: an E4M3 shape with both scales, nothing else.
+    s8 = shp(max_seq_len=8192, dtype="fp8_e4m3")
+
+    def sparse8(**kw):
+        args = dict(shape=s8, q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE,
+                    codes=FAKE, scales=FAKE, bt=None, lens=FAKE, delta=4.0,
+                    S=4, ws=FAKE, ws_bytes=1 << 30, out=FAKE, lse=None,
+                    kept=None)
+        args.update(kw)
+        return lib.fd_decode_attn_sparse_fp8(
+            ctypes.byref(args["shape"]), args["q"], args["k"], args["v"],
+            args["ks"], args["vs"], args["codes"], args["scales"], args["bt"],
+            args["lens"], F(args["delta"]), args["S"], args["ws"],
+            args["ws_bytes"], args["out"], args["lse"], args["kept"], None)
+
+    def summary8(**kw):
+        args = dict(shape=s8, k=FAKE, ks=FAKE, bt=None, lens=FAKE,
+                    codes=FAKE, scales=FAKE)
+        args.update(kw)
+        return lib.fd_build_key_summary_fp8(
+            ctypes.byref(args["shape"]), args["k"], args["ks"], args["bt"],
+            args["lens"], args["codes"], args["scales"], None)
+
+    assert sparse8(ks=None) == fb.FD_ERR_INVALID_ARG
+    assert sparse8(vs=None) == fb.FD_ERR_INVALID_ARG
+    assert sparse8(ks=FAKE + 2) == fb.FD_ERR_INVALID_ARG
+    assert sparse8(shape=s) == fb.FD_ERR_INVALID_ARG          # bf16 shape
+    assert sparse8(shape=shp(max_seq_len=8192, dtype="int8")
+                   ) == fb.FD_ERR_INVALID_ARG
+    assert sparse8(codes=None) == fb.FD_ERR_INVALID_ARG
+    assert sparse8(delta=float("nan")) == fb.FD_ERR_INVALID_ARG
+    assert sparse8(ws_bytes=10) == fb.FD_ERR_WORKSPACE
+    assert sparse8(shape=shp(max_seq_len=16384, dtype="fp8_e4m3"), S=1
+                   ) == fb.FD_ERR_UNSUPPORTED
+    assert summary8(ks=None) == fb.FD_ERR_INVALID_ARG
+    assert summary8(ks=FAKE + 1) == fb.FD_ERR_INVALID_ARG
+    assert summary8(shape=s) == fb.FD_ERR_INVALID_ARG         # bf16 shape
+    assert summary8(codes=FAKE + 8) == fb.FD_ERR_INVALID_ARG
+
     def summary(**kw):
         args = dict(shape=s, k=FAKE, bt=None, lens=FAKE, codes=FAKE,
                     scales=FAKE)

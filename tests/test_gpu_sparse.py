@@ -1,5 +1,6 @@
 """Parity of the block-sparse path (key summary + top-delta + exact attention
-over kept blocks) against the float64 oracle (needs a gfx950 GPU).
+over kept blocks) against the float64 oracle (needs a gfx950 GPU), over bf16
+caches and over E4M3 caches with per-kv-head scales.
 
 * The key summary is integer work decided in fp32 on both sides: codes and
   scales must match the oracle bit for bit.
@@ -43,17 +44,31 @@ def gpu_summary(w, t):
         nrec = (w.batch, w.num_kv_heads, -(-w.max_seq_len // 16))
     codes = torch.full(nrec + (8 * D,), 0xAA, dtype=torch.uint8, device=d)
     scales = torch.full(nrec, -1.0, device=d)
-    print(f"[gpu] summary {w.name} paged={w.paged} D={D}", flush=True)
-    fb.fd_build_key_summary(shape_of(w), t["k"], t["bt"], t["lens"], codes,
-                            scales)
+    print(f"[gpu] summary {w.name} {w.cache_dtype} paged={w.paged} D={D}",
+          flush=True)
+    if w.cache_dtype == "fp8_e4m3":
+        fb.fd_build_key_summary_fp8(shape_of(w), t["k"], t["ks"], t["bt"],
+                                    t["lens"], codes, scales)
+    else:
+        fb.fd_build_key_summary(shape_of(w), t["k"], t["bt"], t["lens"],
+                                codes, scales)
     torch.cuda.synchronize()
     return codes, scales
+
+
+def oracle_summary(w):
+    a = w.numpy_view()
+    return osp.key_summary(a["k"], a["seq_lens"], a["block_table"],
+                           w.block_size, kv_dtype=w.cache_dtype,
+                           k_scale=a["k_scale"])
 
 
 def device_inputs(w):
     d = torch.device("cuda")
     return dict(q=w.q.to(d), k=w.k.to(d), v=w.v.to(d), lens=w.seq_lens.to(d),
-                bt=None if w.block_table is None else w.block_table.to(d))
+                bt=None if w.block_table is None else w.block_table.to(d),
+                ks=None if w.k_scale is None else w.k_scale.to(d),
+                vs=None if w.v_scale is None else w.v_scale.to(d))
 
 
 def written_records(w):
@@ -77,18 +92,19 @@ def written_records(w):
     return tuple(np.array(x) for x in zip(*rec)), row
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("d", [128, 64])
-def test_summary_matches_oracle_bitwise(paged, d):
+def test_summary_matches_oracle_bitwise(paged, d, kv):
     lens = [1, 15, 16, 17, 100, 0, 333]
     w = workloads.make("sum", seed=71, batch=len(lens), num_q_heads=8,
                        num_kv_heads=2, head_dim=d, max_seq_len=333,
-                       paged=paged, seq_lens=lens, poison_tail=True)
+                       paged=paged, seq_lens=lens, poison_tail=True,
+                       kv_dtype=None if kv == "bf16" else kv)
     t = device_inputs(w)
     codes, scales = gpu_summary(w, t)
     a = w.numpy_view()
-    ref_c, ref_s = osp.key_summary(a["k"], a["seq_lens"], a["block_table"],
-                                   w.block_size)
+    ref_c, ref_s = oracle_summary(w)
     got = codes.cpu().numpy()
     recs, rows = written_records(w)
     L = w.max_seq_len
@@ -116,13 +132,14 @@ def test_summary_matches_oracle_bitwise(paged, d):
                 assert np.float32(s_got) == np.float32(s_ref), (b, kvh, j)
 
 
-def sparse_case(seed, paged, d=128, hq=16, hkv=2, L=8192, lens=None):
+def sparse_case(seed, paged, d=128, hq=16, hkv=2, L=8192, lens=None,
+                kv=None):
     lens = lens or [L]
     return workloads.make("sparse", seed=seed, batch=len(lens),
                           num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                           max_seq_len=L, paged=paged, seq_lens=lens,
                           needles=[5, L // 3, L // 2 + 7, lens[-1] - 1],
-                          needle_logit=14.0, poison_tail=True)
+                          needle_logit=14.0, poison_tail=True, kv_dtype=kv)
 
 
 def run_sparse(w, t, codes, scales, delta, S):
@@ -135,10 +152,17 @@ def run_sparse(w, t, codes, scales, delta, S):
     shape = shape_of(w)
     nbytes = fb.fd_workspace_size(shape, S)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=d)
-    print(f"[gpu] sparse {w.name} paged={w.paged} D={D} delta={delta} S={S}",
+    print(f"[gpu] sparse {w.name} {w.cache_dtype} paged={w.paged} D={D} "
+          f"G={w.num_q_heads // w.num_kv_heads} delta={delta} S={S}",
           flush=True)
-    fb.fd_decode_attn_sparse(shape, t["q"], t["k"], t["v"], codes, scales,
-                             t["bt"], t["lens"], delta, S, ws, out, lse, kept)
+    if w.cache_dtype == "fp8_e4m3":
+        fb.fd_decode_attn_sparse_fp8(shape, t["q"], t["k"], t["v"], t["ks"],
+                                     t["vs"], codes, scales, t["bt"],
+                                     t["lens"], delta, S, ws, out, lse, kept)
+    else:
+        fb.fd_decode_attn_sparse(shape, t["q"], t["k"], t["v"], codes,
+                                 scales, t["bt"], t["lens"], delta, S, ws,
+                                 out, lse, kept)
     torch.cuda.synchronize()
     return (out.cpu().double().numpy(), lse.cpu().double().numpy(),
             kept.cpu().numpy())
@@ -148,13 +172,13 @@ def check_sparse(w, delta, S, expect_dropped=True):
     t = device_inputs(w)
     codes, scales = gpu_summary(w, t)
     a = w.numpy_view()
-    ref_c, ref_s = osp.key_summary(a["k"], a["seq_lens"], a["block_table"],
-                                   w.block_size)
+    ref_c, ref_s = oracle_summary(w)
     out, lse, kept = run_sparse(w, t, codes, scales, delta, S)
     ro, rl, est, rkept = osp.sparse_decode_attention(
         a["q"], a["k"], a["v"], a["seq_lens"], ref_c, ref_s, delta=delta,
         num_splits=S, max_seq_len=w.max_seq_len, scale=w.scale,
-        block_table=a["block_table"], block_size=a["block_size"])
+        block_table=a["block_table"], block_size=a["block_size"],
+        kv_dtype=w.cache_dtype, k_scale=a["k_scale"], v_scale=a["v_scale"])
     for b in range(w.batch):
         n = int(a["seq_lens"][b])
         nb = -(-n // 16)
@@ -255,3 +279,26 @@ def test_sparse_more_than_16_heads_per_kv_head(d, hq, hkv, L, S, paged):
     w = sparse_case(86, paged, d=d, hq=hq, hkv=hkv, L=L,
                     lens=[L, 17, L // 2 + 5])
     check_sparse(w, 2.0, S, expect_dropped=False)
+
+
+@pytest.mark.parametrize("paged,S,d,hq,hkv", [
+    (False, 4, 128, 16, 2), (True, 1, 128, 16, 2), (True, 3, 64, 12, 3),
+    (False, 2, 128, 32, 1)])
+def test_sparse_e4m3_cache_matches_oracle(paged, S, d, hq, hkv):
+    # E4M3 codes with per-kv-head scales, NaN codes in every unattended
+    # slot: the same kept sets as the oracle, outputs at the bf16 bar.
+    w = sparse_case(87, paged, d=d, hq=hq, hkv=hkv, L=4000,
+                    lens=[4000, 17, 2500], kv="fp8_e4m3")
+    check_sparse(w, 1.5, S, expect_dropped=False)
+
+
+def test_sparse_e4m3_delta_inf_is_the_dense_e4m3_result():
+    w = sparse_case(88, False, L=3000, lens=[3000, 1234], kv="fp8_e4m3")
+    out, lse, kept = check_sparse(w, math.inf, 2, expect_dropped=False)
+    assert np.all(kept[kept != 7] == 1)
+    a = w.numpy_view()
+    ref = oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                  dtype="bf16", kv_dtype="fp8_e4m3",
+                                  k_scale=a["k_scale"], v_scale=a["v_scale"],
+                                  scale=w.scale)
+    assert np.abs(out - ref[0]).max() <= TOL
