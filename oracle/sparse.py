@@ -33,12 +33,14 @@ The page defines neither the quantizer nor the rule; the readings taken here
 * result: exact softmax attention (as ``decode_attention``) over the tokens
   of every kept block; delta = +inf keeps every block and gives the dense
   result.
-* an E4M3 cache (codes with one float32 scale per kv head for K and one
-  for V): the summary quantizes the keys as float32(decode(code) * k_scale)
-  -- the exact product rounded once to float32, the precision in which
-  both implementations take every decision -- and the rest is unchanged;
-  the exact attention runs over the dequantized cache, decode(code) times
-  its scale in float64 (as ``decode_attention``).
+* an 8-bit cache -- E4M3 codes with one float32 scale per kv head for K
+  and one for V, or int8 codes with one float32 scale per (position, kv
+  head) for each -- : the summary quantizes the keys as
+  float32(decode(code) * k_scale) -- the exact product rounded once to
+  float32, the precision in which both implementations take every
+  decision -- and the rest is unchanged; the exact attention runs over the
+  dequantized cache, decode(code) times its scale in float64 (as
+  ``decode_attention``).
 """
 
 from __future__ import annotations
@@ -48,8 +50,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .attention import decode_values, history_rows, softmax_attention, \
-    split_length
+from .attention import decode_values, history_rows, scale_rows, \
+    softmax_attention, split_length
 
 BLOCK = 16
 
@@ -62,13 +64,15 @@ def quantize_block(rows_bf16_bits) -> Tuple[np.ndarray, np.float32]:
 
 
 def summary_keys(rows, kv_dtype: str = "bf16", k_scale=None) -> np.ndarray:
-    """Key rows as the summary sees them, float32: bf16 exactly; E4M3 as
-    float32(decode(code) * k_scale) (one rounding of the exact product)."""
+    """Key rows as the summary sees them, float32: bf16 exactly; an 8-bit
+    cache as float32(decode(code) * scale) (one rounding of the exact
+    product). k_scale: the kv head's scale (E4M3) or a column of the rows'
+    scales [n, 1] (int8)."""
     if kv_dtype == "bf16":
         return decode_values(rows, "bf16").astype(np.float32)
-    if kv_dtype == "fp8_e4m3":
-        x = decode_values(rows, "fp8_e4m3").astype(np.float32)
-        return (x * np.float32(k_scale)).astype(np.float32)
+    if kv_dtype in ("fp8_e4m3", "int8"):
+        x = decode_values(rows, kv_dtype).astype(np.float32)
+        return (x * np.asarray(k_scale, dtype=np.float32)).astype(np.float32)
     raise ValueError(f"no key summary for {kv_dtype!r} caches")
 
 
@@ -110,8 +114,9 @@ def key_summary(k, seq_lens, block_table=None, block_size: int = 0,
     Contiguous k [B, Hkv, L, D]: scales [B, Hkv, ceil(L/16)].
     Paged pool [NB, Hkv, bs, D]: scales [NB, Hkv, bs/16] (sub-block s of a
     page covers its slots 16s..16s+15). Unattended rows/blocks stay 0.
-    k holds bf16 bit patterns, or E4M3 codes (kv_dtype "fp8_e4m3") with
-    k_scale [Hkv].
+    k holds bf16 bit patterns, E4M3 codes (kv_dtype "fp8_e4m3") with
+    k_scale [Hkv], or int8 codes (kv_dtype "int8") with per-position
+    k_scale laid out as ``scale_rows`` reads it.
     """
     paged = block_table is not None and block_size
     codes = np.zeros(k.shape, dtype=np.int64)
@@ -129,7 +134,13 @@ def key_summary(k, seq_lens, block_table=None, block_size: int = 0,
                 lo, hi = j * BLOCK, min((j + 1) * BLOCK, n)
                 rows = history_rows(k, b, kvh, lo, hi, block_table,
                                     block_size)
-                ks = None if k_scale is None else np.asarray(k_scale)[kvh]
+                if k_scale is None:
+                    ks = None
+                elif np.ndim(k_scale) == 1:
+                    ks = np.asarray(k_scale)[kvh]
+                else:
+                    ks = scale_rows(k_scale, b, kvh, lo, hi, block_table,
+                                    block_size)
                 c, s = quantize_block_values(summary_keys(rows, kv_dtype, ks))
                 if paged:
                     pos = np.arange(lo, hi)
@@ -181,9 +192,10 @@ def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
                             k_scale=None, v_scale=None):
     """Block-sparse decode (readings in the module docstring).
 
-    q [B, Hq, D] bf16 bits; k, v bf16 bits or E4M3 codes (kv_dtype
-    "fp8_e4m3", with k_scale / v_scale [Hkv]), contiguous or paged;
-    codes int (layout of k), scales as ``key_summary`` returns.
+    q [B, Hq, D] bf16 bits; k, v bf16 bits, E4M3 codes (kv_dtype
+    "fp8_e4m3", with k_scale / v_scale [Hkv]) or int8 codes (kv_dtype
+    "int8", per-position scales), contiguous or paged; codes int (layout of
+    k), scales as ``key_summary`` returns.
     Returns out [B, Hq, D], lse [B, Hq], est [B, Hq, nblk] (float32 values
     in base-2 units; NaN where no block), kept [B, Hkv, nblk] (bool), with
     nblk = ceil(L / 16).
@@ -241,9 +253,13 @@ def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
                 v, b, kvh, t, t + 1, block_table, block_size), kv_dtype)
                 for t in toks])
             if k_scale is not None:
-                kr = kr * np.asarray(k_scale, dtype=np.float64)[kvh]
+                kr = kr * np.concatenate([scale_rows(
+                    k_scale, b, kvh, t, t + 1, block_table, block_size)
+                    for t in toks])
             if v_scale is not None:
-                vr = vr * np.asarray(v_scale, dtype=np.float64)[kvh]
+                vr = vr * np.concatenate([scale_rows(
+                    v_scale, b, kvh, t, t + 1, block_table, block_size)
+                    for t in toks])
             o, l = softmax_attention(sc * (qf[b, heads] @ kr.T), vr)
             out[b, heads] = o
             lse[b, heads] = l

@@ -490,3 +490,75 @@ def test_e4m3_sparse_attention_equals_bf16_on_the_same_values(delta, S):
             kv_dtype="fp8_e4m3", k_scale=KS, v_scale=VS, scale=a["scale"])
         assert np.abs(r8[0] - ref[0]).max() < 1e-12
         assert np.abs(r8[1] - ref[1]).max() < 1e-12
+
+
+# ------------------------------------------------------------- int8 caches
+# An int8 code has at most 8 significant bits, so code x 2^e is a bf16
+# value: with power-of-two per-position scales the int8 path must equal the
+# bf16 path on the dequantized values exactly, as for E4M3 above.
+
+def _int8_view(seed, paged=False, lens=(200, 77), L=200):
+    w = workloads.make("sp8", seed=seed, batch=len(lens), num_q_heads=4,
+                       num_kv_heads=2, head_dim=32, max_seq_len=L,
+                       seq_lens=list(lens), needles=[3, L // 2],
+                       needle_logit=12.0, kv_dtype="int8", paged=paged)
+    a = w.numpy_view()
+    rng = np.random.default_rng(seed)
+    a["k_scale"] = 2.0 ** rng.integers(-6, 3, size=a["k_scale"].shape)
+    a["v_scale"] = 2.0 ** rng.integers(-6, 3, size=a["v_scale"].shape)
+    return a
+
+
+def _bf16_per_position(codes, scale):
+    """int8 codes times their per-position scale (cache layout without
+    head_dim, rows possibly padded), as bf16 bits."""
+    n = codes.shape[2]
+    x = oracle.int8_to_f64(codes) * scale[:, :, :n, None]
+    return _bf16(x)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_int8_summary_is_the_bf16_summary_of_the_scaled_keys(paged):
+    a = _int8_view(63, paged=paged)
+    bt, bs = a["block_table"], a["block_size"] if paged else 0
+    c8, s8 = osp.key_summary(a["k"], a["seq_lens"], bt, bs, kv_dtype="int8",
+                             k_scale=a["k_scale"])
+    cb, sb = osp.key_summary(_bf16_per_position(a["k"], a["k_scale"]),
+                             a["seq_lens"], bt, bs)
+    assert np.array_equal(c8, cb)
+    assert np.array_equal(s8, sb)
+    assert np.any(s8 != 0)
+    # Planted mistake: every position takes its neighbour's scale.
+    shifted = np.roll(a["k_scale"], 1, axis=2)
+    c_bad, s_bad = osp.key_summary(a["k"], a["seq_lens"], bt, bs,
+                                   kv_dtype="int8", k_scale=shifted)
+    assert not (np.array_equal(c_bad, cb) and np.array_equal(s_bad, sb))
+
+
+@pytest.mark.parametrize("delta,S,paged", [(0.5, 1, False), (2.0, 3, True),
+                                           (math.inf, 2, False)])
+def test_int8_sparse_attention_equals_bf16_on_the_same_values(delta, S, paged):
+    a = _int8_view(64, paged=paged)
+    bt, bs = a["block_table"], a["block_size"] if paged else 0
+    c8, s8 = osp.key_summary(a["k"], a["seq_lens"], bt, bs, kv_dtype="int8",
+                             k_scale=a["k_scale"])
+    r8 = osp.sparse_decode_attention(
+        a["q"], a["k"], a["v"], a["seq_lens"], c8, s8, delta=delta,
+        num_splits=S, max_seq_len=200, scale=a["scale"], block_table=bt,
+        block_size=bs, kv_dtype="int8", k_scale=a["k_scale"],
+        v_scale=a["v_scale"])
+    kb = _bf16_per_position(a["k"], a["k_scale"])
+    vb = _bf16_per_position(a["v"], a["v_scale"])
+    cb, sb = osp.key_summary(kb, a["seq_lens"], bt, bs)
+    rb = osp.sparse_decode_attention(
+        a["q"], kb, vb, a["seq_lens"], cb, sb, delta=delta, num_splits=S,
+        max_seq_len=200, scale=a["scale"], block_table=bt, block_size=bs)
+    for x8, xb in zip(r8, rb):
+        assert np.array_equal(x8, xb, equal_nan=True)
+    if math.isinf(delta):       # every block kept: the dense int8 oracle
+        ref = oracle.decode_attention(
+            a["q"], a["k"], a["v"], a["seq_lens"], dtype="bf16",
+            kv_dtype="int8", k_scale=a["k_scale"], v_scale=a["v_scale"],
+            scale=a["scale"], block_table=bt, block_size=bs)
+        assert np.abs(r8[0] - ref[0]).max() < 1e-12
+        assert np.abs(r8[1] - ref[1]).max() < 1e-12
