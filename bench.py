@@ -600,17 +600,19 @@ def sparse_run(args):
     b = Bench(args.workload, args.splits, args.steps,
               parse_overrides(args.set), step_fraction=1 / 8)
     w, dev = b.w, torch.device("cuda")
-    if w.cache_dtype not in ("bf16", "fp8_e4m3"):
-        raise SystemExit("the block-sparse path takes bf16 or E4M3 caches")
-    f8 = w.cache_dtype == "fp8_e4m3"
+    q8 = {"fp8_e4m3": "fp8", "int8": "int8"}.get(w.cache_dtype)
+    if q8 is None and w.cache_dtype != "bf16":
+        raise SystemExit("the block-sparse path takes bf16, E4M3 or int8 "
+                         "caches")
+    f8 = q8 is not None
     steps = max(args.steps, b.R)
     D, Hkv = w.head_dim, w.num_kv_heads
     nblk = -(-w.max_seq_len // 16)
 
     def build_into(r, c, sc):
         if f8:
-            fb.fd_build_key_summary_fp8(b.shape, b.ks[r], b.scales(r)[0],
-                                        b.bt, b.lens, c, sc)
+            getattr(fb, "fd_build_key_summary_" + q8)(
+                b.shape, b.ks[r], b.scales(r)[0], b.bt, b.lens, c, sc)
         else:
             fb.fd_build_key_summary(b.shape, b.ks[r], b.bt, b.lens, c, sc)
     codes, scales = [], []
@@ -631,7 +633,7 @@ def sparse_run(args):
     def step(i):
         r = i % b.R
         if f8:
-            fb.fd_decode_attn_sparse_fp8(
+            getattr(fb, "fd_decode_attn_sparse_" + q8)(
                 b.shape, b.q, b.ks[r], b.vs[r], *b.scales(r), codes[r],
                 scales[r], b.bt, b.lens, args.sparse_delta, b.S, b.ws, b.out,
                 b.lse, kept)
@@ -655,6 +657,8 @@ def sparse_run(args):
             kept_tok += int(m[:-1].sum()) * 16 + (
                 (n - 16 * (nb - 1)) if nb and m[-1] else 0)
     row = D * (1 if f8 else 2)                        # cache bytes per row
+    if q8 == "int8":
+        row += 4                                      # its per-position scale
     scan = attended * D // 2 + attended // 16 * 4     # codes + scales
     bytes_read = scan + 2 * kept_tok * row + w.batch * w.num_q_heads * D * 2
     dense = 2 * attended * row

@@ -391,6 +391,38 @@ int fd_decode_attn_sparse_fp8(const fd_shape* shape, const void* q,
                               void* stream);
 
 /*
+ * The same two block-sparse calls over an int8 cache with one fp32 scale
+ * per (position, kv head) (shape->dtype FD_DTYPE_INT8; codes and scales
+ * laid out as for fd_decode_attn_int8): the summary quantizes every
+ * attended key element as the fp32 product code * k_scale[position] (one
+ * rounding), and the result is exact attention over the dequantized cache
+ * (keys code * k_scale, values code * v_scale, per position), otherwise as
+ * fd_decode_attn_sparse.
+ *
+ *   k_scale, v_scale  device fp32, contiguous [batch, Hkv, Lp] with
+ *                     Lp = ceil(max_seq_len / 16) * 16, paged
+ *                     [num_blocks, Hkv, block_size]; 16-byte aligned for
+ *                     the sparse call, 4-byte for the summary
+ * Other arguments, limits and layouts as for the bf16 calls; errors as for
+ * the E4M3 calls.
+ */
+int fd_build_key_summary_int8(const fd_shape* shape, const void* k_cache,
+                              const float* k_scale,
+                              const int32_t* block_table,
+                              const int32_t* seq_lens, void* codes,
+                              float* scales, void* stream);
+int fd_decode_attn_sparse_int8(const fd_shape* shape, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const void* codes, const float* scales,
+                               const int32_t* block_table,
+                               const int32_t* seq_lens, float delta,
+                               int num_splits, void* workspace,
+                               size_t workspace_bytes, float* out,
+                               float* lse_out, uint8_t* kept_out,
+                               void* stream);
+
+/*
  * The reduction step alone: for each (b, h), with M = max_s lse_part[b,h,s],
  *   out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M},
  *   lse = M + ln sum_s e^{lse_s - M};

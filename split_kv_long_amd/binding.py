@@ -33,7 +33,8 @@ SYMBOLS = ["fd_plan_splits", "fd_workspace_size", "fd_decode_attn",
            "fd_decode_partials_int8", "fd_build_key_summary",
            "fd_decode_attn_sparse", "fd_combine_partials", "fd_status_str",
            "fd_version", "fd_read_probe", "fd_decode_attn_noalloc",
-           "fd_build_key_summary_fp8", "fd_decode_attn_sparse_fp8"]
+           "fd_build_key_summary_fp8", "fd_decode_attn_sparse_fp8",
+           "fd_build_key_summary_int8", "fd_decode_attn_sparse_int8"]
 
 
 class FdShape(ctypes.Structure):
@@ -87,10 +88,11 @@ def load() -> ctypes.CDLL:
     lib.fd_decode_attn_sparse.argtypes = [SH, P, P, P, P, P, P, P,
                                           ctypes.c_float, I, P, SZ, P, P, P,
                                           P]
-    lib.fd_build_key_summary_fp8.argtypes = [SH, P, P, P, P, P, P, P]
-    lib.fd_decode_attn_sparse_fp8.argtypes = [SH, P, P, P, P, P, P, P, P, P,
-                                              ctypes.c_float, I, P, SZ, P, P,
-                                              P, P]
+    for nm in ("fd_build_key_summary_fp8", "fd_build_key_summary_int8"):
+        getattr(lib, nm).argtypes = [SH, P, P, P, P, P, P, P]
+    for nm in ("fd_decode_attn_sparse_fp8", "fd_decode_attn_sparse_int8"):
+        getattr(lib, nm).argtypes = [SH, P, P, P, P, P, P, P, P, P,
+                                     ctypes.c_float, I, P, SZ, P, P, P, P]
     lib.fd_combine_partials.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.fd_status_str.argtypes = [I]
     lib.fd_status_str.restype = ctypes.c_char_p
@@ -263,12 +265,39 @@ def fd_decode_attn_sparse(shape: FdShape, q, k_cache, v_cache, codes, scales,
         _ptr(lse_out), _ptr(kept_out), _stream(stream)))
 
 
+def _summary8(name, shape, k_cache, k_scale, block_table, seq_lens, codes,
+              scales, stream):
+    _check(name, getattr(load(), name)(
+        ctypes.byref(shape), _ptr(k_cache), _ptr(k_scale), _ptr(block_table),
+        _ptr(seq_lens), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def _sparse8(name, shape, q, k_cache, v_cache, k_scale, v_scale, codes,
+             scales, block_table, seq_lens, delta, num_splits, workspace, out,
+             lse_out, kept_out, stream, workspace_bytes):
+    ws_bytes = (workspace_bytes if workspace_bytes is not None else
+                (0 if workspace is None or isinstance(workspace, int)
+                 else workspace.numel() * workspace.element_size()))
+    _check(name, getattr(load(), name)(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(codes), _ptr(scales),
+        _ptr(block_table), _ptr(seq_lens), float(delta), int(num_splits),
+        _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse_out), _ptr(kept_out),
+        _stream(stream)))
+
+
 def fd_build_key_summary_fp8(shape: FdShape, k_cache, k_scale, block_table,
                              seq_lens, codes, scales, stream=None) -> None:
     """4-bit key summary of an E4M3 key cache (keys = code x k_scale)."""
-    _check("fd_build_key_summary_fp8", load().fd_build_key_summary_fp8(
-        ctypes.byref(shape), _ptr(k_cache), _ptr(k_scale), _ptr(block_table),
-        _ptr(seq_lens), _ptr(codes), _ptr(scales), _stream(stream)))
+    _summary8("fd_build_key_summary_fp8", shape, k_cache, k_scale,
+              block_table, seq_lens, codes, scales, stream)
+
+
+def fd_build_key_summary_int8(shape: FdShape, k_cache, k_scale, block_table,
+                              seq_lens, codes, scales, stream=None) -> None:
+    """4-bit key summary of an int8 key cache with per-position scales."""
+    _summary8("fd_build_key_summary_int8", shape, k_cache, k_scale,
+              block_table, seq_lens, codes, scales, stream)
 
 
 def fd_decode_attn_sparse_fp8(shape: FdShape, q, k_cache, v_cache, k_scale,
@@ -277,15 +306,22 @@ def fd_decode_attn_sparse_fp8(shape: FdShape, q, k_cache, v_cache, k_scale,
                               lse_out=None, kept_out=None, stream=None,
                               workspace_bytes: Optional[int] = None) -> None:
     """Block-sparse decode over an E4M3 cache with per-kv-head scales."""
-    ws_bytes = (workspace_bytes if workspace_bytes is not None else
-                (0 if workspace is None or isinstance(workspace, int)
-                 else workspace.numel() * workspace.element_size()))
-    _check("fd_decode_attn_sparse_fp8", load().fd_decode_attn_sparse_fp8(
-        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-        _ptr(k_scale), _ptr(v_scale), _ptr(codes), _ptr(scales),
-        _ptr(block_table), _ptr(seq_lens), float(delta), int(num_splits),
-        _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse_out), _ptr(kept_out),
-        _stream(stream)))
+    _sparse8("fd_decode_attn_sparse_fp8", shape, q, k_cache, v_cache,
+             k_scale, v_scale, codes, scales, block_table, seq_lens, delta,
+             num_splits, workspace, out, lse_out, kept_out, stream,
+             workspace_bytes)
+
+
+def fd_decode_attn_sparse_int8(shape: FdShape, q, k_cache, v_cache, k_scale,
+                               v_scale, codes, scales, block_table, seq_lens,
+                               delta: float, num_splits: int, workspace, out,
+                               lse_out=None, kept_out=None, stream=None,
+                               workspace_bytes: Optional[int] = None) -> None:
+    """Block-sparse decode over an int8 cache with per-position scales."""
+    _sparse8("fd_decode_attn_sparse_int8", shape, q, k_cache, v_cache,
+             k_scale, v_scale, codes, scales, block_table, seq_lens, delta,
+             num_splits, workspace, out, lse_out, kept_out, stream,
+             workspace_bytes)
 
 
 def fd_combine_partials(batch: int, num_q_heads: int, head_dim: int,

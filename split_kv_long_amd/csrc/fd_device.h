@@ -12,6 +12,9 @@
 
 namespace fd {
 
+// Cache encodings of the MFMA kernels (dense and block-sparse).
+enum : int { kCacheBf16 = 0, kCacheE4M3 = 1, kCacheI8 = 2 };
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));

@@ -418,12 +418,12 @@ int fd_decode_partials_int8(const fd_shape* shape, const void* q,
                          o_part, lse_part, stream);
 }
 
-// The sparse calls take bf16 caches (scaled = -1) or E4M3 caches with their
-// per-kv-head scales (scaled = FD_DTYPE_FP8_E4M3), each through its own
-// entry point.
+// The sparse calls take bf16 caches (scaled = -1), E4M3 caches with their
+// per-kv-head scales (scaled = FD_DTYPE_FP8_E4M3) or int8 caches with their
+// per-position scales (FD_DTYPE_INT8), each through its own entry points.
 static int check_sparse_dtype(const Shape& s, int scaled) {
   if (scaled < 0) return s.dtype == FD_DTYPE_BF16 ? FD_OK : FD_ERR_UNSUPPORTED;
-  return s.dtype == FD_DTYPE_FP8_E4M3 ? FD_OK : FD_ERR_INVALID_ARG;
+  return s.dtype == scaled ? FD_OK : FD_ERR_INVALID_ARG;
 }
 
 static int build_key_summary(const fd_shape* shape, const void* k_cache,
@@ -473,6 +473,15 @@ int fd_build_key_summary_fp8(const fd_shape* shape, const void* k_cache,
                              const int32_t* seq_lens, void* codes,
                              float* scales, void* stream) {
   return build_key_summary(shape, k_cache, k_scale, FD_DTYPE_FP8_E4M3,
+                           block_table, seq_lens, codes, scales, stream);
+}
+
+int fd_build_key_summary_int8(const fd_shape* shape, const void* k_cache,
+                              const float* k_scale,
+                              const int32_t* block_table,
+                              const int32_t* seq_lens, void* codes,
+                              float* scales, void* stream) {
+  return build_key_summary(shape, k_cache, k_scale, FD_DTYPE_INT8,
                            block_table, seq_lens, codes, scales, stream);
 }
 
@@ -573,6 +582,21 @@ int fd_decode_attn_sparse_fp8(const fd_shape* shape, const void* q,
                               uint8_t* kept_out, void* stream) {
   return decode_attn_sparse(shape, q, k_cache, v_cache, k_scale, v_scale,
                             FD_DTYPE_FP8_E4M3, codes, scales, block_table,
+                            seq_lens, delta, num_splits, workspace, ws_bytes,
+                            out, lse_out, kept_out, stream);
+}
+
+int fd_decode_attn_sparse_int8(const fd_shape* shape, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const void* codes, const float* scales,
+                               const int32_t* block_table,
+                               const int32_t* seq_lens, float delta,
+                               int num_splits, void* workspace,
+                               size_t ws_bytes, float* out, float* lse_out,
+                               uint8_t* kept_out, void* stream) {
+  return decode_attn_sparse(shape, q, k_cache, v_cache, k_scale, v_scale,
+                            FD_DTYPE_INT8, codes, scales, block_table,
                             seq_lens, delta, num_splits, workspace, ws_bytes,
                             out, lse_out, kept_out, stream);
 }

@@ -379,8 +379,6 @@ __device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
   return pc;
 }
 
-// Cache encodings of the MFMA kernel.
-enum : int { kCacheBf16 = 0, kCacheE4M3 = 1, kCacheI8 = 2 };
 
 // Waves per SIMD the register allocation targets: two for bf16, whose
 // waves hold two subtiles of registers (the reissue schedule below), three

@@ -9,9 +9,10 @@
 // through the ordinary log-sum-exp combine.
 //
 // Kernels:
-//   summary_kernel<D, F8>
-//                       bf16 keys (or E4M3 codes times their kv head's
-//                       scale, rounded once to fp32)
+//   summary_kernel<D, QM>
+//                       bf16 keys (or 8-bit codes times their scale -- per
+//                       kv head for E4M3, per position for int8 -- rounded
+//                       once to fp32)
 //                       -> 4-bit codes (two per byte, even dim in
 //                       the low nibble) + one fp32 scale per 16-token block
 //                       and kv head: scale = amax / 7, code =
@@ -21,15 +22,15 @@
 //                       + D/8 - 1 hold piece p (dims D/4 * p ..) of row n, so
 //                       every lane's request is contiguous with its
 //                       neighbours'.
-//   split_sparse<D, NW, GM, PAGED, CHUNK, MULTI, F8>
+//   split_sparse<D, NW, GM, PAGED, CHUNK, MULTI, QM>
 //                       one workgroup per (split, kv head, sequence):
 //                       phase 1 scans the split's summary blocks (8-bit
 //                       query x 4-bit codes, exact, on the int8 matrix
 //                       cores), phase 2 keeps blocks per top-delta, phase 3
 //                       runs exact attention over the kept blocks (bf16
-//                       products; an E4M3 cache's codes are converted to
-//                       bf16 in registers, exactly, and its scales folded
-//                       into the logit scale and the output).
+//                       products; an 8-bit cache's codes are converted to
+//                       bf16 in registers, exactly, and its scales applied
+//                       as in the dense kernel).
 //                       A kv head with more than GM query heads is served
 //                       GM heads at a time in phases 1 and 3 (the keep
 //                       decision in phase 2 needs every head's estimates).
@@ -56,7 +57,7 @@ constexpr int kSumBlock = 16;   // tokens per summary block
 // of the block and the quarter l % 4 of its dims. Blocks with no attended
 // token are skipped; rows past the length (all 16 rows of a record exist)
 // get code 0.
-template <int D, bool F8>
+template <int D, int QM>
 __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
   constexpr int QD = D / 4;                  // dims per lane
   const int lane = threadIdx.x;
@@ -87,17 +88,24 @@ __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
   }
   float x[QD];
   float amax = 0.f;
-  if (valid && F8) {
-    // E4M3: codes -> bf16 (exact) -> fp32, times the kv head's scale (one
-    // fp32 rounding).
+  if (valid && QM != kCacheBf16) {
+    // 8-bit codes -> bf16 (exact) -> fp32, times the scale (one fp32
+    // rounding): the kv head's for E4M3, the row's for int8 (rows of a
+    // contiguous cache's scales are padded to whole 16-position groups; a
+    // paged pool's scales are indexed like its rows).
     const uint8_t* kp = static_cast<const uint8_t*>(a.k) + row * D + part * QD;
-    const float ks = a.k_scale[kvh];
+    const size_t Lp = ((size_t)a.L + 15) & ~(size_t)15;
+    const float ks =
+        QM == kCacheE4M3 ? a.k_scale[kvh]
+                         : a.k_scale[a.bs == 0 ? (size_t)(b * a.Hkv + kvh) * Lp + t
+                                               : row];
 #pragma unroll
     for (int c = 0; c < QD / 16; ++c) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(kp + 16 * c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint2 p = e4m3x4_to_bf16x4(w[e]);
+        const uint2 p = QM == kCacheI8 ? s8x4_to_bf16x4(w[e])
+                                       : e4m3x4_to_bf16x4(w[e]);
         x[16 * c + 4 * e] = __uint_as_float(p.x << 16) * ks;
         x[16 * c + 4 * e + 1] = __uint_as_float(p.x & 0xffff0000u) * ks;
         x[16 * c + 4 * e + 2] = __uint_as_float(p.y << 16) * ks;
@@ -164,9 +172,11 @@ constexpr int kMaxSparseEstimates = kMaxSparseEst / kSumBlock;
 // query bytes of each lane follow the order its code bytes arrive in, and
 // since every (lane group, byte) pair names one k-slot of the product for
 // both operands alike, the sum runs over every dim exactly once.
-template <int D, int NW, int GM, bool PAGED, int CHUNK, bool MULTI, bool F8>
+template <int D, int NW, int GM, bool PAGED, int CHUNK, bool MULTI, int QM>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void split_sparse(SplitArgs a, SparseArgs sp) {
+  constexpr bool F8 = QM != kCacheBf16;        // one byte per element
+  constexpr bool I8 = QM == kCacheI8;
   constexpr int KC = D / 32;
   constexpr int NV = D / 16;
   constexpr int DP = D + 4;
@@ -421,11 +431,22 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
   // bf16: lane (n, j) requests 16 bytes of key row n at dims 32c + 8j. E4M3
   // (as in the dense kernel): 16 codes at dims 64c' + 16j, which feed two
   // products (dims 64c' + 16j and + 8), and 8 value codes per row; the
-  // query fragments follow the same dim order. The key scale joins the
-  // logit scale and the value scale the final normalisation.
+  // query fragments follow the same dim order. An E4M3 key scale joins the
+  // logit scale and its value scale the final normalisation; int8 scales
+  // are per position: a lane requests the key and value scales of its rows
+  // 4j..4j+3 of each block (one 16-byte request each), the key scale
+  // multiplies the score and the value scale the probability entering the
+  // PV product (the softmax sum takes the unscaled one), and masked rows
+  // get a zero value scale, so a NaN scale of an unattended slot stays out.
   constexpr int KL = F8 ? D / 64 : KC;         // 16-byte key requests per row
-  const float sl2 = F8 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
-  const float vsc = F8 ? a.v_scale[kvh] : 1.f;
+  const float sl2 =
+      QM == kCacheE4M3 ? a.scale_log2 * a.k_scale[kvh] : a.scale_log2;
+  const float vsc = QM == kCacheE4M3 ? a.v_scale[kvh] : 1.f;
+  const size_t Lp = ((size_t)L + 15) & ~(size_t)15;   // L may be INT32_MAX
+  auto cvt4 = [](unsigned x) -> uint2 {
+    if constexpr (I8) return s8x4_to_bf16x4(x);
+    else return e4m3x4_to_bf16x4(x);
+  };
   for (int hg = 0; hg < nhg; ++hg) {
     const int hb = hg * GM, ng = min(GM, G - hb);
     const uint16_t* qrow = q_row(hb, ng);
@@ -467,6 +488,19 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         kr[0][c] = ld16<true>(K0 + r0 + KS * c);
         kr[1][c] = ld16<true>(K1 + r1 + KS * c);
       }
+      f32x4 k_sc[2], v_sc[2];
+      if constexpr (I8) {
+        const size_t sa = (PAGED ? ra : (size_t)(b * Hkv + kvh) * Lp + ta) + 4 * j;
+        const size_t sb = (PAGED ? rb : (size_t)(b * Hkv + kvh) * Lp + tb) + 4 * j;
+        k_sc[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(a.k_scale + sa));
+        k_sc[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(a.k_scale + sb));
+        v_sc[0] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(a.v_scale + sa));
+        v_sc[1] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(a.v_scale + sb));
+      }
       const int vcol = D == 128 ? 8 * n : 8 * (n & 7);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -489,8 +523,8 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
           bf16x8 kop;
           if constexpr (F8) {
             const u32x4 x = kr[tg][c >> 1];
-            const uint2 p = e4m3x4_to_bf16x4(x[2 * (c & 1)]);
-            const uint2 q = e4m3x4_to_bf16x4(x[2 * (c & 1) + 1]);
+            const uint2 p = cvt4(x[2 * (c & 1)]);
+            const uint2 q = cvt4(x[2 * (c & 1) + 1]);
             kop = as_bf16x8(u32x4{p.x, p.y, q.x, q.y});
           } else {
             kop = as_bf16x8(kr[tg][c]);
@@ -507,9 +541,11 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i;
           const bool ok = tg == 0 ? r <= lasta : (jb >= 0 && r <= lastb);
-          const float x = ok ? sacc[tg][i] * sl2 : -INFINITY;
+          const float ls = I8 ? sl2 * k_sc[tg][i] : sl2;
+          const float x = ok ? sacc[tg][i] * ls : -INFINITY;
           sv[4 * tg + i] = x;
           mx = fmaxf(mx, x);
+          if constexpr (I8) v_sc[tg][i] = ok ? v_sc[tg][i] : 0.f;
         }
       mx = max_x32(max_x16(mx));
       const float mn = fmaxf(m_run, mx);
@@ -521,17 +557,18 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
       for (int e = 0; e < 8; ++e) {
         const float p = fexp2(sv[e] - mn);
         psum += p;
-        const __bf16 hb = (__bf16)p;
+        const float pw = I8 ? p * v_sc[e >> 2][e & 3] : p;   // value row e
+        const __bf16 hb = (__bf16)pw;
         ph[e] = hb;
-        pl[e] = (__bf16)(p - (float)hb);
+        pl[e] = (__bf16)(pw - (float)hb);
       }
       l_run = l_run * alpha + psum;
       u32x4 vr[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if constexpr (F8) {
-          const uint2 p = e4m3x4_to_bf16x4(vraw[e][0]);
-          const uint2 q = e4m3x4_to_bf16x4(vraw[e][1]);
+          const uint2 p = cvt4(vraw[e][0]);
+          const uint2 q = cvt4(vraw[e][1]);
           vr[e] = u32x4{p.x, p.y, q.x, q.y};
         } else {
           vr[e] = vraw[e];
@@ -593,39 +630,39 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
 // more (256K, cold summary: 35.3 -> 33.2 us), else 4 (a 512-token split
 // gives each wave only 4 blocks; 8 measured 3 % slower at 64K).
 // MULTI: more than GM query heads per kv head (served GM at a time).
-template <int D, int GM, bool PAGED, bool MULTI, bool F8>
+template <int D, int GM, bool PAGED, bool MULTI, int QM>
 void launch_sparse_gm(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                       hipStream_t st) {
   const dim3 grid((unsigned)s.Hkv, (unsigned)s.B, (unsigned)a.S);
   if (a.P >= 2048)
-    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 8, MULTI, F8>), grid,
+    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 8, MULTI, QM>), grid,
                        dim3(8 * 64), 0, st, a, sp);
   else
-    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 4, MULTI, F8>), grid,
+    hipLaunchKernelGGL((split_sparse<D, 8, GM, PAGED, 4, MULTI, QM>), grid,
                        dim3(8 * 64), 0, st, a, sp);
 }
 
-template <int D, bool PAGED, bool F8>
+template <int D, bool PAGED, int QM>
 void launch_sparse_d(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                      hipStream_t st) {
   if (s.G <= 8)
-    launch_sparse_gm<D, 8, PAGED, false, F8>(s, a, sp, st);
+    launch_sparse_gm<D, 8, PAGED, false, QM>(s, a, sp, st);
   else if (s.G <= 16)
-    launch_sparse_gm<D, 16, PAGED, false, F8>(s, a, sp, st);
+    launch_sparse_gm<D, 16, PAGED, false, QM>(s, a, sp, st);
   else
-    launch_sparse_gm<D, 16, PAGED, true, F8>(s, a, sp, st);
+    launch_sparse_gm<D, 16, PAGED, true, QM>(s, a, sp, st);
 }
 
-template <bool F8>
+template <int QM>
 void launch_sparse_dtype(const Shape& s, const SplitArgs& a,
                          const SparseArgs& sp, hipStream_t st) {
   const bool paged = s.bs > 0;
   if (s.D == 128) {
-    if (paged) launch_sparse_d<128, true, F8>(s, a, sp, st);
-    else launch_sparse_d<128, false, F8>(s, a, sp, st);
+    if (paged) launch_sparse_d<128, true, QM>(s, a, sp, st);
+    else launch_sparse_d<128, false, QM>(s, a, sp, st);
   } else {
-    if (paged) launch_sparse_d<64, true, F8>(s, a, sp, st);
-    else launch_sparse_d<64, false, F8>(s, a, sp, st);
+    if (paged) launch_sparse_d<64, true, QM>(s, a, sp, st);
+    else launch_sparse_d<64, false, QM>(s, a, sp, st);
   }
 }
 
@@ -637,13 +674,21 @@ int launch_summary(const Shape& s, const SummaryArgs& a, void* stream) {
   // INT32_MAX)
   const dim3 grid((unsigned)a.nblk_row, (unsigned)s.Hkv, (unsigned)s.B);
   if (grid.x == 0) return 0;
-  const bool f8 = s.dtype == FD_DTYPE_FP8_E4M3;
+  const dim3 blk(64);
   if (s.D == 128) {
-    if (f8) hipLaunchKernelGGL((summary_kernel<128, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((summary_kernel<128, false>), grid, dim3(64), 0, st, a);
+    if (s.dtype == FD_DTYPE_FP8_E4M3)
+      hipLaunchKernelGGL((summary_kernel<128, kCacheE4M3>), grid, blk, 0, st, a);
+    else if (s.dtype == FD_DTYPE_INT8)
+      hipLaunchKernelGGL((summary_kernel<128, kCacheI8>), grid, blk, 0, st, a);
+    else
+      hipLaunchKernelGGL((summary_kernel<128, kCacheBf16>), grid, blk, 0, st, a);
   } else {
-    if (f8) hipLaunchKernelGGL((summary_kernel<64, true>), grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL((summary_kernel<64, false>), grid, dim3(64), 0, st, a);
+    if (s.dtype == FD_DTYPE_FP8_E4M3)
+      hipLaunchKernelGGL((summary_kernel<64, kCacheE4M3>), grid, blk, 0, st, a);
+    else if (s.dtype == FD_DTYPE_INT8)
+      hipLaunchKernelGGL((summary_kernel<64, kCacheI8>), grid, blk, 0, st, a);
+    else
+      hipLaunchKernelGGL((summary_kernel<64, kCacheBf16>), grid, blk, 0, st, a);
   }
   return (int)hipGetLastError();
 }
@@ -652,9 +697,11 @@ int launch_sparse(const Shape& s, const SplitArgs& a, const SparseArgs& sp,
                   void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.dtype == FD_DTYPE_FP8_E4M3)
-    launch_sparse_dtype<true>(s, a, sp, st);
+    launch_sparse_dtype<kCacheE4M3>(s, a, sp, st);
+  else if (s.dtype == FD_DTYPE_INT8)
+    launch_sparse_dtype<kCacheI8>(s, a, sp, st);
   else
-    launch_sparse_dtype<false>(s, a, sp, st);
+    launch_sparse_dtype<kCacheBf16>(s, a, sp, st);
   return (int)hipGetLastError();
 }
 

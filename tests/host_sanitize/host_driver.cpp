@@ -97,8 +97,9 @@ int launch_combine(int D, const CombineArgs& c, void*) {
 
 int launch_summary(const Shape& s, const SummaryArgs& a, void*) {
   ++g_launches;
-  EXPECT(s.dtype == FD_DTYPE_BF16 || s.dtype == FD_DTYPE_FP8_E4M3);
-  EXPECT((a.k_scale != nullptr) == (s.dtype == FD_DTYPE_FP8_E4M3));
+  EXPECT(s.dtype == FD_DTYPE_BF16 || s.dtype == FD_DTYPE_FP8_E4M3 ||
+         s.dtype == FD_DTYPE_INT8);
+  EXPECT((a.k_scale != nullptr) == (s.dtype != FD_DTYPE_BF16));
   EXPECT(a.k && a.seq_lens && a.codes && a.scales);
   EXPECT(a.nblk_row == ((int64_t)s.L + 15) / 16);
   EXPECT((a.block_table != nullptr) == (s.bs > 0));
@@ -188,7 +189,7 @@ int main() {
     const bool paged = s.block_size > 0;
     const int32_t* tbl = paged ? bt : nullptr;
     const long before = g_launches;
-    const int which = (int)(rnd() % 10);
+    const int which = (int)(rnd() % 12);
     if (which == 1 || which == 6) g_ws = 0;   // caller's own partials
     int st;
     switch (which) {
@@ -225,6 +226,16 @@ int main() {
                                        tbl, lens, (rnd() % 2) ? 3.f : INFINITY,
                                        S, (void*)ws, g_ws_bytes, out, lse,
                                        nullptr, nullptr);
+        break;
+      case 10:
+        st = fd_build_key_summary_int8(&s, k, ks, tbl, lens, codes, cscales,
+                                       nullptr);
+        break;
+      case 11:
+        st = fd_decode_attn_sparse_int8(&s, q, k, v, ks, vs, codes, cscales,
+                                        tbl, lens, (rnd() % 2) ? 3.f : INFINITY,
+                                        S, (void*)ws, g_ws_bytes, out, lse,
+                                        nullptr, nullptr);
         break;
       case 7:                                   // partials in the scratch
         g_ws = fd::kScratchAddr;

@@ -348,6 +348,28 @@ def test_sparse_and_summary_reject_bad_args():
     assert sparse8(ws_bytes=10) == fb.FD_ERR_WORKSPACE
     assert sparse8(shape=shp(max_seq_len=16384, dtype="fp8_e4m3"), S=1
                    ) == fb.FD_ERR_UNSUPPORTED
+    # int8: per-position scales, 16-byte aligned for the sparse call
+    si = shp(max_seq_len=8192, dtype="int8")
+
+    def sparse_i8(**kw):
+        args = dict(shape=si, ks=FAKE, vs=FAKE)
+        args.update(kw)
+        return lib.fd_decode_attn_sparse_int8(
+            ctypes.byref(args["shape"]), FAKE, FAKE, FAKE, args["ks"],
+            args["vs"], FAKE, FAKE, None, FAKE, F(4.0), 4, FAKE, 1 << 30,
+            FAKE, None, None, None)
+
+    assert sparse_i8(ks=None) == fb.FD_ERR_INVALID_ARG
+    assert sparse_i8(vs=FAKE + 4) == fb.FD_ERR_INVALID_ARG    # not 16-aligned
+    assert sparse_i8(shape=s8) == fb.FD_ERR_INVALID_ARG       # E4M3 shape
+    assert sparse_i8(shape=s) == fb.FD_ERR_INVALID_ARG        # bf16 shape
+    assert lib.fd_build_key_summary_int8(
+        ctypes.byref(si), FAKE, None, None, FAKE, FAKE, FAKE,
+        None) == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_build_key_summary_int8(
+        ctypes.byref(s8), FAKE, FAKE, None, FAKE, FAKE, FAKE,
+        None) == fb.FD_ERR_INVALID_ARG
+    assert sparse(shape=si) == fb.FD_ERR_UNSUPPORTED          # bf16 call
     assert summary8(ks=None) == fb.FD_ERR_INVALID_ARG
     assert summary8(ks=FAKE + 1) == fb.FD_ERR_INVALID_ARG
     assert summary8(shape=s) == fb.FD_ERR_INVALID_ARG         # bf16 shape

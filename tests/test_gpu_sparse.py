@@ -1,6 +1,7 @@
 """Parity of the block-sparse path (key summary + top-delta + exact attention
 over kept blocks) against the float64 oracle (needs a gfx950 GPU), over bf16
-caches and over E4M3 caches with per-kv-head scales.
+caches, E4M3 caches with per-kv-head scales and int8 caches with
+per-position scales.
 
 * The key summary is integer work decided in fp32 on both sides: codes and
   scales must match the oracle bit for bit.
@@ -46,9 +47,10 @@ def gpu_summary(w, t):
     scales = torch.full(nrec, -1.0, device=d)
     print(f"[gpu] summary {w.name} {w.cache_dtype} paged={w.paged} D={D}",
           flush=True)
-    if w.cache_dtype == "fp8_e4m3":
-        fb.fd_build_key_summary_fp8(shape_of(w), t["k"], t["ks"], t["bt"],
-                                    t["lens"], codes, scales)
+    if w.cache_dtype in ("fp8_e4m3", "int8"):
+        call = (fb.fd_build_key_summary_fp8 if w.cache_dtype == "fp8_e4m3"
+                else fb.fd_build_key_summary_int8)
+        call(shape_of(w), t["k"], t["ks"], t["bt"], t["lens"], codes, scales)
     else:
         fb.fd_build_key_summary(shape_of(w), t["k"], t["bt"], t["lens"],
                                 codes, scales)
@@ -92,7 +94,7 @@ def written_records(w):
     return tuple(np.array(x) for x in zip(*rec)), row
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3", "int8"])
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("d", [128, 64])
 def test_summary_matches_oracle_bitwise(paged, d, kv):
@@ -155,10 +157,11 @@ def run_sparse(w, t, codes, scales, delta, S):
     print(f"[gpu] sparse {w.name} {w.cache_dtype} paged={w.paged} D={D} "
           f"G={w.num_q_heads // w.num_kv_heads} delta={delta} S={S}",
           flush=True)
-    if w.cache_dtype == "fp8_e4m3":
-        fb.fd_decode_attn_sparse_fp8(shape, t["q"], t["k"], t["v"], t["ks"],
-                                     t["vs"], codes, scales, t["bt"],
-                                     t["lens"], delta, S, ws, out, lse, kept)
+    if w.cache_dtype in ("fp8_e4m3", "int8"):
+        call = (fb.fd_decode_attn_sparse_fp8 if w.cache_dtype == "fp8_e4m3"
+                else fb.fd_decode_attn_sparse_int8)
+        call(shape, t["q"], t["k"], t["v"], t["ks"], t["vs"], codes, scales,
+             t["bt"], t["lens"], delta, S, ws, out, lse, kept)
     else:
         fb.fd_decode_attn_sparse(shape, t["q"], t["k"], t["v"], codes,
                                  scales, t["bt"], t["lens"], delta, S, ws,
@@ -301,4 +304,29 @@ def test_sparse_e4m3_delta_inf_is_the_dense_e4m3_result():
                                   dtype="bf16", kv_dtype="fp8_e4m3",
                                   k_scale=a["k_scale"], v_scale=a["v_scale"],
                                   scale=w.scale)
+    assert np.abs(out - ref[0]).max() <= TOL
+
+
+@pytest.mark.parametrize("paged,S,d,hq,hkv", [
+    (False, 4, 128, 16, 2), (True, 1, 128, 16, 2), (True, 3, 64, 12, 3),
+    (False, 2, 128, 32, 1)])
+def test_sparse_int8_cache_matches_oracle(paged, S, d, hq, hkv):
+    # int8 codes with per-position scales; unattended slots hold code 127
+    # with a NaN scale (also the padding of contiguous scale rows): the same
+    # kept sets as the oracle, outputs at the bf16 bar.
+    w = sparse_case(89, paged, d=d, hq=hq, hkv=hkv, L=4000,
+                    lens=[4000, 17, 2500], kv="int8")
+    check_sparse(w, 1.5, S, expect_dropped=False)
+
+
+def test_sparse_int8_delta_inf_is_the_dense_int8_result():
+    w = sparse_case(90, True, L=3000, lens=[3000, 1234], kv="int8")
+    out, lse, kept = check_sparse(w, math.inf, 2, expect_dropped=False)
+    assert np.all(kept[kept != 7] == 1)
+    a = w.numpy_view()
+    ref = oracle.decode_attention(a["q"], a["k"], a["v"], a["seq_lens"],
+                                  dtype="bf16", kv_dtype="int8",
+                                  k_scale=a["k_scale"], v_scale=a["v_scale"],
+                                  scale=w.scale, block_table=a["block_table"],
+                                  block_size=a["block_size"])
     assert np.abs(out - ref[0]).max() <= TOL
