@@ -4,14 +4,16 @@ The compute lives in ``lib/libfd_decode.so`` (hand-written HIP kernels behind
 the C ABI in ``include/fd_decode.h``); ``binding`` exposes the same calls to
 Python, and ``decode_attention`` below is a convenience wrapper that checks
 the tensors, sizes and allocates the outputs with torch before calling
-``fd_decode_attn``.
+``fd_decode_attn``; ``build_key_summary`` and ``sparse_decode_attention``
+do the same for the block-sparse calls.
 """
 
 from __future__ import annotations
 
 from typing import Optional
 
-__all__ = ["decode_attention", "shape_for", "validate_inputs"]
+__all__ = ["decode_attention", "shape_for", "validate_inputs",
+           "build_key_summary", "sparse_decode_attention", "sparse_splits"]
 
 
 def shape_for(q, k_cache, seq_lens, block_table=None, max_seq_len=None,
@@ -140,3 +142,109 @@ def decode_attention(q, k_cache, v_cache, seq_lens, block_table=None,
         binding.fd_decode_attn(shape, q, k_cache, v_cache, block_table,
                                seq_lens, num_splits, ws, out, lse)
     return (out, lse) if return_lse else out
+
+
+# Block-sparse calls: tokens per split at most 8192, and tokens per split x
+# max(16, query heads per kv head) at most 131072 (the block estimates of a
+# split live in on-chip memory).
+_SPARSE_MAX_SPLIT = 8192
+_SPARSE_MAX_EST = 8192 * 16
+
+
+def sparse_splits(shape, num_splits: int) -> int:
+    """The smallest split count >= num_splits whose splits the block-sparse
+    calls accept (doubling; at most 65535)."""
+    g = max(16, shape.block_size)
+    G = shape.num_q_heads // shape.num_kv_heads
+    cap = min(_SPARSE_MAX_SPLIT, _SPARSE_MAX_EST // max(16, G))
+    L = max(int(shape.max_seq_len), 1)
+    S = max(1, int(num_splits))
+    while True:
+        P = -(-(-(-L // S)) // g) * g
+        if P <= cap or S >= 65535:
+            return S
+        S = min(65535, 2 * S)
+
+
+def _sparse_call(name, k_cache):
+    import torch
+    from . import binding
+    suffix = {torch.bfloat16: "", torch.float8_e4m3fn: "_fp8",
+              torch.int8: "_int8"}.get(k_cache.dtype)
+    if suffix is None:
+        raise ValueError("the block-sparse path takes bf16, E4M3 or int8 "
+                         f"caches (got {k_cache.dtype})")
+    return getattr(binding, name + suffix), bool(suffix)
+
+
+def build_key_summary(q, k_cache, seq_lens, block_table=None, k_scale=None,
+                      max_seq_len=None):
+    """The 4-bit key summary the block-sparse call scans: (codes, scales)
+    tensors on the cache's device, laid out as the C ABI describes
+    (contiguous [B, Hkv, ceil(L/16), 8 * D] / [B, Hkv, ceil(L/16)], paged
+    [NB, Hkv, bs/16, ...]). q only fixes the head layout of the shape."""
+    import torch
+    call, scaled = _sparse_call("fd_build_key_summary", k_cache)
+    shape = validate_inputs(q, k_cache, k_cache, seq_lens, block_table,
+                            k_scale, k_scale, max_seq_len)
+    D, Hkv = shape.head_dim, shape.num_kv_heads
+    if block_table is None:
+        nrec = (shape.batch, Hkv, -(-shape.max_seq_len // 16))
+    else:
+        nrec = (shape.num_blocks, Hkv, shape.block_size // 16)
+    dev = k_cache.device
+    codes = torch.zeros(nrec + (8 * D,), dtype=torch.uint8, device=dev)
+    scales = torch.zeros(nrec, dtype=torch.float32, device=dev)
+    if scaled:
+        call(shape, k_cache, k_scale, block_table, seq_lens, codes, scales)
+    else:
+        call(shape, k_cache, block_table, seq_lens, codes, scales)
+    return codes, scales
+
+
+def sparse_decode_attention(q, k_cache, v_cache, seq_lens, summary,
+                            delta: float, block_table=None,
+                            num_splits: Optional[int] = None, scale=None,
+                            max_seq_len=None, k_scale=None, v_scale=None,
+                            return_lse: bool = False,
+                            return_kept: bool = False):
+    """Block-sparse decode: the blocks whose estimated best logit (from the
+    summary ``build_key_summary`` returned) comes within ``delta`` (natural
+    log units, >= 0; inf keeps everything) of the split's best, for some
+    query head of the kv head, then exact attention over them. Tensors as
+    for ``decode_attention``; the split count defaults to the planner's,
+    raised until the splits fit the sparse path's limits."""
+    import torch
+    from . import binding
+    call, scaled = _sparse_call("fd_decode_attn_sparse", k_cache)
+    shape = validate_inputs(q, k_cache, v_cache, seq_lens, block_table,
+                            k_scale, v_scale, max_seq_len)
+    if scale:
+        shape.scale = float(scale)
+    if num_splits is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        num_splits = sparse_splits(shape, binding.fd_plan_splits(shape, cus,
+                                                                 -1))
+    codes, scales = summary
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    kept = None
+    if return_kept:
+        kept = torch.zeros(shape.batch, shape.num_kv_heads,
+                           -(-shape.max_seq_len // 16), dtype=torch.uint8,
+                           device=q.device)
+    nbytes = binding.fd_workspace_size(shape, num_splits)
+    ws = (torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+          if nbytes else None)
+    if scaled:
+        call(shape, q, k_cache, v_cache, k_scale, v_scale, codes, scales,
+             block_table, seq_lens, delta, num_splits, ws, out, lse, kept)
+    else:
+        call(shape, q, k_cache, v_cache, codes, scales, block_table, seq_lens,
+             delta, num_splits, ws, out, lse, kept)
+    res = (out,)
+    if return_lse:
+        res += (lse,)
+    if return_kept:
+        res += (kept,)
+    return res[0] if len(res) == 1 else res

@@ -330,3 +330,46 @@ def test_sparse_int8_delta_inf_is_the_dense_int8_result():
                                   scale=w.scale, block_table=a["block_table"],
                                   block_size=a["block_size"])
     assert np.abs(out - ref[0]).max() <= TOL
+
+
+@pytest.mark.parametrize("kv,paged,hq,hkv", [(None, False, 16, 2),
+                                             ("fp8_e4m3", True, 12, 3),
+                                             ("int8", False, 64, 2)])
+def test_python_wrappers_match_the_oracle(kv, paged, hq, hkv):
+    # build_key_summary + sparse_decode_attention (planner split count,
+    # raised to the sparse limits where needed: 32 heads per kv head).
+    import split_kv_long_amd as fd
+    w = sparse_case(91, paged, hq=hq, hkv=hkv, L=12000,
+                    lens=[12000, 333, 7000], kv=kv)
+    t = device_inputs(w)
+    print(f"[gpu] wrappers {w.cache_dtype} paged={paged} G={hq // hkv}",
+          flush=True)
+    summary = fd.build_key_summary(t["q"], t["k"], t["lens"], t["bt"],
+                                   k_scale=t["ks"],
+                                   max_seq_len=w.max_seq_len if paged
+                                   else None)
+    out, lse, kept = fd.sparse_decode_attention(
+        t["q"], t["k"], t["v"], t["lens"], summary, 2.0, t["bt"],
+        k_scale=t["ks"], v_scale=t["vs"],
+        max_seq_len=w.max_seq_len if paged else None, return_lse=True,
+        return_kept=True)
+    torch.cuda.synchronize()
+    shape = shape_of(w)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = fd.sparse_splits(shape, fb.fd_plan_splits(shape, cus, -1))
+    a = w.numpy_view()
+    ref_c, ref_s = oracle_summary(w)
+    ro, rl, est, rkept = osp.sparse_decode_attention(
+        a["q"], a["k"], a["v"], a["seq_lens"], ref_c, ref_s, delta=2.0,
+        num_splits=S, max_seq_len=w.max_seq_len, scale=w.scale,
+        block_table=a["block_table"], block_size=a["block_size"],
+        kv_dtype=w.cache_dtype, k_scale=a["k_scale"], v_scale=a["v_scale"])
+    kept = kept.cpu().numpy().astype(bool)
+    for b in range(w.batch):
+        nb = -(-int(a["seq_lens"][b]) // 16)
+        assert np.array_equal(kept[b, :, :nb], rkept[b, :, :nb]), b
+    err = float(np.abs(out.cpu().double().numpy() - ro).max())
+    lerr = float(np.abs(lse.cpu().double().numpy() - rl).max())
+    print(f"[gpu] wrappers S={S} max|out-ref|={err:.3g} lse={lerr:.3g}",
+          flush=True)
+    assert err <= TOL and lerr <= LSE_TOL

@@ -111,3 +111,29 @@ def test_e4m3_scales_per_kv_head_and_no_scales_otherwise():
               v_scale=s)
     with pytest.raises(ValueError, match="only taken"):
         check(k_scale=s, v_scale=s)
+
+
+def test_sparse_split_count_fits_the_sparse_limits():
+    from split_kv_long_amd import binding as fb
+    for L, G, bs, S in [(65536, 8, 0, 128), (65536, 32, 0, 1),
+                        (1 << 20, 128, 0, 4), (100, 4, 16, 1),
+                        (8193, 16, 0, 1), (40000, 20, 64, 3)]:
+        nb = -(-L // bs) if bs else 0
+        sh = fb.make_shape(1, 2 * G, 2, 128, L, "bf16", bs, nb, nb, 0.0)
+        got = fd.sparse_splits(sh, S)
+        g = max(16, bs)
+        P = -(-(-(-L // got)) // g) * g
+        assert got >= S
+        assert P <= 8192 and P * max(16, G) <= 8192 * 16, (L, G, got, P)
+        if got > S:      # the doubling stopped at the first fit
+            half = got // 2
+            Ph = -(-(-(-L // half)) // g) * g
+            assert Ph > 8192 or Ph * max(16, G) > 8192 * 16
+
+
+def test_sparse_wrappers_refuse_fp32_caches():
+    q, k, v, lens, bt = tensors(cache=torch.float32)
+    with pytest.raises(ValueError, match="bf16, E4M3 or int8"):
+        fd.build_key_summary(q, k, lens)
+    with pytest.raises(ValueError, match="bf16, E4M3 or int8"):
+        fd.sparse_decode_attention(q, k, v, lens, (None, None), 1.0)
