@@ -373,3 +373,94 @@ def test_python_wrappers_match_the_oracle(kv, paged, hq, hkv):
     print(f"[gpu] wrappers S={S} max|out-ref|={err:.3g} lse={lerr:.3g}",
           flush=True)
     assert err <= TOL and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("kv", [None, "fp8_e4m3", "int8"])
+def test_sparse_graph_replays_match_eager(kv):
+    """The sparse calls (summary, then decode) enqueue kernels only: in a
+    captured graph every replay, with eager work and synchronisations in
+    between, reproduces the eager results bitwise."""
+    w = sparse_case(92, True, L=4000, lens=[4000, 17, 2500], kv=kv)
+    t = device_inputs(w)
+    d = torch.device("cuda")
+    shape, S = shape_of(w), 3
+    nrec = (w.k.shape[0], w.num_kv_heads, w.block_size // 16)
+    codes = torch.empty(nrec + (8 * w.head_dim,), dtype=torch.uint8, device=d)
+    scales = torch.empty(nrec, device=d)
+    out = torch.empty(w.batch, w.num_q_heads, w.head_dim, device=d)
+    lse = torch.empty(w.batch, w.num_q_heads, device=d)
+    kept = torch.empty(w.batch, w.num_kv_heads, -(-w.max_seq_len // 16),
+                       dtype=torch.uint8, device=d)
+    ws = torch.empty(max(fb.fd_workspace_size(shape, S), 16),
+                     dtype=torch.uint8, device=d)
+
+    def call():
+        if kv is None:
+            fb.fd_build_key_summary(shape, t["k"], t["bt"], t["lens"], codes,
+                                    scales)
+            fb.fd_decode_attn_sparse(shape, t["q"], t["k"], t["v"], codes,
+                                     scales, t["bt"], t["lens"], 1.5, S, ws,
+                                     out, lse, kept)
+        else:
+            sfx = "fp8" if kv == "fp8_e4m3" else "int8"
+            getattr(fb, "fd_build_key_summary_" + sfx)(
+                shape, t["k"], t["ks"], t["bt"], t["lens"], codes, scales)
+            getattr(fb, "fd_decode_attn_sparse_" + sfx)(
+                shape, t["q"], t["k"], t["v"], t["ks"], t["vs"], codes,
+                scales, t["bt"], t["lens"], 1.5, S, ws, out, lse, kept)
+
+    def reset():
+        codes.fill_(0xAA)
+        scales.fill_(-1.0)
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        kept.fill_(7)
+        ws.fill_(0xFF)
+
+    reset()
+    call()
+    torch.cuda.synchronize()
+    ref = [x.cpu().clone() for x in (codes, scales, out, lse, kept)]
+    reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    print(f"[gpu] sparse graph capture {w.cache_dtype}", flush=True)
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            call()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()                              # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (codes, scales, out, lse, kept)):
+            assert torch.equal(a, b.cpu()), rep
+
+
+def test_sparse_random_shapes_all_encodings():
+    # Seeded sweep over cache encoding, group size (one pass of heads or
+    # several), kv heads, head_dim, ragged lengths, paging, delta and split
+    # count (raised to the sparse limits where needed).
+    import random
+    import split_kv_long_amd as fd
+    rng = random.Random(919)
+    for case in range(12):
+        kv = rng.choice([None, "fp8_e4m3", "int8"])
+        hkv, g = rng.choice([1, 2]), rng.choice([1, 4, 8, 16, 20, 32, 64])
+        L = rng.choice([100, 700, 1500, 3000])
+        b = rng.choice([1, 2, 3])
+        lens = [rng.randint(1, L) for _ in range(b)]
+        lens[rng.randrange(b)] = L
+        w = workloads.make(f"sparse_any{case}", seed=5000 + case, batch=b,
+                           num_q_heads=g * hkv, num_kv_heads=hkv,
+                           head_dim=rng.choice([64, 128]), max_seq_len=L,
+                           paged=rng.random() < 0.5, seq_lens=lens,
+                           needles=[0, L // 2, L - 1], needle_logit=10.0,
+                           poison_tail=True, kv_dtype=kv)
+        S = fd.sparse_splits(shape_of(w), rng.choice([1, 2, 3, 5]))
+        check_sparse(w, rng.choice([0.0, 0.5, 2.0, 5.0]), S,
+                     expect_dropped=False)
