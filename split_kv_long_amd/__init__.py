@@ -177,6 +177,13 @@ def _sparse_call(name, k_cache):
     return getattr(binding, name + suffix), bool(suffix)
 
 
+def _summary_records(shape):
+    """Leading dims of the summary (one record per 16-token block)."""
+    if shape.block_size == 0:
+        return (shape.batch, shape.num_kv_heads, -(-shape.max_seq_len // 16))
+    return (shape.num_blocks, shape.num_kv_heads, shape.block_size // 16)
+
+
 def build_key_summary(q, k_cache, seq_lens, block_table=None, k_scale=None,
                       max_seq_len=None):
     """The 4-bit key summary the block-sparse call scans: (codes, scales)
@@ -187,11 +194,8 @@ def build_key_summary(q, k_cache, seq_lens, block_table=None, k_scale=None,
     call, scaled = _sparse_call("fd_build_key_summary", k_cache)
     shape = validate_inputs(q, k_cache, k_cache, seq_lens, block_table,
                             k_scale, k_scale, max_seq_len)
-    D, Hkv = shape.head_dim, shape.num_kv_heads
-    if block_table is None:
-        nrec = (shape.batch, Hkv, -(-shape.max_seq_len // 16))
-    else:
-        nrec = (shape.num_blocks, Hkv, shape.block_size // 16)
+    nrec = _summary_records(shape)
+    D = shape.head_dim
     dev = k_cache.device
     codes = torch.zeros(nrec + (8 * D,), dtype=torch.uint8, device=dev)
     scales = torch.zeros(nrec, dtype=torch.float32, device=dev)
@@ -226,6 +230,16 @@ def sparse_decode_attention(q, k_cache, v_cache, seq_lens, summary,
         num_splits = sparse_splits(shape, binding.fd_plan_splits(shape, cus,
                                                                  -1))
     codes, scales = summary
+    nrec = _summary_records(shape)
+    want = {"codes": (codes, torch.uint8, nrec + (8 * shape.head_dim,)),
+            "scales": (scales, torch.float32, nrec)}
+    for name, (t, dt, shp) in want.items():
+        if (not isinstance(t, torch.Tensor) or t.dtype != dt
+                or tuple(t.shape) != shp or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError(f"summary {name} must be a contiguous {dt} "
+                             f"{shp} tensor on {q.device} (as "
+                             "build_key_summary returns)")
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     kept = None

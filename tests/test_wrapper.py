@@ -137,3 +137,24 @@ def test_sparse_wrappers_refuse_fp32_caches():
         fd.build_key_summary(q, k, lens)
     with pytest.raises(ValueError, match="bf16, E4M3 or int8"):
         fd.sparse_decode_attention(q, k, v, lens, (None, None), 1.0)
+
+
+def test_sparse_call_checks_the_summary_layout():
+    # The kernel reads the summary by the shape's layout: a summary of
+    # another shape, dtype or device is refused before any call.
+    q, k, v, lens, bt = tensors()
+    nrec = (B, HKV, -(-L // 16))
+    good_c = torch.zeros(nrec + (8 * D,), dtype=torch.uint8)
+    good_s = torch.zeros(nrec)
+
+    def call(c, s):
+        fd.sparse_decode_attention(q, k, v, lens, (c, s), 1.0, num_splits=1)
+
+    with pytest.raises(ValueError, match="summary codes"):
+        call(good_c[:, :, :-1], good_s)
+    with pytest.raises(ValueError, match="summary codes"):
+        call(good_c.to(torch.int8), good_s)
+    with pytest.raises(ValueError, match="summary scales"):
+        call(good_c, good_s.double())
+    with pytest.raises(ValueError, match="summary scales"):
+        call(good_c, torch.zeros(B, HKV, 16 * nrec[2]))
