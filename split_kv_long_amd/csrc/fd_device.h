@@ -93,12 +93,12 @@ __device__ __forceinline__ int clamp_len(const SplitArgs& a, int b) {
 template <int D>
 __device__ __forceinline__ float* o_dst(const SplitArgs& a, int b, int h, int s) {
   return a.final_out ? a.o_dst + ((size_t)b * a.Hq + h) * D
-                     : a.o_dst + (((size_t)b * a.Hq + h) * (a.S * (a.wave_slots > 1 ? a.wave_slots : 1)) + s) * D;
+                     : a.o_dst + (((size_t)b * a.Hq + h) * a.S + s) * D;
 }
 __device__ __forceinline__ float* lse_dst(const SplitArgs& a, int b, int h, int s) {
   if (a.final_out)
     return a.lse_dst ? a.lse_dst + (size_t)b * a.Hq + h : nullptr;
-  return a.lse_dst + ((size_t)b * a.Hq + h) * (a.S * (a.wave_slots > 1 ? a.wave_slots : 1)) + s;
+  return a.lse_dst + ((size_t)b * a.Hq + h) * a.S + s;
 }
 
 // An empty split (or an empty history when final_out): o = 0, lse = -inf.

@@ -238,7 +238,7 @@ int fd_workspace_size(const fd_shape* shape, int num_splits, size_t* bytes) {
   if (!bytes) return FD_ERR_INVALID_ARG;
   st = check_splits(s, num_splits);
   if (st != FD_OK) return st;
-  *bytes = workspace_bytes(s, num_splits * 4);   // experiment: per-wave slots
+  *bytes = workspace_bytes(s, num_splits);
   return FD_OK;
 }
 
@@ -265,11 +265,8 @@ static int decode_attn(const fd_shape* shape, const void* q,
   if (!out || !aligned16(out)) return FD_ERR_INVALID_ARG;
   if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0)
     return FD_ERR_INVALID_ARG;
-  // Experiment: batch-one bf16 calls give every wave its own partial slot.
-  const int wslots =
-      (num_splits > 1 && s.B == 1 && s.dtype == FD_DTYPE_BF16) ? 4 : 1;
   if (num_splits > 1) {
-    if (!workspace || ws_bytes < workspace_bytes(s, num_splits * wslots))
+    if (!workspace || ws_bytes < workspace_bytes(s, num_splits))
       return FD_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FD_ERR_INVALID_ARG;
   }
@@ -289,8 +286,7 @@ static int decode_attn(const fd_shape* shape, const void* q,
   }
   float* o_part = static_cast<float*>(workspace);
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             partial_o_bytes(s, num_splits * wslots));
-  a.wave_slots = wslots;
+                                             partial_o_bytes(s, num_splits));
   a.o_dst = o_part;
   a.lse_dst = lse_part;
   a.final_out = 0;
@@ -302,7 +298,7 @@ static int decode_attn(const fd_shape* shape, const void* q,
   c.lse_out = lse_out;
   c.B = s.B;
   c.Hq = s.Hq;
-  c.S = num_splits * wslots;
+  c.S = num_splits;
   return launch_combine(s.D, c, stream) == 0 ? FD_OK : FD_ERR_HIP;
 }
 

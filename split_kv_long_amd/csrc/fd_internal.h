@@ -73,7 +73,6 @@ struct SplitArgs {
   int balance_cus;    // > 0 (CU count): length-aware pieces for batches
   int bal_target;     // set by the launcher: pieces per kv head unit
   float scale_log2;   // scale * log2(e)
-  int wave_slots;     // >1: each wave writes its own partial slot
 };
 
 struct CombineArgs {

@@ -802,29 +802,6 @@ void split_mfma(
 
   // Per-head sum over the 4 lane groups; then park (O, m, l) in LDS.
   l_run = sum_x32(sum_x16(l_run));
-  // Experiment: every wave writes its own normalised partial to slot
-  // s * NW + w (no LDS merge); the combine then reduces NW x the slots.
-  if (!BAL && a.wave_slots > 1) {
-    const float vsc = QM == kCacheE4M3 ? a.v_scale[kvh] : 1.f;
-    if (n < nh) {
-      const bool none = m_run == -INFINITY;
-      const float f = none ? 0.f : vsc / l_run;
-      float* dst = o_dst<D>(a, b, h0 + n, s * NW + w);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* row = dst + out_dim<D>(0, i, j);
-        *reinterpret_cast<f32x4*>(row) =
-            f32x4{o[0][i], o[1][i], o[2][i], o[3][i]} * f;
-        if (D == 128)
-          *reinterpret_cast<f32x4*>(row + 4) =
-              f32x4{o[4][i], o[5][i], o[6][i], o[7][i]} * f;
-      }
-      if (j == 0)
-        *lse_dst(a, b, h0 + n, s * NW + w) =
-            none ? -INFINITY : (m_run + flog2(l_run)) * kLn2;
-    }
-    return;
-  }
   if (n < nh) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
