@@ -863,21 +863,8 @@ __global__ __launch_bounds__(64) void combine_kernel(
   constexpr int SL = D / 16;                // slices per head
   constexpr int CH = 8;                     // splits per lane per chunk
   const int lane = threadIdx.x;
-  // Experiment: workgroups are dealt round-robin to the 8 XCDs (id mod 8),
-  // and two slices share each 128-byte line of a partial row: the slices of
-  // one head all go to one XCD, so its L2 fetches every line once. Heads
-  // past the last multiple of 8 take consecutive ids.
-  const int nbh8 = (int)(gridDim.x / SL) & ~7;
-  int bh, sl;
-  if ((int)blockIdx.x < nbh8 * SL) {
-    const int r = (int)blockIdx.x >> 3;
-    bh = (r / SL) * 8 + ((int)blockIdx.x & 7);
-    sl = r % SL;
-  } else {
-    const int k = (int)blockIdx.x - nbh8 * SL;
-    bh = nbh8 + k / SL;
-    sl = k % SL;
-  }
+  const int bh = blockIdx.x / SL;
+  const int sl = blockIdx.x - bh * SL;
   const int g = lane >> 2, qd = lane & 3;
   const float* lse = lse_part + (size_t)bh * S;
   const float* op = o_part + (size_t)bh * S * D + 16 * sl + 4 * qd;
