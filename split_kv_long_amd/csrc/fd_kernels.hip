@@ -939,7 +939,7 @@ dim3 split_grid(int units, int B, int S) {
 // requests help; 16 waves were no better).
 int split_waves(int P, bool f8) {
   const int nsub = (P + 31) / 32;
-  return f8 && nsub > 8 ? 16 : 4;   // experiment: 16 waves for 8-bit caches
+  return f8 && nsub > 8 ? 8 : 4;
 }
 
 // The leading scalar arguments are what a wave needs before its first K/V
@@ -958,9 +958,7 @@ void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
 template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false>
 void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
   constexpr bool F8 = QM != kCacheBf16;
-  if (F8 && nw == 16)
-    launch_one<D, F8 ? 16 : 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
-  else if (F8 && nw == 8)
+  if (F8 && nw == 8)
     launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
   else
     launch_one<D, 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
