@@ -402,17 +402,15 @@ constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
 //     product, while the softmax sum takes the unscaled probability.
 //     Positions at or past the length are masked, whatever their scales.
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
-          bool BAL = false, int SUBW = 1>
+          bool BAL = false>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(
-    split_waves_per_simd(QM != kCacheBf16 && SUBW == 1))))
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(QM != kCacheBf16))))
 void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,
     const int32_t* __restrict__ bt_or_lens, int bs, SplitArgs a) {
   constexpr bool F8 = QM != kCacheBf16;     // one byte per element
   constexpr bool I8 = QM == kCacheI8;
-  static_assert(SUBW == 1 || QM == kCacheE4M3, "chunks of two subtiles: E4M3");
   using KT = typename std::conditional<F8, uint8_t, uint16_t>::type;
   using VT = typename std::conditional<F8, u32x2, u32x4>::type;
   const KT* __restrict__ K = static_cast<const KT*>(Kp);
@@ -583,12 +581,10 @@ void split_mfma(
       return;
     }
   }
-  const int t_first = lo + 32 * SUBW * w;
-  u32x4 kp[2][KL], kp2[2][KL];
-  VT vp[8], vp2[8];
+  const int t_first = lo + 32 * w;
+  u32x4 kp[2][KL];
+  VT vp[8];
   load_subtile(min(t_first, (hi - 1) & ~15), hi, kp, vp, 3);
-  if constexpr (SUBW == 2)
-    load_subtile(min(t_first + 32, (hi - 1) & ~15), hi, kp2, vp2, 3);
 
   // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
   // scores are computed and never used.
@@ -755,52 +751,15 @@ void split_mfma(
   // The first subtile is consumed without a branch on the length (a branch
   // would let the compiler sink its loads behind the length load). A
   // subtile past hi is fully masked and changes nothing.
-  if (SPEC && t_first + 32 * SUBW > hi) {
+  if (SPEC && t_first + 32 > hi) {
     // Rows at or past hi were read speculatively: zero their V.
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int t = t_first + (e < 4 ? 4 * j + e : 12 + 4 * j + e);
       if (t >= hi) vp[e] = VT{};
-      if (SUBW == 2 && t + 32 >= hi) vp2[e] = VT{};
     }
   }
-  if constexpr (SUBW == 2) {
-    // Experiment: E4M3 in chunks of two subtiles (64 positions, as many
-    // bytes as one bf16 subtile) with reissue on arrival: once a chunk is
-    // in registers the next one is requested, then the chunk is consumed.
-    u32x4 kq[2][KL], kq2[2][KL];
-    VT vq[8], vq2[8];
-    auto chunk = [&](int tc, const u32x4 (&k0)[2][KL], const VT (&v0)[8],
-                     const u32x4 (&k1)[2][KL], const VT (&v1)[8],
-                     u32x4 (&kn0)[2][KL], VT (&vn0)[8], u32x4 (&kn1)[2][KL],
-                     VT (&vn1)[8], bool first) -> bool {
-      const int tn = tc + 64 * NW;
-      const bool more = tn < hi;
-#pragma unroll
-      for (int tg = 0; tg < 2; ++tg)
-#pragma unroll
-        for (int c = 0; c < KL; ++c)
-          asm volatile("" ::"v"(k0[tg][c]), "v"(k1[tg][c]));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(v0[e]), "v"(v1[e]));
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) {
-        load_subtile(tn, hi, kn0, vn0, 3);
-        if (tn + 32 < hi) load_subtile(tn + 32, hi, kn1, vn1, 3);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      compute_subtile(tc, k0, v0, [] {});
-      if (first || tc + 32 < hi) compute_subtile(tc + 32, k1, v1, [] {});
-      return more;
-    };
-    if (chunk(t_first, kp, vp, kp2, vp2, kq, vq, kq2, vq2, true)) {
-      for (int t0 = t_first + 64 * NW;; t0 += 128 * NW) {
-        if (!chunk(t0, kq, vq, kq2, vq2, kp, vp, kp2, vp2, false)) break;
-        if (!chunk(t0 + 64 * NW, kp, vp, kp2, vp2, kq, vq, kq2, vq2, false))
-          break;
-      }
-    }
-  } else if constexpr (kPipe) {
+  if constexpr (kPipe) {
     // Two register sets, used in turn. An empty asm statement that takes a
     // subtile's registers as inputs makes the compiler wait for exactly
     // those loads there; the scheduling barriers keep the next requests
@@ -988,9 +947,9 @@ int split_waves(int P, bool f8) {
 // at dispatch, so no wave waits on an argument load before its first
 // request (such loads queue behind other waves' K/V traffic).
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
-          bool BAL = false, int SUBW = 1>
+          bool BAL = false>
 void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL, SUBW>), grid,
+  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL>), grid,
                      dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
                      a.nhg, a.G, PAGED ? a.block_table : a.seq_lens, a.bs, a);
@@ -999,10 +958,7 @@ void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
 template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false>
 void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
   constexpr bool F8 = QM != kCacheBf16;
-  if (QM == kCacheE4M3 && nw == 8)   // experiment: 4 waves, 64-token chunks
-    launch_one<D, 4, GM, PAGED, SPEC, QM, BAL, QM == kCacheE4M3 ? 2 : 1>(
-        grid, a, st);
-  else if (F8 && nw == 8)
+  if (F8 && nw == 8)
     launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
   else
     launch_one<D, 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
