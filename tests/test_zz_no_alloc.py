@@ -66,3 +66,43 @@ def test_noalloc_matches_the_workspace_call_on_two_calls():
         assert np.abs(o2 - ro).max() <= TOL, w.name
         fin = np.isfinite(rl)
         assert np.abs(l2[fin] - rl[fin]).max() <= 1e-4, w.name
+
+
+def test_noalloc_call_replays_in_a_graph():
+    """What the entry point is for: captured in a HIP graph (nothing to
+    allocate, nothing cleared), every replay with eager work between --
+    including a workspace call of another shape -- reproduces the eager
+    result bit for bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = workloads.make("long_gqa_64k", max_seq_len=16384)
+    other = workloads.make("ragged_paged", seed=96, batch=2, max_seq_len=3000,
+                           min_seq_len=1)
+    t, to = inputs(w), inputs(other)
+    shape = fb.make_shape(**w.shape_dict())
+    S = fb.fd_plan_splits(shape, cus, w.sum_seq_len())
+    assert S > 1
+    out = torch.empty(w.batch, w.num_q_heads, w.head_dim, device="cuda")
+    lse = torch.empty(w.batch, w.num_q_heads, device="cuda")
+
+    def call():
+        fb.fd_decode_attn_noalloc(shape, t["q"], t["k"], t["v"], t["bt"],
+                                  t["lens"], S, out, lse)
+    call()
+    torch.cuda.synchronize()
+    ref = (out.cpu().clone(), lse.cpu().clone())
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    print(f"[gpu] noalloc graph capture S={S}", flush=True)
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            call()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        both_calls(other, 3)                 # eager work, scratch reused
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), ref[0]) and torch.equal(lse.cpu(), ref[1])
