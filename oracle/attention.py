@@ -195,7 +195,8 @@ def decode_attention(q, k, v, seq_lens, *, dtype: str,
 
 
 def split_length(max_seq_len: int, num_splits: int, granule: int = 16) -> int:
-    """Tokens per split: ceil(L / S) rounded up to a whole 16-token page.
+    """Tokens per split: ceil(L / S) rounded up to a whole page of
+    ``granule`` tokens (16, or the page size of a paged cache when larger).
 
     The pages say only that the history is cut into parts processed by
     separate blocks; contiguous, equal-length ranges aligned to the page size
@@ -209,18 +210,21 @@ def split_length(max_seq_len: int, num_splits: int, granule: int = 16) -> int:
 
 def split_partials(q, k, v, seq_lens, num_splits: int, *, dtype: str,
                    max_seq_len: int, scale: Optional[float] = None,
-                   block_table=None, block_size: int = 0, granule: int = 16,
+                   block_table=None, block_size: int = 0,
+                   granule: Optional[int] = None,
                    kv_dtype: Optional[str] = None, k_scale=None,
                    v_scale=None):
     """Per-split partial outputs and log-sum-exps (the method's first step).
 
     Split s covers positions [s*P, (s+1)*P) clipped to the history, with
-    P = split_length(L, S). Each partial is attention over that range alone:
+    P = split_length(L, S, g), g = max(16, block_size) unless given. Each
+    partial is attention over that range alone:
     o_s normalised by its own softmax sum, lse_s = ln of that sum. An empty
     range gives o_s = 0, lse_s = -inf.
     Returns o_part [B, Hq, S, D], lse_part [B, Hq, S].
     """
-    P = split_length(max_seq_len, num_splits, granule)
+    P = split_length(max_seq_len, num_splits,
+                     granule or max(16, block_size or 0))
     qf = decode_values(q, dtype)
     B, Hq, D = qf.shape
     o_part = np.zeros((B, Hq, num_splits, D))

@@ -25,6 +25,8 @@ The page defines neither the quantizer nor the rule; the readings taken here
   est[j, h] = ((float(dmax) * s_q) * scale_j) * scale_log2, with
   scale_log2 = float32(scale * log2 e) -- the block's largest logit, in
   base-2 units, as the summary sees it.
+* splits: contiguous ranges of P = ceil(ceil(L / S) / g) * g tokens,
+  g = max(16, page size) -- the dense path's boundaries;
 * top-delta, per split (no cross-split synchronization): with M[h] the
   largest est over the split's blocks and delta2 = float32(delta * log2 e),
   block j is kept when est[j, h] >= float32(M[h] - delta2) for at least one
@@ -207,7 +209,8 @@ def sparse_decode_attention(q, k, v, seq_lens, codes, scales, *, delta: float,
     sc = scale if scale else 1.0 / math.sqrt(D)
     sl2 = log2_units(sc)
     d2 = log2_units(delta) if math.isfinite(delta) else np.float32(np.inf)
-    P = split_length(max_seq_len, num_splits)
+    # Split boundaries as for the dense path: whole pages of max(16, bs).
+    P = split_length(max_seq_len, num_splits, max(16, block_size or 0))
     nblk = -(-max(max_seq_len, 1) // BLOCK)
     out = np.zeros((B, Hq, D))
     lse = np.full((B, Hq), -np.inf)

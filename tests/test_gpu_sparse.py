@@ -464,3 +464,19 @@ def test_sparse_random_shapes_all_encodings():
         S = fd.sparse_splits(shape_of(w), rng.choice([1, 2, 3, 5]))
         check_sparse(w, rng.choice([0.0, 0.5, 2.0, 5.0]), S,
                      expect_dropped=False)
+
+
+
+@pytest.mark.parametrize("kv,bs,g", [(None, 32, 8), ("int8", 32, 48),
+                                     ("fp8_e4m3", 64, 16), (None, 64, 20)])
+def test_sparse_splits_are_whole_pages(kv, bs, g):
+    # With 32- or 64-token pages the split length rounds to whole pages
+    # (L = 5000, S = 3: 1696 or 1728 tokens, not 1680), which moves blocks
+    # between splits and so changes per-split keep decisions; the kept
+    # sets must still equal the oracle's.
+    w = workloads.make("sparse_pages", seed=97, batch=2, num_q_heads=2 * g,
+                       num_kv_heads=2, head_dim=128, max_seq_len=5000,
+                       paged=True, block_size=bs, seq_lens=[5000, 3333],
+                       needles=[5, 1690, 2500, 4999], needle_logit=10.0,
+                       poison_tail=True, kv_dtype=kv)
+    check_sparse(w, 0.5, 3, expect_dropped=False)

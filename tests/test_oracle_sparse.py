@@ -562,3 +562,40 @@ def test_int8_sparse_attention_equals_bf16_on_the_same_values(delta, S, paged):
             scale=a["scale"], block_table=bt, block_size=bs)
         assert np.abs(r8[0] - ref[0]).max() < 1e-12
         assert np.abs(r8[1] - ref[1]).max() < 1e-12
+
+
+# ------------------------------------------------------------- split bounds
+
+def test_split_boundaries_follow_the_page_size():
+    # Splits are whole pages: P = ceil(ceil(L / S) / g) * g with
+    # g = max(16, page size), the dense path's boundaries. With 64-token
+    # pages, L = 5000 and S = 3 that is 1728 (16-token rounding would give
+    # 1680); the per-split maxima, and so the kept sets, depend on it.
+    assert oracle.split_length(5000, 3, 16) == 1680
+    assert oracle.split_length(5000, 3, 32) == 1696
+    assert oracle.split_length(5000, 3, 64) == 1728
+    w = workloads.make("spb", seed=65, batch=1, num_q_heads=2,
+                       num_kv_heads=1, head_dim=32, max_seq_len=5000,
+                       seq_lens=[5000], paged=True, block_size=64,
+                       needles=[1700], needle_logit=12.0)
+    a = w.numpy_view()
+    codes, scales = osp.key_summary(a["k"], a["seq_lens"], a["block_table"],
+                                    64)
+    _, _, est, kept = osp.sparse_decode_attention(
+        a["q"], a["k"], a["v"], a["seq_lens"], codes, scales, delta=0.0,
+        num_splits=3, max_seq_len=5000, scale=a["scale"],
+        block_table=a["block_table"], block_size=64)
+    # delta = 0 keeps, per split, each head's best block: recompute with
+    # the page-aligned boundaries by explicit loops.
+    want = np.zeros(kept.shape[2], dtype=bool)
+    P = 1728
+    for s in range(3):
+        j0, j1 = s * P // 16, min(-(-min((s + 1) * P, 5000) // 16),
+                                  kept.shape[2])
+        for h in range(2):
+            e = est[0, h, j0:j1].astype(np.float32)
+            want[j0:j1] |= e >= e.max()
+    assert np.array_equal(kept[0, 0], want)
+    # The needle's block (1700 // 16 = 106) is in split 0 here, in split 1
+    # with 16-token rounding (1680): it must be the best of split 0.
+    assert kept[0, 0, 106]
