@@ -299,10 +299,13 @@ def test_drifting_logits(rise, period):
                       ref_out, ref_lse)
 
 
-def test_partials_and_combine_entry_points():
+@pytest.mark.parametrize("bs", [16, 64])
+def test_partials_and_combine_entry_points(bs):
+    # With 64-token pages the splits are whole pages: 192 tokens for
+    # L = 900, S = 7 (16-token rounding would give 144).
     w = workloads.make("ragged_paged", seed=28, batch=3, num_q_heads=16,
                        num_kv_heads=4, head_dim=128, max_seq_len=900,
-                       min_seq_len=1, poison_tail=True)
+                       min_seq_len=1, poison_tail=True, block_size=bs)
     S = 7
     t = device_inputs(w)
     shape = shape_of(w)

@@ -187,7 +187,8 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
          num_kv_heads: Optional[int] = None, head_dim: Optional[int] = None,
          max_seq_len: Optional[int] = None, dtype: Optional[str] = None,
          scale: Optional[float] = "spec", paged: Optional[bool] = None,
-         block_size: int = 16, seq_lens: Optional[Sequence[int]] = None,
+         block_size: Optional[int] = None,
+         seq_lens: Optional[Sequence[int]] = None,
          min_seq_len: Optional[int] = None,
          hot_key_fraction: float = None, hot_key_gain: float = None,
          poison_tail: bool = False,
@@ -238,7 +239,9 @@ def make(name: str = "custom", *, seed: Optional[int] = None,
     assert kvd in (None, FP8, INT8) and (kvd is None or dt == BF16)
     sc = spec.get("scale") if scale == "spec" else scale
     pg = spec.get("paged", False) if paged is None else paged
-    bs = (spec.get("block_size", block_size) if pg else 0)
+    # An explicit page size overrides the recipe's (16 when neither says).
+    bs = ((block_size if block_size is not None
+           else spec.get("block_size", 16)) if pg else 0)
     hk_frac = (spec.get("hot_key_fraction", 0.0) if hot_key_fraction is None
                else hot_key_fraction)
     hk_gain = (spec.get("hot_key_gain", 1.0) if hot_key_gain is None
