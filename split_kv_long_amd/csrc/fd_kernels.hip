@@ -823,21 +823,32 @@ void split_mfma(
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
     const int g = idx / (D / 4);
     const int d = 4 * (idx - g * (D / 4));
-    float M = mm[0][g];
+    // Every LDS read goes out at once (one round trip), and the
+    // normalisation uses the hardware reciprocal (1 ulp).
+    float mw[NW], lw[NW];
+    f32x4 ow[NW];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, mm[ww][g]);
+    for (int ww = 0; ww < NW; ++ww) {
+      mw[ww] = mm[ww][g];
+      lw[ww] = ml[ww][g];
+      ow[ww] = *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
+    }
+    float M = mw[0];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, mw[ww]);
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
     const float Ms = M == -INFINITY ? 0.f : M;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const float wt = fexp2(mm[ww][g] - Ms);
-      acc += wt * *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
-      lsum += wt * ml[ww][g];
+      const float wt = fexp2(mw[ww] - Ms);
+      acc += wt * ow[ww];
+      lsum += wt * lw[ww];
     }
     const bool none = M == -INFINITY;       // no token in this split
+    const f32x4 res = acc * (vsc * __builtin_amdgcn_rcpf(lsum));
     *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + g, s) + d) =
-        none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (vsc / lsum);
+        none ? f32x4{0.f, 0.f, 0.f, 0.f} : res;
     if (d == 0) {
       float* l = lse_dst(a, b, h0 + g, s);
       if (l) *l = none ? -INFINITY : (M + flog2(lsum)) * kLn2;
@@ -912,9 +923,10 @@ __global__ __launch_bounds__(64) void combine_kernel(
   z += __shfl_xor(z, 8);
   z = sum_x32(sum_x16(z));
   float* out = out_base + (size_t)bh * D + 16 * sl + 4 * qd;
+  const f32x4 res = acc * __builtin_amdgcn_rcpf(z);   // 1 ulp
   if (g == 0)
     *reinterpret_cast<f32x4*>(out) =
-        M == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / z);
+        M == -INFINITY ? f32x4{0.f, 0.f, 0.f, 0.f} : res;
   if (lane == 0 && sl == 0 && lse_out)
     lse_out[bh] = M == -INFINITY ? -INFINITY : M + flog2(z) * kLn2;
 }

@@ -602,21 +602,31 @@ void split_sparse(SplitArgs a, SparseArgs sp) {
     for (int idx = threadIdx.x; idx < ng * (D / 4); idx += NW * 64) {
       const int g = idx / (D / 4);
       const int d = 4 * (idx - g * (D / 4));
-      float Mx = mm[0][g];
+      // As in the dense kernel: every LDS read at once, hardware reciprocal.
+      float mw[NW], lw[NW];
+      f32x4 ow[NW];
 #pragma unroll
-      for (int ww = 1; ww < NW; ++ww) Mx = fmaxf(Mx, mm[ww][g]);
+      for (int ww = 0; ww < NW; ++ww) {
+        mw[ww] = mm[ww][g];
+        lw[ww] = ml[ww][g];
+        ow[ww] = *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
+      }
+      float Mx = mw[0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) Mx = fmaxf(Mx, mw[ww]);
       const float Ms = Mx == -INFINITY ? 0.f : Mx;
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
       float lsum = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
-        const float wt = fexp2(mm[ww][g] - Ms);
-        acc += wt * *reinterpret_cast<const f32x4*>(&mo[ww][g][d]);
-        lsum += wt * ml[ww][g];
+        const float wt = fexp2(mw[ww] - Ms);
+        acc += wt * ow[ww];
+        lsum += wt * lw[ww];
       }
       const bool none = Mx == -INFINITY;
+      const f32x4 res = acc * (vsc * __builtin_amdgcn_rcpf(lsum));
       *reinterpret_cast<f32x4*>(o_dst<D>(a, b, h0 + hb + g, s) + d) =
-          none ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (vsc / lsum);
+          none ? f32x4{0.f, 0.f, 0.f, 0.f} : res;
       if (d == 0) {
         float* l = lse_dst(a, b, h0 + hb + g, s);
         if (l) *l = none ? -INFINITY : (Mx + flog2(lsum)) * kLn2;
