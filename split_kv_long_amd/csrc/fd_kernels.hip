@@ -299,14 +299,21 @@ __device__ __forceinline__ int wave_sum(int v) {
                                                     false, false);
   return (int)(r32[0] + r32[1]);
 }
+// Inclusive prefix sum over the wave without LDS: shifts by 1, 2, 4 and 8
+// inside each 16-lane row (DPP; lanes shifted in from outside the row read
+// 0), then each row adds the totals of the rows below it (read from lanes
+// 15, 31 and 47 into scalars).
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int x = __shfl_up(v, off);
-    if (lane >= off) v += x;
-  }
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) +
+         (lane >= 48 ? r2 : 0);
 }
 
 __device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
@@ -348,7 +355,7 @@ __device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
   const int unused = lane < B ? S - nb : 0;
   const int incl = wave_incl_scan(nb);
   const int eincl = wave_incl_scan(unused);
-  const int total = __shfl(incl, 63);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
   // Dispatch-order index: kv head unit fastest, then piece.
   const unsigned gid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   Piece pc;
@@ -357,11 +364,12 @@ __device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
   if (i < total) {
     const unsigned long long m = __builtin_amdgcn_ballot_w64(
         lane < B && i >= incl - nb && i < incl);
-    const int bb = __builtin_ctzll(m);
+    // bb is wave-uniform (from a ballot): read its values as scalars.
+    const int bb = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
     pc.b = bb;
-    const int lb = __shfl(len, bb);
-    const int npc = __shfl(nb, bb);
-    const int p = i - (__shfl(incl, bb) - npc);
+    const int lb = __builtin_amdgcn_readlane(len, bb);
+    const int npc = __builtin_amdgcn_readlane(nb, bb);
+    const int p = i - (__builtin_amdgcn_readlane(incl, bb) - npc);
     const long long len_p =                     // equal pieces
         (((long long)lb + npc - 1) / npc + 15) & ~15LL;
     pc.slot = p;
@@ -371,9 +379,11 @@ __device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
     const int k = i - total;
     const unsigned long long m = __builtin_amdgcn_ballot_w64(
         lane < B && k >= eincl - unused && k < eincl);
-    const int bb = __builtin_ctzll(m);
+    const int bb = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
     pc.b = bb;
-    pc.slot = __shfl(nb, bb) + (k - (__shfl(eincl, bb) - __shfl(unused, bb)));
+    pc.slot = __builtin_amdgcn_readlane(nb, bb) +
+              (k - (__builtin_amdgcn_readlane(eincl, bb) -
+                    __builtin_amdgcn_readlane(unused, bb)));
     pc.lo = pc.hi = 0;
   }
   return pc;
@@ -885,19 +895,28 @@ __global__ __launch_bounds__(64) void combine_kernel(
   for (int base = 0; base < S; base += 16 * CH) {
     float lv[CH];
     f32x4 ov[CH];
+    // Splits past S re-read the last one (every load unconditional, no
+    // branch) and are masked once they have arrived.
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int sp = base + g + 16 * k;
-      const bool ok = sp < S;
-      lv[k] = ok ? lse[sp] : -INFINITY;
-      ov[k] = ok ? *reinterpret_cast<const f32x4*>(op + (size_t)sp * D)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int sp = min(base + g + 16 * k, S - 1);
+      lv[k] = lse[sp];
+      ov[k] = *reinterpret_cast<const f32x4*>(op + (size_t)sp * D);
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const bool ok = base + g + 16 * k < S;
+      lv[k] = ok ? lv[k] : -INFINITY;
+      ov[k] = ok ? ov[k] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float mx = lv[0];
 #pragma unroll
     for (int k = 1; k < CH; ++k) mx = fmaxf(mx, lv[k]);
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
-    mx = fmaxf(mx, __shfl_xor(mx, 8));
+    // The 4 lanes of a 16-lane row with the same dims (lane % 4) hold
+    // split groups g, g + 1, ...: rotations by 4 and 8 inside the row (DPP,
+    // no LDS round trip), then the row exchanges.
+    mx = fmaxf(mx, dpp_f<0x124>(mx));
+    mx = fmaxf(mx, dpp_f<0x128>(mx));
     mx = max_x32(max_x16(mx));
     const float Mn = fmaxf(M, mx);           // wave-uniform
     if (Mn == -INFINITY) continue;
@@ -915,12 +934,12 @@ __global__ __launch_bounds__(64) void combine_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float x = acc[i];
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += dpp_f<0x124>(x);
+    x += dpp_f<0x128>(x);
     acc[i] = sum_x32(sum_x16(x));
   }
-  z += __shfl_xor(z, 4);
-  z += __shfl_xor(z, 8);
+  z += dpp_f<0x124>(z);
+  z += dpp_f<0x128>(z);
   z = sum_x32(sum_x16(z));
   float* out = out_base + (size_t)bh * D + 16 * sl + 4 * qd;
   const f32x4 res = acc * __builtin_amdgcn_rcpf(z);   // 1 ulp
