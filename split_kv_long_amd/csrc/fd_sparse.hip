@@ -131,8 +131,7 @@ __global__ __launch_bounds__(64) void summary_kernel(SummaryArgs a) {
 #pragma unroll
     for (int i = 0; i < QD; ++i) x[i] = 0.f;
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  amax = wave_max_f(amax);                   // DPP and lane swaps, no LDS
   // Correctly rounded fp32 quotients (HIP's default division).
   const float inv = amax > 0.f ? 7.0f / amax : 0.f;
   const float scale = amax > 0.f ? amax / 7.0f : 0.f;
