@@ -10,7 +10,7 @@
 // list), so one pass over K and V suffices.
 //
 // Kernels:
-//   split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL>
+//   split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL, PIPE>
 //                        bf16, 8-bit E4M3 or int8 K/V (QM), head_dim
 //                        64/128. One
 //                        workgroup per (split, kv head x group of <= GM
@@ -21,7 +21,9 @@
 //                        16x16x32 bf16 matrix cores. SPEC: batch one, first
 //                        requests before the length is known. BAL: batched
 //                        calls, length-aware pieces instead of uniform
-//                        splits.
+//                        splits. PIPE: the reissue-on-arrival schedule
+//                        (always for bf16; for E4M3 on long splits of one
+//                        sequence).
 //   split_f32<D>         fp32 caches: LDS-tiled, plain fp32 FMA, exact fp32
 //                        products.
 //   combine_kernel<D>    log-sum-exp reduction of the split partials.
@@ -412,7 +414,7 @@ constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
 //     product, while the softmax sum takes the unscaled probability.
 //     Positions at or past the length are masked, whatever their scales.
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
-          bool BAL = false>
+          bool BAL = false, bool PIPE = QM == kCacheBf16>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(split_waves_per_simd(QM != kCacheBf16))))
 void split_mfma(
@@ -630,15 +632,20 @@ void split_mfma(
   // critical path: it branches (uniformly) around the masking of full
   // subtiles and around unneeded rescales.
   //
-  // bf16 (reissue on arrival): the next subtile's keys are requested once
+  // Reissue on arrival (PIPE): the next subtile's keys are requested once
   // the current keys are in registers, its values once the current values
   // are, each before the current data is used, so a wave's compute never
-  // delays its next request (two subtiles of registers; two waves per
-  // SIMD). Issuing the next subtile earlier, before the current one lands,
-  // measured slower; so did this schedule for 8-bit subtiles (half the
-  // bytes per request, plus the conversions: E4M3 6-12 %, int8 ~25 %
-  // slower at 64K), which keep the plain loop.
-  constexpr bool kPipe = !F8;
+  // delays its next request (two subtiles of registers). bf16 always runs
+  // it (two waves per SIMD); issuing the next subtile earlier, before the
+  // current one lands, measured slower. 8-bit subtiles (half the bytes per
+  // request, plus the conversions) keep the plain loop where a wave streams
+  // few subtiles (E4M3 6-12 %, int8 ~25 % slower at 64K with the schedule)
+  // or where the pieces want two workgroups per CU (its registers leave
+  // room for one); a single sequence's E4M3 splits of 16 or more subtiles
+  // per wave run it (256K: 3-6 % faster). int8 never does: its scales
+  // have one register set.
+  constexpr bool kPipe = PIPE;
+  static_assert(!(PIPE && I8), "int8 scales are single-buffered");
 
   // Four 8-bit codes -> four bf16 (exact).
   auto cvt4 = [](unsigned w) -> uint2 {
@@ -969,7 +976,7 @@ dim3 split_grid(int units, int B, int S) {
 // (the in-register conversion lengthens the compute tail more than extra
 // requests help; 16 waves were no better).
 int split_waves(int P, bool f8) {
-  const int nsub = (P + 31) / 32;
+  const int64_t nsub = ((int64_t)P + 31) / 32;   // P may be near INT32_MAX
   return f8 && nsub > 8 ? 8 : 4;
 }
 
@@ -978,17 +985,24 @@ int split_waves(int P, bool f8) {
 // at dispatch, so no wave waits on an argument load before its first
 // request (such loads queue behind other waves' K/V traffic).
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
-          bool BAL = false>
+          bool BAL = false, bool PIPE = QM == kCacheBf16>
 void launch_one(dim3 grid, const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL>), grid,
+  hipLaunchKernelGGL((split_mfma<D, NW, GM, PAGED, SPEC, QM, BAL, PIPE>), grid,
                      dim3(NW * 64), 0, st, a.k, a.v,
                      static_cast<const uint16_t*>(a.q), a.L, a.P, a.Hkv,
                      a.nhg, a.G, PAGED ? a.block_table : a.seq_lens, a.bs, a);
 }
 
 template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false>
-void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
+void launch_mfma_spec(dim3 grid, int nw, bool pipe8, const SplitArgs& a,
+                      hipStream_t st) {
   constexpr bool F8 = QM != kCacheBf16;
+  if constexpr (QM == kCacheE4M3 && SPEC) {
+    if (pipe8 && nw == 8) {
+      launch_one<D, 8, GM, PAGED, SPEC, QM, BAL, true>(grid, a, st);
+      return;
+    }
+  }
   if (F8 && nw == 8)
     launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
   else
@@ -999,13 +1013,14 @@ void launch_mfma_spec(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
 // full when the caller's bound is its length); for a batch, whose lengths
 // may differ, they could read splits that turn out empty.
 template <int D, bool PAGED, int GM, int QM>
-void launch_mfma_gm(dim3 grid, int nw, const SplitArgs& a, hipStream_t st) {
+void launch_mfma_gm(dim3 grid, int nw, bool pipe8, const SplitArgs& a,
+                    hipStream_t st) {
   if (a.B == 1)
-    launch_mfma_spec<D, PAGED, GM, true, QM>(grid, nw, a, st);
+    launch_mfma_spec<D, PAGED, GM, true, QM>(grid, nw, pipe8, a, st);
   else if (a.bal_target > 0 && a.B <= 64)       // lane = sequence
-    launch_mfma_spec<D, PAGED, GM, false, QM, true>(grid, nw, a, st);
+    launch_mfma_spec<D, PAGED, GM, false, QM, true>(grid, nw, false, a, st);
   else
-    launch_mfma_spec<D, PAGED, GM, false, QM>(grid, nw, a, st);
+    launch_mfma_spec<D, PAGED, GM, false, QM>(grid, nw, false, a, st);
 }
 
 template <int D, bool PAGED, int QM>
@@ -1023,10 +1038,14 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const bool pieces = a.B > 1 && a.B <= 64 && a.bal_target > 0;
   const int nw = QM == kCacheI8 && pieces
                      ? 4 : split_waves(a.P, QM != kCacheBf16);
+  // E4M3, one sequence: the reissue schedule from 16 subtiles per wave
+  // (measured at 256K: 3-6 % faster; at 64K, 2 per wave, 8 % slower).
+  const bool pipe8 = QM == kCacheE4M3 && a.B == 1 &&
+                     ((int64_t)a.P + 31) / 32 >= 16 * nw;
   if (gm == 8)
-    launch_mfma_gm<D, PAGED, 8, QM>(grid, nw, a, st);
+    launch_mfma_gm<D, PAGED, 8, QM>(grid, nw, pipe8, a, st);
   else
-    launch_mfma_gm<D, PAGED, 16, QM>(grid, nw, a, st);
+    launch_mfma_gm<D, PAGED, 16, QM>(grid, nw, pipe8, a, st);
 }
 
 template <int QM>

@@ -474,6 +474,22 @@ def test_fp8_paged_matches_contiguous_bitwise():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("hq,d", [(16, 128), (32, 128), (40, 64)])
+def test_fp8_single_sequence_long_splits(paged, hq, d):
+    """A single sequence's E4M3 splits of 4096 tokens or more (16 subtiles
+    per wave and up) take the reissue schedule: full histories, lengths
+    ending inside a subtile and inside the last split, NaN-poisoned slots
+    past the length, one and two head passes."""
+    for i, (L, n) in enumerate(((8192, 8192), (8192, 8179), (12288, 9001))):
+        w = workloads.make("fp8long", seed=46 + i, batch=1, num_q_heads=hq,
+                           num_kv_heads=2, head_dim=d, max_seq_len=L,
+                           paged=paged, seq_lens=[n], poison_tail=True,
+                           kv_dtype="fp8_e4m3")
+        for S in (1, 2):
+            check(w, S)
+
+
 # ------------------------------- 8-bit integer cache, per-position scales
 
 def test_int8_64k_at_planned_and_forced_splits():
