@@ -1031,10 +1031,10 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   a.bal_target = a.balance_cus > 0 && a.S > 1
                      ? max(1, 2 * a.balance_cus / (s.Hkv * a.nhg)) : 0;
   const dim3 grid = split_grid(s.Hkv * a.nhg, s.B, a.S);
-  // The int8 kernel with length-aware pieces (batches of 2..64) holds
-  // ~148 VGPRs, 3 waves per SIMD: with 8 waves a CU holds one of its
-  // workgroups, with 4 the two per CU the pieces are sized for (measured
-  // 5-6 % faster on the ragged batch of 16, contiguous and paged).
+  // int8 length-aware pieces (batches of 2..64) run 4 waves: 5-6 % faster
+  // than 8 on the ragged batch of 16 when the kernel held ~148 VGPRs (one
+  // 8-wave workgroup per CU), and still 1.5-4 % faster at its present
+  // 118-126, where two would fit.
   const bool pieces = a.B > 1 && a.B <= 64 && a.bal_target > 0;
   const int nw = QM == kCacheI8 && pieces
                      ? 4 : split_waves(a.P, QM != kCacheBf16);
