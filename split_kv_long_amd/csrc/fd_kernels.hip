@@ -641,8 +641,8 @@ void split_mfma(
   // request, plus the conversions) keep the plain loop where a wave streams
   // few subtiles (E4M3 6-12 %, int8 ~25 % slower at 64K with the schedule)
   // or where the pieces want two workgroups per CU (its registers leave
-  // room for one); a single sequence's E4M3 splits of 16 or more subtiles
-  // per wave run it (256K: 3-6 % faster). int8 never does: its scales
+  // room for one); a single sequence's E4M3 splits of 8 or more subtiles
+  // per wave run it (2-6 % faster). int8 never does: its scales
   // have one register set.
   constexpr bool kPipe = PIPE;
   static_assert(!(PIPE && I8), "int8 scales are single-buffered");
@@ -1038,10 +1038,11 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const bool pieces = a.B > 1 && a.B <= 64 && a.bal_target > 0;
   const int nw = QM == kCacheI8 && pieces
                      ? 4 : split_waves(a.P, QM != kCacheBf16);
-  // E4M3, one sequence: the reissue schedule from 16 subtiles per wave
-  // (measured at 256K: 3-6 % faster; at 64K, 2 per wave, 8 % slower).
+  // E4M3, one sequence: the reissue schedule from 8 subtiles per wave
+  // (measured 2-6 % faster at 8 and 32 per wave; even at 4; at 64K, 2 per
+  // wave, 8 % slower).
   const bool pipe8 = QM == kCacheE4M3 && a.B == 1 &&
-                     ((int64_t)a.P + 31) / 32 >= 16 * nw;
+                     ((int64_t)a.P + 31) / 32 >= 8 * nw;
   if (gm == 8)
     launch_mfma_gm<D, PAGED, 8, QM>(grid, nw, pipe8, a, st);
   else

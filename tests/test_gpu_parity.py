@@ -477,16 +477,17 @@ def test_fp8_paged_matches_contiguous_bitwise():
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("hq,d", [(16, 128), (32, 128), (40, 64)])
 def test_fp8_single_sequence_long_splits(paged, hq, d):
-    """A single sequence's E4M3 splits of 4096 tokens or more (16 subtiles
+    """A single sequence's E4M3 splits of 2048 tokens or more (8 subtiles
     per wave and up) take the reissue schedule: full histories, lengths
     ending inside a subtile and inside the last split, NaN-poisoned slots
-    past the length, one and two head passes."""
+    past the length, one and two head passes (S = 4 is the threshold
+    itself at L = 8192)."""
     for i, (L, n) in enumerate(((8192, 8192), (8192, 8179), (12288, 9001))):
         w = workloads.make("fp8long", seed=46 + i, batch=1, num_q_heads=hq,
                            num_kv_heads=2, head_dim=d, max_seq_len=L,
                            paged=paged, seq_lens=[n], poison_tail=True,
                            kv_dtype="fp8_e4m3")
-        for S in (1, 2):
+        for S in (1, 2, 4):
             check(w, S)
 
 
