@@ -972,9 +972,9 @@ dim3 split_grid(int units, int B, int S) {
 // split length (64K, 256K, the ragged batch and the batch of 64 short
 // histories; 8 waves, or 4 waves with two subtiles requested at once, were
 // 1-4 % slower). The 8-bit caches (E4M3 and int8; 64K and 256K,
-// S = 64..256) keep the plain loop with 8 waves from 9 subtiles per split
-// (the in-register conversion lengthens the compute tail more than extra
-// requests help; 16 waves were no better).
+// S = 64..256) run 8 waves from 9 subtiles per split (16 waves were no
+// better at 64K, and 0-5 % slower on 8192-token splits), on the plain loop
+// except a single sequence's long E4M3 splits (see launch_mfma).
 int split_waves(int P, bool f8) {
   const int64_t nsub = ((int64_t)P + 31) / 32;   // P may be near INT32_MAX
   return f8 && nsub > 8 ? 8 : 4;
