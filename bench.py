@@ -279,10 +279,11 @@ def copy_probe(torch):
 
 
 # Shapes the read probe is timed at: the split kernel's launch shape at
-# the headline workload (256 workgroups of 4 waves, 8 KB per wave in
-# flight) and the others a sweep found fastest on MI355X.
-PROBE_SHAPES = [(256, 4, 8), (256, 16, 2), (256, 16, 4), (512, 4, 8),
-                (2048, 8, 2)]
+# the headline workload (256 workgroups of 4 waves, 16 KB per wave in
+# flight: a 32-token subtile of K and of V), the same grid with half of
+# that in flight, and the others a sweep found fastest on MI355X.
+PROBE_SHAPES = [(256, 4, 16), (256, 4, 8), (256, 16, 2), (256, 16, 4),
+                (512, 4, 8), (2048, 8, 2)]
 
 
 def read_probe(torch, nbytes, steps, warmup):
@@ -310,7 +311,7 @@ def read_probe(torch, nbytes, steps, warmup):
     del bufs
     best = max(shapes, key=lambda k: shapes[k]["GBps"])
     return {"bytes": n, "copies_rotated": R, "shapes": shapes,
-            "split_grid_shape": "256x4w_128B", "best_shape": best,
+            "split_grid_shape": "256x4w_256B", "best_shape": best,
             "best_GBps": shapes[best]["GBps"]}
 
 
@@ -476,6 +477,12 @@ def run_one(args, name, steps, warmup, with_cpu):
             rec["roofline"]["probe_GBps"] = probe["best_GBps"]
             rec["roofline"]["frac_of_probe"] = round(
                 split_gbps / probe["best_GBps"], 4)
+            same = probe["shapes"].get(probe["split_grid_shape"])
+            if same:
+                # against a bare read with the split kernel's grid and
+                # bytes in flight per wave
+                rec["roofline"]["frac_of_probe_same_shape"] = round(
+                    split_gbps / same["GBps"], 4)
             rec["read_probe"] = probe
     if args.copy_probe and name == args.workload:
         rec["copy_probe"] = copy_probe(torch)
