@@ -593,15 +593,15 @@ void split_mfma(
       return;
     }
   }
-  const int t_first = lo + 32 * w;
-  u32x4 kp[2][KL];
-  VT vp[8];
-  load_subtile(min(t_first, (hi - 1) & ~15), hi, kp, vp, 3);
-
   // Q^T fragments. Padded columns (n >= nh) load head h0's row: their
-  // scores are computed and never used.
+  // scores are computed and never used. Loads return in order, so a wait
+  // for Q also waits for every request issued before it: a batch's waves
+  // (their length already known) request Q ahead of the first subtile,
+  // while a single sequence's waves send the first subtile out first (Q
+  // first measured 0.4 us slower at 64K) and so do int8 batches (0.7 %
+  // slower with Q first).
   bf16x8 qf[KC];
-  {
+  auto load_q = [&] {
     const uint16_t* qp =
         Q + ((size_t)b * G * Hkv + h0 + (n < nh ? n : 0)) * D;
 #pragma unroll
@@ -609,7 +609,14 @@ void split_mfma(
       const int d0 = F8 ? 16 * j + 64 * (c >> 1) + 8 * (c & 1) : 8 * j + 32 * c;
       qf[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + d0));
     }
-  }
+  };
+  const int t_first = lo + 32 * w;
+  constexpr bool kQFirst = !SPEC && !I8;
+  if (kQFirst) load_q();
+  u32x4 kp[2][KL];
+  VT vp[8];
+  load_subtile(min(t_first, (hi - 1) & ~15), hi, kp, vp, 3);
+  if (!kQFirst) load_q();
 
   // With SPEC nothing branches on the length before the compute: a split
   // past the end of its sequence computes nothing and is written as empty
@@ -784,9 +791,9 @@ void split_mfma(
     u32x4 kq[2][KL];
     VT vq[8];
     auto step = [&](int tc, const u32x4 (&kc)[2][KL], const VT (&vc)[8],
-                    u32x4 (&kn)[2][KL], VT (&vn)[8]) -> bool {
+                    u32x4 (&kn)[2][KL], VT (&vn)[8], auto more_c) {
+      constexpr bool more = decltype(more_c)::value;
       const int tn = tc + 32 * NW;
-      const bool more = tn < hi;
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg)
 #pragma unroll
@@ -801,11 +808,23 @@ void split_mfma(
         if (more) load_subtile(tn, hi, kn, vn, 2);
         __builtin_amdgcn_sched_barrier(0);
       });
-      return more;
     };
-    for (int t0 = t_first;; t0 += 64 * NW) {
-      if (!step(t0, kp, vp, kq, vq)) break;
-      if (!step(t0 + 32 * NW, kq, vq, kp, vp)) break;
+    // Whether a step requests the next subtile is fixed when the code is
+    // generated: with a run-time condition the compiler's wait counts are
+    // those of the path that requested nothing, so every step would also
+    // wait for the next subtile's keys before using its own values (64K
+    // batch-one split kernel 12.4 -> 12.15 us without that wait).
+    const int nsub = t_first < hi ? (hi - t_first - 1) / (32 * NW) + 1 : 1;
+    int t0 = t_first, rem = nsub;
+    for (; rem > 2; rem -= 2, t0 += 64 * NW) {
+      step(t0, kp, vp, kq, vq, std::true_type{});
+      step(t0 + 32 * NW, kq, vq, kp, vp, std::true_type{});
+    }
+    if (rem == 2) {
+      step(t0, kp, vp, kq, vq, std::true_type{});
+      step(t0 + 32 * NW, kq, vq, kp, vp, std::false_type{});
+    } else {
+      step(t0, kp, vp, kq, vq, std::false_type{});
     }
   } else {
     compute_subtile(t_first, kp, vp, [] {});
