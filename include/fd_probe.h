@@ -21,7 +21,8 @@
  *                   workgroups * waves * 64 * 16 * loads_per_lane
  *   workgroups      1 .. 65535
  *   waves           4, 8 or 16 per workgroup
- *   loads_per_lane  2, 4, 8 or 16 sixteen-byte loads per lane per batch
+ *   loads_per_lane  2, 4 or 8 sixteen-byte loads per lane per batch, or
+ *                   16 with at most 8 waves
  *   sink            device uint32 [workgroups] (written only in the
  *                   improbable case; must be valid)
  *   stream          hipStream_t as void* (NULL = null stream)

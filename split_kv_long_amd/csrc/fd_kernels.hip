@@ -392,10 +392,11 @@ __device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
 }
 
 
-// Waves per SIMD the register allocation targets: two for bf16, whose
-// waves hold two subtiles of registers (the reissue schedule below), three
-// for the 8-bit caches.
-constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
+// Waves per SIMD the register allocation targets: two wherever a wave
+// holds two subtiles of registers (the reissue schedule below: bf16, and
+// E4M3 on a single sequence's long splits, whose 8-wave workgroups fill a
+// CU at two waves per SIMD anyway), three for the 8-bit caches' plain loop.
+constexpr int split_waves_per_simd(bool two_sets) { return two_sets ? 2 : 3; }
 
 // 8-bit caches (QM != kCacheBf16). A lane reads 16 bytes = 16 dims of a key
 // row per request (dims 16(j + 4c)..+15) and 8 bytes = 8 dims of a value
@@ -416,7 +417,7 @@ constexpr int split_waves_per_simd(bool f8) { return f8 ? 3 : 2; }
 template <int D, int NW, int GM, bool PAGED, bool SPEC, int QM,
           bool BAL = false, bool PIPE = QM == kCacheBf16>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(QM != kCacheBf16))))
+__attribute__((amdgpu_waves_per_eu(split_waves_per_simd(PIPE))))
 void split_mfma(
     const void* __restrict__ Kp, const void* __restrict__ Vp,
     const uint16_t* __restrict__ Q, int L, int P, int Hkv, int nhg, int G,

@@ -68,7 +68,7 @@ int launch_probe(const u32x4* buf, unsigned per, int wg, int u, uint32_t* sink,
   else if (u == 8)
     hipLaunchKernelGGL((read_probe<NW, 8>), dim3(wg), dim3(NW * 64), 0, st,
                        buf, per, sink);
-  else
+  else if constexpr (NW <= 8)   // 16 loads per lane: two sets fill 128 VGPRs
     hipLaunchKernelGGL((read_probe<NW, 16>), dim3(wg), dim3(NW * 64), 0, st,
                        buf, per, sink);
   return (int)hipGetLastError();
@@ -86,7 +86,7 @@ extern "C" int fd_read_probe(const void* buf, size_t bytes, int workgroups,
   if (workgroups < 1 || workgroups > 65535) return FD_ERR_INVALID_ARG;
   if (waves != 4 && waves != 8 && waves != 16) return FD_ERR_INVALID_ARG;
   if (loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8 &&
-      loads_per_lane != 16)
+      !(loads_per_lane == 16 && waves <= 8))
     return FD_ERR_INVALID_ARG;
   const size_t step = (size_t)waves * 64 * 16 * loads_per_lane;
   if (bytes == 0 || bytes % ((size_t)workgroups * step) != 0)

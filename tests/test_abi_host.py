@@ -531,3 +531,26 @@ def test_noalloc_entry_point_refuses_oversized_calls():
         fb.fd_decode_attn_noalloc(fb.make_shape(1, 2, 2, 128, 64), 16, 16,
                                   16, None, 16, 0, 16, None, stream=0)
     assert e.value.status == fb.FD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args", [
+    # (bytes, workgroups, waves, loads_per_lane)
+    (1 << 24, 256, 3, 8),            # waves not 4, 8 or 16
+    (1 << 24, 256, 4, 3),            # loads per lane not 2, 4, 8 or 16
+    (1 << 26, 256, 16, 16),          # 16 loads per lane need <= 8 waves
+    (1 << 24, 0, 4, 8),              # no workgroups
+    (1 << 24, 65536, 4, 8),          # grid past 65535
+    ((1 << 24) + 16, 256, 4, 8),     # bytes not a multiple of a step
+    (0, 256, 4, 8),                  # nothing to read
+])
+def test_read_probe_rejects_bad_args_on_the_host(args):
+    """fd_read_probe validates before it launches anything (a fake aligned
+    device address is never dereferenced)."""
+    lib = fb.load()
+    nbytes, wg, nw, lpl = args
+    sink = ctypes.c_void_p(0x10000)
+    st = lib.fd_read_probe(ctypes.c_void_p(0x100000), ctypes.c_size_t(nbytes),
+                           wg, nw, lpl, sink, None)
+    assert st == fb.FD_ERR_INVALID_ARG
+    assert lib.fd_read_probe(ctypes.c_void_p(0x100008), ctypes.c_size_t(1 << 24),
+                             256, 4, 8, sink, None) == fb.FD_ERR_INVALID_ARG
