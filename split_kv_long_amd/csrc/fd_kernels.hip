@@ -394,8 +394,9 @@ __device__ Piece balanced_piece(const SplitArgs& a, const int32_t* lens,
 
 // Waves per SIMD the register allocation targets: two wherever a wave
 // holds two subtiles of registers (the reissue schedule below: bf16, and
-// E4M3 on a single sequence's long splits, whose 8-wave workgroups fill a
-// CU at two waves per SIMD anyway), three for the 8-bit caches' plain loop.
+// the 8-bit caches on a single sequence's long splits, whose 8-wave
+// workgroups fill a CU at two waves per SIMD anyway), three for the 8-bit
+// caches' plain loop.
 constexpr int split_waves_per_simd(bool two_sets) { return two_sets ? 2 : 3; }
 
 // 8-bit caches (QM != kCacheBf16). A lane reads 16 bytes = 16 dims of a key
@@ -501,7 +502,8 @@ void split_mfma(
   // int8 cache: the per-position scales of the subtile in flight (the
   // lane's rows 4j + e of each 16-row group). Contiguous scale rows are
   // padded to whole groups; a paged pool's pages are whole groups.
-  f32x4 k_sc[2], v_sc[2];
+  struct Sc { f32x4 k[2], v[2]; };       // key and value scales
+  Sc scp;                                 // (part of a subtile's registers)
   const float* __restrict__ k_scales = I8 ? a.k_scale : nullptr;
   const float* __restrict__ v_scales = I8 ? a.v_scale : nullptr;
   const size_t Lp = ((size_t)L + 15) & ~(size_t)15;    // L may be INT32_MAX
@@ -513,7 +515,7 @@ void split_mfma(
   // Requests the subtile starting at t0 with every row clamped below `end`.
   // `part` selects the key requests (1), the value requests (2) or both.
   auto load_subtile = [&](int t0, int end, u32x4 (&kr)[2][KL],
-                          VT (&vr)[8], int part) {
+                          VT (&vr)[8], int part, Sc& sc) {
     const int last0 = min(15, end - 1 - t0);
     const int last1 = end - 1 - (t0 + 16);
     const size_t g0 = group_base(t0);
@@ -539,15 +541,15 @@ void split_mfma(
       const size_t s0 = scale_row(g0, t0) + 4 * j;
       const size_t s1 = last1 >= 0 ? scale_row(g1, t0 + 16) + 4 * j : s0;
       if (part & 1) {
-        k_sc[0] = __builtin_nontemporal_load(
+        sc.k[0] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(k_scales + s0));
-        k_sc[1] = __builtin_nontemporal_load(
+        sc.k[1] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(k_scales + s1));
       }
       if (part & 2) {
-        v_sc[0] = __builtin_nontemporal_load(
+        sc.v[0] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(v_scales + s0));
-        v_sc[1] = __builtin_nontemporal_load(
+        sc.v[1] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(v_scales + s1));
       }
     }
@@ -616,7 +618,7 @@ void split_mfma(
   if (kQFirst) load_q();
   u32x4 kp[2][KL];
   VT vp[8];
-  load_subtile(min(t_first, (hi - 1) & ~15), hi, kp, vp, 3);
+  load_subtile(min(t_first, (hi - 1) & ~15), hi, kp, vp, 3, scp);
   if (!kQFirst) load_q();
 
   // With SPEC nothing branches on the length before the compute: a split
@@ -649,11 +651,10 @@ void split_mfma(
   // request, plus the conversions) keep the plain loop where a wave streams
   // few subtiles (E4M3 6-12 %, int8 ~25 % slower at 64K with the schedule)
   // or where the pieces want two workgroups per CU (its registers leave
-  // room for one); a single sequence's E4M3 splits of 8 or more subtiles
-  // per wave run it (2-6 % faster). int8 never does: its scales
-  // have one register set.
+  // room for one); a single sequence's 8-bit splits of 8 or more subtiles
+  // per wave run it (E4M3 2-6 %, int8 0.6 % faster at 256K; an int8
+  // register set includes the subtile's scales).
   constexpr bool kPipe = PIPE;
-  static_assert(!(PIPE && I8), "int8 scales are single-buffered");
 
   // Four 8-bit codes -> four bf16 (exact).
   auto cvt4 = [](unsigned w) -> uint2 {
@@ -675,7 +676,8 @@ void split_mfma(
 
   // `after_scores` runs between the softmax step and the PV products.
   auto compute_subtile = [&](int t0, const u32x4 (&kr)[2][KL],
-                             const VT (&vraw)[8], auto&& after_scores) {
+                             const VT (&vraw)[8], Sc& sc,
+                             auto&& after_scores) {
     f32x4 sacc[2];
 #pragma unroll
     for (int tg = 0; tg < 2; ++tg) {
@@ -689,7 +691,7 @@ void split_mfma(
     float mx = -INFINITY;
     // Per-score logit scale (an int8 cache's key scale of that position).
     auto lscale = [&](int e) -> float {
-      return I8 ? sl2 * k_sc[e >> 2][e & 3] : sl2;
+      return I8 ? sl2 * sc.k[e >> 2][e & 3] : sl2;
     };
     if (t0 + 32 <= hi) {                    // every token valid (uniform)
 #pragma unroll
@@ -712,7 +714,7 @@ void split_mfma(
           mx = fmaxf(mx, x);
           // A masked position's value scale may be anything (even NaN):
           // its probability is 0 and must stay 0.
-          if constexpr (I8) v_sc[tg][i] = tok < hi ? v_sc[tg][i] : 0.f;
+          if constexpr (I8) sc.v[tg][i] = tok < hi ? sc.v[tg][i] : 0.f;
         }
     }
     mx = max_x32(max_x16(mx));
@@ -736,7 +738,7 @@ void split_mfma(
     for (int e = 0; e < 8; ++e) {
       const float p = fexp2(sv[e] - mref);
       psum += p;
-      const float pw = I8 ? p * v_sc[e >> 2][e & 3] : p;   // value row e
+      const float pw = I8 ? p * sc.v[e >> 2][e & 3] : p;   // value row e
       const __bf16 hb = (__bf16)pw;
       ph[e] = hb;
       pl[e] = (__bf16)(pw - (float)hb);
@@ -791,8 +793,10 @@ void split_mfma(
     // between that wait and the first use of the current data.
     u32x4 kq[2][KL];
     VT vq[8];
+    Sc scq;
     auto step = [&](int tc, const u32x4 (&kc)[2][KL], const VT (&vc)[8],
-                    u32x4 (&kn)[2][KL], VT (&vn)[8], auto more_c) {
+                    Sc& scc, u32x4 (&kn)[2][KL], VT (&vn)[8], Sc& scn,
+                    auto more_c) {
       constexpr bool more = decltype(more_c)::value;
       const int tn = tc + 32 * NW;
 #pragma unroll
@@ -800,13 +804,13 @@ void split_mfma(
 #pragma unroll
         for (int c = 0; c < KL; ++c) asm volatile("" ::"v"(kc[tg][c]));
       __builtin_amdgcn_sched_barrier(0);
-      if (more) load_subtile(tn, hi, kn, vn, 1);
+      if (more) load_subtile(tn, hi, kn, vn, 1, scn);
       __builtin_amdgcn_sched_barrier(0);
-      compute_subtile(tc, kc, vc, [&] {
+      compute_subtile(tc, kc, vc, scc, [&] {
 #pragma unroll
         for (int e = 0; e < 8; ++e) asm volatile("" ::"v"(vc[e]));
         __builtin_amdgcn_sched_barrier(0);
-        if (more) load_subtile(tn, hi, kn, vn, 2);
+        if (more) load_subtile(tn, hi, kn, vn, 2, scn);
         __builtin_amdgcn_sched_barrier(0);
       });
     };
@@ -818,22 +822,22 @@ void split_mfma(
     const int nsub = t_first < hi ? (hi - t_first - 1) / (32 * NW) + 1 : 1;
     int t0 = t_first, rem = nsub;
     for (; rem > 2; rem -= 2, t0 += 64 * NW) {
-      step(t0, kp, vp, kq, vq, std::true_type{});
-      step(t0 + 32 * NW, kq, vq, kp, vp, std::true_type{});
+      step(t0, kp, vp, scp, kq, vq, scq, std::true_type{});
+      step(t0 + 32 * NW, kq, vq, scq, kp, vp, scp, std::true_type{});
     }
     if (rem == 2) {
-      step(t0, kp, vp, kq, vq, std::true_type{});
-      step(t0 + 32 * NW, kq, vq, kp, vp, std::false_type{});
+      step(t0, kp, vp, scp, kq, vq, scq, std::true_type{});
+      step(t0 + 32 * NW, kq, vq, scq, kp, vp, scp, std::false_type{});
     } else {
-      step(t0, kp, vp, kq, vq, std::false_type{});
+      step(t0, kp, vp, scp, kq, vq, scq, std::false_type{});
     }
   } else {
-    compute_subtile(t_first, kp, vp, [] {});
+    compute_subtile(t_first, kp, vp, scp, [] {});
     for (int t0 = t_first + 32 * NW; t0 < hi; t0 += 32 * NW) {
-      load_subtile(t0, hi, kp, vp, 3);
+      load_subtile(t0, hi, kp, vp, 3, scp);
       // All of the subtile's requests go out before its first use.
       __builtin_amdgcn_sched_barrier(0);
-      compute_subtile(t0, kp, vp, [] {});
+      compute_subtile(t0, kp, vp, scp, [] {});
     }
   }
 
@@ -1017,7 +1021,7 @@ template <int D, bool PAGED, int GM, bool SPEC, int QM, bool BAL = false>
 void launch_mfma_spec(dim3 grid, int nw, bool pipe8, const SplitArgs& a,
                       hipStream_t st) {
   constexpr bool F8 = QM != kCacheBf16;
-  if constexpr (QM == kCacheE4M3 && SPEC) {
+  if constexpr (QM != kCacheBf16 && SPEC) {
     if (pipe8 && nw == 8) {
       launch_one<D, 8, GM, PAGED, SPEC, QM, BAL, true>(grid, a, st);
       return;
@@ -1058,10 +1062,10 @@ void launch_mfma(const Shape& s, SplitArgs a, hipStream_t st) {
   const bool pieces = a.B > 1 && a.B <= 64 && a.bal_target > 0;
   const int nw = QM == kCacheI8 && pieces
                      ? 4 : split_waves(a.P, QM != kCacheBf16);
-  // E4M3, one sequence: the reissue schedule from 8 subtiles per wave
-  // (measured 2-6 % faster at 8 and 32 per wave; even at 4; at 64K, 2 per
-  // wave, 8 % slower).
-  const bool pipe8 = QM == kCacheE4M3 && a.B == 1 &&
+  // 8-bit caches, one sequence: the reissue schedule from 8 subtiles per
+  // wave (E4M3 measured 2-6 % faster at 8 and 32 per wave, even at 4, and
+  // at 64K, 2 per wave, 5-8 % slower; int8 0.6 % faster at 32 per wave).
+  const bool pipe8 = QM != kCacheBf16 && a.B == 1 &&
                      ((int64_t)a.P + 31) / 32 >= 8 * nw;
   if (gm == 8)
     launch_mfma_gm<D, PAGED, 8, QM>(grid, nw, pipe8, a, st);

@@ -474,19 +474,21 @@ def test_fp8_paged_matches_contiguous_bitwise():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int8"])
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("hq,d", [(16, 128), (32, 128), (40, 64)])
-def test_fp8_single_sequence_long_splits(paged, hq, d):
-    """A single sequence's E4M3 splits of 2048 tokens or more (8 subtiles
-    per wave and up) take the reissue schedule: full histories, lengths
-    ending inside a subtile and inside the last split, NaN-poisoned slots
-    past the length, one and two head passes (S = 4 is the threshold
-    itself at L = 8192)."""
+def test_8bit_single_sequence_long_splits(kv, paged, hq, d):
+    """A single sequence's 8-bit splits of 2048 tokens or more (8 subtiles
+    per wave and up) take the reissue schedule (for int8 the subtile's
+    scales are part of each register set): full histories, lengths ending
+    inside a subtile and inside the last split, NaN-poisoned slots past
+    the length, one and two head passes (S = 4 is the threshold itself at
+    L = 8192), and odd and even subtile counts per wave."""
     for i, (L, n) in enumerate(((8192, 8192), (8192, 8179), (12288, 9001))):
-        w = workloads.make("fp8long", seed=46 + i, batch=1, num_q_heads=hq,
+        w = workloads.make("8bitlong", seed=46 + i, batch=1, num_q_heads=hq,
                            num_kv_heads=2, head_dim=d, max_seq_len=L,
                            paged=paged, seq_lens=[n], poison_tail=True,
-                           kv_dtype="fp8_e4m3")
+                           kv_dtype=kv)
         for S in (1, 2, 4):
             check(w, S)
 
