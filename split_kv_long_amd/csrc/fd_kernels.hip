@@ -650,10 +650,11 @@ void split_mfma(
   // current one lands, measured slower. 8-bit subtiles (half the bytes per
   // request, plus the conversions) keep the plain loop where a wave streams
   // few subtiles (E4M3 6-12 %, int8 ~25 % slower at 64K with the schedule)
-  // or where the pieces want two workgroups per CU (its registers leave
+  // or where int8 pieces want two workgroups per CU (its registers leave
   // room for one); a single sequence's 8-bit splits of 8 or more subtiles
   // per wave run it (E4M3 2-6 %, int8 0.6 % faster at 256K; an int8
-  // register set includes the subtile's scales).
+  // register set includes the subtile's scales), and so do E4M3 pieces on
+  // 4 waves.
   constexpr bool kPipe = PIPE;
 
   // Four 8-bit codes -> four bf16 (exact).
@@ -1026,6 +1027,13 @@ void launch_mfma_spec(dim3 grid, int nw, bool pipe8, const SplitArgs& a,
       launch_one<D, 8, GM, PAGED, SPEC, QM, BAL, true>(grid, a, st);
       return;
     }
+  }
+  // E4M3 length-aware pieces: 4 waves on the reissue schedule (ragged paged
+  // batch of 16 91.0 -> 88.9 us, 8 x 32K 27.6 -> 25.8 us, 16 x 2K even;
+  // int8 pieces measured 1 % slower with it and keep their plain loop).
+  if constexpr (QM == kCacheE4M3 && BAL) {
+    launch_one<D, 4, GM, PAGED, SPEC, QM, BAL, true>(grid, a, st);
+    return;
   }
   if (F8 && nw == 8)
     launch_one<D, F8 ? 8 : 4, GM, PAGED, SPEC, QM, BAL>(grid, a, st);
